@@ -1,0 +1,344 @@
+"""Pins for the fp64 oracle: facts that do not come from the oracle itself.
+
+Each test checks the oracle against a closed form, an exact invariant, finite
+differences, a pure-Python brute force or an fp64 library routine.  The mutant
+tests at the end plant plausible mistakes in the oracle (by swapping in a wrong
+function) and check that the pins catch every one of them.
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import oracle.attention as oa
+
+pytestmark = pytest.mark.filterwarnings("ignore::RuntimeWarning")
+
+
+def rnd(shape, seed):
+    return np.random.default_rng(seed).standard_normal(shape)
+
+
+# ---------------------------------------------------------------- closed forms
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("G", [1, 2])
+def test_uniform_scores_give_mean_of_v(causal, G):
+    """Q = 0 makes every visible score equal: O_i is the mean of the visible V rows
+    and LSE_i = log(number of visible keys)."""
+    B, Hkv, S, d = 2, 2, 37, 8
+    q = np.zeros((B, Hkv * G, S, d))
+    k = rnd((B, Hkv, S, d), 1)
+    v = rnd((B, Hkv, S, d), 2)
+    o, lse = oracle.attention_forward(q, k, v, 0.3, causal)
+    n = np.arange(1, S + 1) if causal else np.full(S, S)
+    for b in range(B):
+        for h in range(Hkv * G):
+            vh = v[b, h // G]
+            exp_o = np.cumsum(vh, axis=0) / n[:, None] if causal else np.broadcast_to(vh.mean(0), (S, d))
+            np.testing.assert_allclose(o[b, h], exp_o, rtol=0, atol=1e-13)
+            np.testing.assert_allclose(lse[b, h], np.log(n), rtol=0, atol=1e-13)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("alpha", [1.5, 7.0, 400.0])
+def test_one_hot_two_level_scores(causal, alpha):
+    """q_i = alpha*e0, k_{j*} = e0 and every other key orthogonal to e0: one score
+    is a = alpha*scale, the rest are 0, so P_{ij*} = e^a/(e^a + n - 1)."""
+    S, d, jstar, scale = 19, 5, 6, 0.25
+    q = np.zeros((S, d)); q[:, 0] = alpha
+    k = rnd((S, d), 3); k[:, 0] = 0.0; k[jstar] = 0.0; k[jstar, 0] = 1.0
+    v = rnd((S, d), 4)
+    o, lse = oracle.head_forward(q, k, v, scale, causal)
+    a = alpha * scale
+    for i in range(S):
+        vis = list(range(i + 1)) if causal else list(range(S))
+        n = len(vis)
+        if jstar in vis:
+            others = [j for j in vis if j != jstar]
+            # log(e^a + n - 1) written stably for large a
+            exp_lse = a + math.log1p((n - 1) * math.exp(-a))
+            p = math.exp(a - exp_lse)
+            mean_others = v[others].mean(0) if others else np.zeros(d)
+            exp_o = p * v[jstar] + (1 - p) * mean_others
+        else:
+            exp_lse = math.log(n)
+            exp_o = v[vis].mean(0)
+        np.testing.assert_allclose(o[i], exp_o, rtol=0, atol=1e-12)
+        assert abs(lse[i] - exp_lse) < 1e-12
+    if alpha == 400.0:  # P_{ij*} -> 1: the output is v_{j*} itself where j* is visible
+        rows = np.arange(jstar, S)
+        np.testing.assert_allclose(o[rows], np.broadcast_to(v[jstar], (rows.size, d)), rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_rows_sum_to_one_and_lse_matches_fsum(causal):
+    """With V = identity the output rows are the probability rows themselves: each
+    sums to 1, is 0 on masked keys, and LSE equals an fsum-based log-sum-exp of
+    scores computed with plain Python dot products."""
+    S, d, scale = 23, 6, 0.7
+    q, k = rnd((S, d), 5), rnd((S, d), 6)
+    p, lse = oracle.head_forward(q, k, np.eye(S), scale, causal)
+    np.testing.assert_allclose(p.sum(1), 1.0, rtol=0, atol=1e-12)
+    assert (p >= 0).all()
+    if causal:
+        assert (p[np.triu_indices(S, 1)] == 0.0).all()
+    for i in range(S):
+        js = range(i + 1) if causal else range(S)
+        s = [scale * math.fsum(q[i, t] * k[j, t] for t in range(d)) for j in js]
+        m = max(s)
+        ref = m + math.log(math.fsum(math.exp(x - m) for x in s))
+        assert abs(lse[i] - ref) < 1e-12
+        for j, sj in zip(js, s):
+            assert abs(p[i, j] - math.exp(sj - ref)) < 1e-12
+
+
+def test_causal_row_zero():
+    """Query 0 sees only key 0: O_0 = v_0 and LSE_0 = scale*<q_0, k_0>."""
+    S, d, scale = 33, 16, 0.125
+    q, k, v = rnd((S, d), 7), rnd((S, d), 8), rnd((S, d), 9)
+    o, lse = oracle.head_forward(q, k, v, scale, True)
+    np.testing.assert_array_equal(o[0], v[0])
+    assert abs(lse[0] - scale * float(q[0] @ k[0])) < 1e-14
+
+
+# ------------------------------------------------------------------ brute force
+
+def brute_forward(q, k, v, scale, causal):
+    """Pure-Python loops with math.exp, straight from the definition."""
+    S, d = len(q), len(q[0])
+    o, lse = [], []
+    for i in range(S):
+        js = range(i + 1) if causal else range(S)
+        s = {j: scale * sum(q[i][t] * k[j][t] for t in range(d)) for j in js}
+        z = sum(math.exp(x) for x in s.values())
+        lse.append(math.log(z))
+        o.append([sum(math.exp(s[j]) / z * v[j][t] for j in js) for t in range(len(v[0]))])
+    return np.array(o), np.array(lse)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("S", [1, 2, 9, 16])
+def test_brute_force_forward(causal, S):
+    d, scale = 4, 0.5
+    q, k, v = rnd((S, d), 10 + S), rnd((S, d), 20 + S), rnd((S, d), 30 + S)
+    o, lse = oracle.head_forward(q, k, v, scale, causal)
+    bo, blse = brute_forward(q.tolist(), k.tolist(), v.tolist(), scale, causal)
+    np.testing.assert_allclose(o, bo, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(lse, blse, rtol=0, atol=1e-12)
+
+
+# ---------------------------------------------------------- finite differences
+
+def loss(q, k, v, do, scale, causal):
+    o, _ = oracle.attention_forward(q, k, v, scale, causal)
+    return float((o * do).sum())
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("G", [1, 2])
+def test_finite_difference_gradients(causal, G):
+    """Central differences of L = sum(O * dO) against the analytic backward."""
+    B, Hkv, S, d, scale, h = 1, 1, 6, 3, 0.8, 1e-6
+    q, k, v = rnd((B, Hkv * G, S, d), 40), rnd((B, Hkv, S, d), 41), rnd((B, Hkv, S, d), 42)
+    do = rnd((B, Hkv * G, S, d), 43)
+    dq, dk, dv = oracle.attention_backward(q, k, v, do, scale, causal)
+    for name, x, g in (("q", q, dq), ("k", k, dk), ("v", v, dv)):
+        num = np.zeros_like(x)
+        for idx in np.ndindex(*x.shape):
+            xp, xm = x.copy(), x.copy()
+            xp[idx] += h
+            xm[idx] -= h
+            args = {"q": q, "k": k, "v": v}
+            args[name] = xp
+            lp = loss(args["q"], args["k"], args["v"], do, scale, causal)
+            args[name] = xm
+            lm = loss(args["q"], args["k"], args["v"], do, scale, causal)
+            num[idx] = (lp - lm) / (2 * h)
+        err = np.abs(num - g).max() / max(1.0, np.abs(g).max())
+        assert err < 1e-6, (name, err)
+
+
+# ------------------------------------------------------- fp64 library routine
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("G", [1, 4])
+def test_matches_torch_sdpa_fp64(causal, G):
+    """torch's CPU scaled_dot_product_attention in float64 with autograd, K/V
+    repeated per group (repeat_interleave), gradients summed back per group."""
+    B, Hkv, S, d, scale = 2, 2, 45, 16, 0.2
+    q, k, v, do = (rnd((B, Hkv * G, S, d), 50), rnd((B, Hkv, S, d), 51),
+                   rnd((B, Hkv, S, d), 52), rnd((B, Hkv * G, S, d), 53))
+    tq, tk, tv = (torch.tensor(x, requires_grad=True) for x in (q, k, v))
+    to = torch.nn.functional.scaled_dot_product_attention(
+        tq, tk.repeat_interleave(G, dim=1), tv.repeat_interleave(G, dim=1), is_causal=causal, scale=scale)
+    to.backward(torch.tensor(do))
+    o, _ = oracle.attention_forward(q, k, v, scale, causal)
+    dq, dk, dv = oracle.attention_backward(q, k, v, do, scale, causal)
+    np.testing.assert_allclose(o, to.detach().numpy(), rtol=0, atol=1e-12)
+    np.testing.assert_allclose(dq, tq.grad.numpy(), rtol=0, atol=1e-11)
+    np.testing.assert_allclose(dk, tk.grad.numpy(), rtol=0, atol=1e-11)
+    np.testing.assert_allclose(dv, tv.grad.numpy(), rtol=0, atol=1e-11)
+
+
+# --------------------------------------------------------------- invariants
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_gqa_equals_repeated_mha(causal):
+    B, Hkv, G, S, d, scale = 2, 2, 4, 29, 8, 0.35
+    q, k, v, do = rnd((B, Hkv * G, S, d), 60), rnd((B, Hkv, S, d), 61), rnd((B, Hkv, S, d), 62), rnd((B, Hkv * G, S, d), 63)
+    kr, vr = np.repeat(k, G, axis=1), np.repeat(v, G, axis=1)
+    o, lse = oracle.attention_forward(q, k, v, scale, causal)
+    o2, lse2 = oracle.attention_forward(q, kr, vr, scale, causal)
+    np.testing.assert_array_equal(o, o2)
+    np.testing.assert_array_equal(lse, lse2)
+    dq, dk, dv = oracle.attention_backward(q, k, v, do, scale, causal)
+    dq2, dk2, dv2 = oracle.attention_backward(q, kr, vr, do, scale, causal)
+    np.testing.assert_allclose(dq, dq2, rtol=0, atol=1e-13)
+    np.testing.assert_allclose(dk, dk2.reshape(B, Hkv, G, S, d).sum(2), rtol=0, atol=1e-12)
+    np.testing.assert_allclose(dv, dv2.reshape(B, Hkv, G, S, d).sum(2), rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("shift", [0.5, 60.0])
+def test_key_shift_invariance(causal, shift):
+    """K' = K + 1 u^T adds scale*<q_i,u> to every score of row i: O is unchanged
+    and LSE moves by exactly that amount, even for huge offsets."""
+    B, H, S, d, scale = 1, 2, 41, 8, 0.3
+    q, k, v = rnd((B, H, S, d), 70), rnd((B, H, S, d), 71), rnd((B, H, S, d), 72)
+    u = shift * rnd((d,), 73)
+    o, lse = oracle.attention_forward(q, k, v, scale, causal)
+    o2, lse2 = oracle.attention_forward(q, k + u, v, scale, causal)
+    np.testing.assert_allclose(o2, o, rtol=0, atol=1e-10)
+    np.testing.assert_allclose(lse2, lse + scale * (q @ u), rtol=0, atol=1e-9 * max(1.0, shift))
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("G", [1, 2])
+def test_gradient_identities(causal, G):
+    """sum_j dK_j = 0 (rows of dS sum to 0), sum_j dV_j = sum of dO over the group,
+    and sum_i <q_i, dQ_i> = sum_j <k_j, dK_j> (both equal sum dS*s)."""
+    B, Hkv, S, d, scale = 2, 2, 31, 8, 0.4
+    q, k, v, do = rnd((B, Hkv * G, S, d), 80), rnd((B, Hkv, S, d), 81), rnd((B, Hkv, S, d), 82), rnd((B, Hkv * G, S, d), 83)
+    dq, dk, dv = oracle.attention_backward(q, k, v, do, scale, causal)
+    np.testing.assert_allclose(dk.sum(2), 0.0, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(dv.sum(2), do.reshape(B, Hkv, G, S, d).sum((2, 3)), rtol=0, atol=1e-12)
+    lhs = (q * dq).reshape(B, Hkv, G, S, d).sum((2, 3, 4))
+    rhs = (k * dk).sum((2, 3))
+    np.testing.assert_allclose(lhs, rhs, rtol=0, atol=1e-12)
+
+
+def test_row_blocking_does_not_change_results(monkeypatch):
+    """Blocking over query rows only bounds memory: a different block size gives
+    the same numbers (up to BLAS summation order)."""
+    S, d = 1100, 8
+    q, k, v, do = rnd((1, 1, S, d), 90), rnd((1, 1, S, d), 91), rnd((1, 1, S, d), 92), rnd((1, 1, S, d), 93)
+    ref = oracle.attention_forward(q, k, v, 0.3, True) + oracle.attention_backward(q, k, v, do, 0.3, True)
+    monkeypatch.setattr(oa, "ROW_BLOCK", 97)
+    alt = oracle.attention_forward(q, k, v, 0.3, True) + oracle.attention_backward(q, k, v, do, 0.3, True)
+    for a, b in zip(ref, alt):
+        np.testing.assert_allclose(a, b, rtol=0, atol=1e-11)
+
+
+def test_rejects_bad_group():
+    with pytest.raises(ValueError):
+        oracle.attention_forward(np.zeros((1, 3, 4, 2)), np.zeros((1, 2, 4, 2)), np.zeros((1, 2, 4, 2)), 1.0, False)
+
+
+# ------------------------------------------------------------ planted mistakes
+
+def _mut_scores_excluding_diagonal(q_rows, k, rows, scale, causal):
+    s = scale * (q_rows @ k.T)
+    if causal:
+        s[np.arange(k.shape[0])[None, :] >= rows[:, None]] = -np.inf
+    return s
+
+
+def _mut_scores_transposed_mask(q_rows, k, rows, scale, causal):
+    s = scale * (q_rows @ k.T)
+    if causal:
+        s[np.arange(k.shape[0])[None, :] < rows[:, None]] = -np.inf
+    return s
+
+
+def _mut_softmax_log2(s):
+    m = s.max(axis=1, keepdims=True)
+    e = np.exp(s - m)
+    l = e.sum(axis=1, keepdims=True)
+    return e / l, (m + np.log2(l))[:, 0]
+
+
+def _mut_backward(kind):
+    def head_backward(q, k, v, do, scale, causal):
+        q, k, v, do = (np.asarray(x, dtype=np.float64) for x in (q, k, v, do))
+        S = q.shape[0]
+        rows = np.arange(S)
+        p, _ = oa._softmax_rows(oa._scores(q, k, rows, scale, causal))
+        dp = do @ v.T
+        D = (p * dp).sum(axis=1, keepdims=True)
+        ds = p * dp if kind == "dropped_D" else p * (dp - D)
+        dq = (ds @ k) if kind == "dq_unscaled" else scale * (ds @ k)
+        dk = scale * (ds.T @ (k if kind == "dk_uses_k" else q))
+        dv = (p @ do) if kind == "dv_transposed" else p.T @ do
+        return dq, dk, dv
+    return head_backward
+
+
+def _pins_pass():
+    """Run a compact set of the pins above; True if all of them hold."""
+    checks = [
+        lambda: test_causal_row_zero(),
+        lambda: test_uniform_scores_give_mean_of_v(True, 1),
+        lambda: test_rows_sum_to_one_and_lse_matches_fsum(True),
+        lambda: test_brute_force_forward(True, 9),
+        lambda: test_finite_difference_gradients(True, 1),
+        lambda: test_finite_difference_gradients(False, 2),
+    ]
+    for c in checks:
+        try:
+            c()
+        except (AssertionError, ValueError, IndexError):
+            return False
+    return True
+
+
+def test_pins_pass_on_the_oracle():
+    assert _pins_pass()
+
+
+@pytest.mark.parametrize("mutant", [
+    ("_scores", _mut_scores_excluding_diagonal),
+    ("_scores", _mut_scores_transposed_mask),
+    ("_softmax_rows", _mut_softmax_log2),
+    ("head_backward", _mut_backward("dropped_D")),
+    ("head_backward", _mut_backward("dq_unscaled")),
+    ("head_backward", _mut_backward("dk_uses_k")),
+    ("head_backward", _mut_backward("dv_transposed")),
+], ids=["diag_excluded", "mask_transposed", "lse_log2", "dropped_D", "dq_unscaled", "dk_uses_k", "dv_transposed"])
+def test_pins_catch_planted_mistake(monkeypatch, mutant):
+    name, fn = mutant
+    monkeypatch.setattr(oa, name, fn)
+    if name == "head_backward":
+        monkeypatch.setattr(oracle, "head_backward", fn)
+    assert not _pins_pass()
+
+
+def test_regression_fixture():
+    """The oracle still reproduces the stored tiny-case outputs (tests/golden)."""
+    import json
+    import os
+
+    import workloads
+    path = os.path.join(os.path.dirname(__file__), "golden", "oracle_tiny.json")
+    with open(path) as f:
+        g = json.load(f)
+    c = g["case"]
+    t = workloads.make_tensors(c["B"], c["Hq"], c["Hkv"], c["S"], c["d"], c["seed"])
+    x = {n: t[n].float().numpy() for n in ("q", "k", "v", "do")}
+    o, lse = oracle.attention_forward(x["q"], x["k"], x["v"], c["scale"], c["causal"])
+    dq, dk, dv = oracle.attention_backward(x["q"], x["k"], x["v"], x["do"], c["scale"], c["causal"])
+    for name, val in (("o", o), ("lse", lse), ("dq", dq), ("dk", dk), ("dv", dv)):
+        np.testing.assert_allclose(val, np.array(g[name]), rtol=0, atol=1e-12)

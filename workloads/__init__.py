@@ -1,0 +1,105 @@
+"""Seeded synthetic inputs for the attention workloads (shared by tests, smoke and bench).
+
+This module only draws random numbers and shapes tensors.  It holds none of the
+attention arithmetic, so both the fp64 oracle and the HIP path can be fed from it
+without sharing any of the method.
+
+Recipe (the same everywhere):
+  * ``torch.Generator('cpu').manual_seed(seed)``; by default ``seed`` is the
+    workload number (1-5).
+  * Draw order: Q, K, V, dO, each ``torch.randn`` fp32 N(0, 1) with its full
+    shape ([B,Hq,S,d] for Q and dO, [B,Hkv,S,d] for K and V).
+  * Long-context workload only: for each batch entry, ``floor(0.01 * S)`` distinct
+    positions from ``torch.randperm(S)``; the K rows at those positions (all KV
+    heads) are multiplied by 3 in fp32, giving large-max outlier scores.
+  * Everything is then rounded to bf16 (round to nearest even) on the CPU.
+The scale is ``1/sqrt(d)`` for every workload.
+"""
+
+from __future__ import annotations
+
+import dataclasses
+import math
+from typing import Dict, Tuple
+
+import torch
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    number: int
+    name: str
+    B: int
+    Hq: int
+    Hkv: int
+    S: int
+    d: int
+    causal: bool
+    passes: Tuple[str, ...]
+    outlier_frac: float = 0.0
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / math.sqrt(self.d)
+
+    @property
+    def group(self) -> int:
+        return self.Hq // self.Hkv
+
+    def fwd_flop(self) -> float:
+        """Algorithmic forward flop: 4*B*Hq*S^2*d, halved when causal."""
+        f = 4.0 * self.B * self.Hq * self.S * self.S * self.d
+        return f / 2 if self.causal else f
+
+    def bwd_flop(self) -> float:
+        """Algorithmic backward flop: 2.5x the forward (five products, recompute included)."""
+        return 2.5 * self.fwd_flop()
+
+    def describe(self) -> str:
+        return (f"B={self.B} Hq={self.Hq} Hkv={self.Hkv} S={self.S} d={self.d} "
+                f"{'causal' if self.causal else 'non-causal'}")
+
+
+WORKLOADS: Dict[int, Workload] = {
+    1: Workload(1, "tiny_fwd", 1, 2, 2, 128, 64, False, ("fwd",)),
+    2: Workload(2, "prefill_fwd", 4, 16, 16, 2048, 128, True, ("fwd",)),
+    3: Workload(3, "long_context_fwd", 1, 16, 16, 32768, 128, True, ("fwd",), outlier_frac=0.01),
+    4: Workload(4, "bwd", 4, 16, 16, 4096, 128, True, ("fwd", "bwd")),
+    5: Workload(5, "gqa_fwd_bwd", 2, 32, 8, 8192, 128, True, ("fwd", "bwd")),
+}
+
+
+def make_tensors(B: int, Hq: int, Hkv: int, S: int, d: int, seed: int,
+                 outlier_frac: float = 0.0, with_do: bool = True) -> Dict[str, torch.Tensor]:
+    """Seeded bf16 CPU tensors q, k, v (and do) following the recipe above."""
+    g = torch.Generator("cpu").manual_seed(seed)
+    q = torch.randn((B, Hq, S, d), generator=g, dtype=torch.float32)
+    k = torch.randn((B, Hkv, S, d), generator=g, dtype=torch.float32)
+    v = torch.randn((B, Hkv, S, d), generator=g, dtype=torch.float32)
+    do = torch.randn((B, Hq, S, d), generator=g, dtype=torch.float32) if with_do else None
+    if outlier_frac > 0.0:
+        n = int(math.floor(outlier_frac * S))
+        for b in range(B):
+            pos = torch.randperm(S, generator=g)[:n]
+            k[b, :, pos, :] *= 3.0
+    out = {"q": q.to(torch.bfloat16), "k": k.to(torch.bfloat16), "v": v.to(torch.bfloat16)}
+    if do is not None:
+        out["do"] = do.to(torch.bfloat16)
+    return out
+
+
+def make_inputs(w: Workload, seed: int | None = None, with_do: bool = True) -> Dict[str, torch.Tensor]:
+    """Inputs of workload ``w`` (seed defaults to the workload number)."""
+    return make_tensors(w.B, w.Hq, w.Hkv, w.S, w.d, w.number if seed is None else seed,
+                        w.outlier_frac, with_do)
+
+
+def outlier_positions(w: Workload, seed: int | None = None):
+    """The outlier positions per batch entry that ``make_inputs`` scaled (same draws)."""
+    if w.outlier_frac <= 0.0:
+        return [torch.empty(0, dtype=torch.long) for _ in range(w.B)]
+    g = torch.Generator("cpu").manual_seed(w.number if seed is None else seed)
+    for shape in ((w.B, w.Hq, w.S, w.d), (w.B, w.Hkv, w.S, w.d), (w.B, w.Hkv, w.S, w.d), (w.B, w.Hq, w.S, w.d)):
+        torch.randn(shape, generator=g, dtype=torch.float32)
+    n = int(math.floor(w.outlier_frac * w.S))
+    return [torch.randperm(w.S, generator=g)[:n] for _ in range(w.B)]
