@@ -1,0 +1,239 @@
+"""Python binding of libattn.so, the gfx950 exact-attention library (C ABI in include/attn.h).
+
+Argument marshalling only: every step of the computation runs in the library's HIP
+kernels.  torch supplies device memory and the current stream.  There is no fallback:
+if libattn.so is missing or fails to load, every call raises.
+
+The functions carry the C names:
+    attn_fwd, attn_fwd_ex, attn_bwd, attn_bwd_ex, attn_bwd_workspace_bytes,
+    attn_default_options, attn_status_string, attn_exp2_eval, attn_exp2_poly_host
+"""
+
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional, Tuple
+
+import torch
+
+__all__ = [
+    "AttnError", "attn_options", "library_path", "lib",
+    "attn_fwd", "attn_fwd_ex", "attn_bwd", "attn_bwd_ex", "attn_bwd_workspace_bytes",
+    "attn_default_options", "attn_status_string", "attn_exp2_eval", "attn_exp2_poly_host",
+    "ATTN_EXP_HW", "ATTN_EXP_POLY3",
+]
+
+ATTN_EXP_HW = 0
+ATTN_EXP_POLY3 = 1
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+
+
+def library_path() -> str:
+    return os.path.join(_HERE, "libattn.so")
+
+
+class AttnError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{message} (status {status})")
+        self.status = status
+
+
+class attn_options(ctypes.Structure):
+    _fields_ = [("exp_mode", ctypes.c_int), ("tau", ctypes.c_float), ("variant", ctypes.c_int)]
+
+
+_lib = None
+
+_P = ctypes.c_void_p
+_I = ctypes.c_int
+_F = ctypes.c_float
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libattn.so (raises if it is not built)."""
+    global _lib
+    if _lib is None:
+        path = library_path()
+        if not os.path.exists(path):
+            raise RuntimeError(f"{path} is missing: build it with __graft_entry__.build() "
+                               "(python -m exact_attention_27_amd.build)")
+        L = ctypes.CDLL(path)
+        L.attn_default_options.restype = attn_options
+        L.attn_default_options.argtypes = []
+        L.attn_status_string.restype = ctypes.c_char_p
+        L.attn_status_string.argtypes = [_I]
+        L.attn_fwd.restype = _I
+        L.attn_fwd.argtypes = [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _P]
+        L.attn_fwd_ex.restype = _I
+        L.attn_fwd_ex.argtypes = [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I,
+                                  ctypes.POINTER(attn_options), _P]
+        L.attn_bwd_workspace_bytes.restype = ctypes.c_size_t
+        L.attn_bwd_workspace_bytes.argtypes = [_I, _I, _I, _I, _I]
+        L.attn_bwd.restype = _I
+        L.attn_bwd.argtypes = [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I,
+                               _P, ctypes.c_size_t, _P]
+        L.attn_bwd_ex.restype = _I
+        L.attn_bwd_ex.argtypes = [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I,
+                                  _P, ctypes.c_size_t, ctypes.POINTER(attn_options), _P]
+        L.attn_exp2_eval.restype = _I
+        L.attn_exp2_eval.argtypes = [_P, _P, ctypes.c_long, _I, _P]
+        L.attn_exp2_poly_host.restype = None
+        L.attn_exp2_poly_host.argtypes = [_P, _P, ctypes.c_long]
+        _lib = L
+    return _lib
+
+
+def attn_status_string(status: int) -> str:
+    return lib().attn_status_string(int(status)).decode()
+
+
+def attn_default_options() -> attn_options:
+    return lib().attn_default_options()
+
+
+def _check(status: int) -> None:
+    if status != 0:
+        raise AttnError(status, attn_status_string(status))
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    if isinstance(stream, torch.cuda.Stream):
+        stream = stream.cuda_stream
+    return ctypes.c_void_p(int(stream))
+
+
+def _need(t: torch.Tensor, name: str, dtype: torch.dtype, shape) -> None:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on a GPU device (got {t.device})")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype} (got {t.dtype})")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _options(opt, exp_mode, tau):
+    if opt is None and exp_mode is None and tau is None:
+        return None
+    o = attn_default_options() if opt is None else attn_options(opt.exp_mode, opt.tau, opt.variant)
+    if exp_mode is not None:
+        o.exp_mode = int(exp_mode)
+    if tau is not None:
+        o.tau = float(tau)
+    return o
+
+
+def _dims(q: torch.Tensor, k: torch.Tensor):
+    if q.dim() != 4 or k.dim() != 4:
+        raise ValueError("q must be [B,Hq,S,d] and k, v [B,Hkv,S,d]")
+    B, Hq, S, d = q.shape
+    Hkv = k.shape[1]
+    return B, Hq, Hkv, S, d
+
+
+def attn_fwd_ex(q, k, v, scale: Optional[float] = None, causal: bool = False,
+                o: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                opt: Optional[attn_options] = None, exp_mode: Optional[int] = None,
+                tau: Optional[float] = None, stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Forward pass; returns (o [B,Hq,S,d] bf16, lse [B,Hq,S] fp32).  scale defaults to 1/sqrt(d)."""
+    B, Hq, Hkv, S, d = _dims(q, k)
+    _need(q, "q", torch.bfloat16, (B, Hq, S, d))
+    _need(k, "k", torch.bfloat16, (B, Hkv, S, d))
+    _need(v, "v", torch.bfloat16, (B, Hkv, S, d))
+    if o is None:
+        o = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, Hq, S), dtype=torch.float32, device=q.device)
+    _need(o, "o", torch.bfloat16, (B, Hq, S, d))
+    _need(lse, "lse", torch.float32, (B, Hq, S))
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    op = _options(opt, exp_mode, tau)
+    with torch.cuda.device(q.device):
+        st = lib().attn_fwd_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, Hq, Hkv, S, d,
+                               scale, int(bool(causal)), None if op is None else ctypes.byref(op),
+                               _stream(stream))
+    _check(st)
+    return o, lse
+
+
+def attn_fwd(q, k, v, scale: Optional[float] = None, causal: bool = False,
+             o: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None, stream=None):
+    """Forward pass with the default options (see attn_fwd_ex)."""
+    return attn_fwd_ex(q, k, v, scale, causal, o, lse, stream=stream)
+
+
+def attn_bwd_workspace_bytes(B: int, Hq: int, Hkv: int, S: int, d: int) -> int:
+    return int(lib().attn_bwd_workspace_bytes(B, Hq, Hkv, S, d))
+
+
+def attn_bwd_ex(q, k, v, o, lse, do, scale: Optional[float] = None, causal: bool = False,
+                dq=None, dk=None, dv=None, workspace: Optional[torch.Tensor] = None,
+                opt: Optional[attn_options] = None, exp_mode: Optional[int] = None,
+                tau: Optional[float] = None, stream=None):
+    """Backward pass; returns (dq, dk, dv).  workspace (uint8, >= attn_bwd_workspace_bytes)
+    is allocated with torch when not given."""
+    B, Hq, Hkv, S, d = _dims(q, k)
+    _need(q, "q", torch.bfloat16, (B, Hq, S, d))
+    _need(k, "k", torch.bfloat16, (B, Hkv, S, d))
+    _need(v, "v", torch.bfloat16, (B, Hkv, S, d))
+    _need(o, "o", torch.bfloat16, (B, Hq, S, d))
+    _need(lse, "lse", torch.float32, (B, Hq, S))
+    _need(do, "do", torch.bfloat16, (B, Hq, S, d))
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    _need(dq, "dq", torch.bfloat16, (B, Hq, S, d))
+    _need(dk, "dk", torch.bfloat16, (B, Hkv, S, d))
+    _need(dv, "dv", torch.bfloat16, (B, Hkv, S, d))
+    nbytes = attn_bwd_workspace_bytes(B, Hq, Hkv, S, d)
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
+    elif workspace.device.type != "cuda" or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous GPU tensor")
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    op = _options(opt, exp_mode, tau)
+    with torch.cuda.device(q.device):
+        st = lib().attn_bwd_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(do),
+                               _ptr(dq), _ptr(dk), _ptr(dv), B, Hq, Hkv, S, d, scale,
+                               int(bool(causal)), _ptr(workspace),
+                               workspace.numel() * workspace.element_size(),
+                               None if op is None else ctypes.byref(op), _stream(stream))
+    _check(st)
+    return dq, dk, dv
+
+
+def attn_bwd(q, k, v, o, lse, do, scale: Optional[float] = None, causal: bool = False,
+             dq=None, dk=None, dv=None, workspace=None, stream=None):
+    """Backward pass with the default options (see attn_bwd_ex)."""
+    return attn_bwd_ex(q, k, v, o, lse, do, scale, causal, dq, dk, dv, workspace, stream=stream)
+
+
+def attn_exp2_eval(x: torch.Tensor, exp_mode: int = ATTN_EXP_HW, stream=None) -> torch.Tensor:
+    """2^x on the GPU with the kernels' exp2 (x: fp32 GPU tensor)."""
+    if x.device.type != "cuda" or x.dtype != torch.float32 or not x.is_contiguous():
+        raise ValueError("x must be a contiguous fp32 GPU tensor")
+    y = torch.empty_like(x)
+    with torch.cuda.device(x.device):
+        _check(lib().attn_exp2_eval(_ptr(x), _ptr(y), x.numel(), int(exp_mode), _stream(stream)))
+    return y
+
+
+def attn_exp2_poly_host(x) -> "numpy.ndarray":  # noqa: F821
+    """Host evaluation of the cubic-polynomial exp2 (numpy float32 in, float32 out)."""
+    import numpy as np
+    xa = np.ascontiguousarray(np.asarray(x, dtype=np.float32))
+    y = np.empty_like(xa)
+    lib().attn_exp2_poly_host(xa.ctypes.data_as(ctypes.c_void_p), y.ctypes.data_as(ctypes.c_void_p), xa.size)
+    return y

@@ -1,0 +1,143 @@
+// attn_device.h - device-side building blocks shared by the gfx950 attention kernels.
+//
+// Register/lane layouts used throughout (CDNA4 MFMA, wave64), checked on the GPU by
+// a one-instruction test against known matrices:
+//   v_mfma_f32_32x32x16_bf16  D[32x32] += A[32x16] * B[16x32]
+//     A: lane l holds row (l % 32), k = (l / 32) * 8 + e, e = 0..7   (8 bf16)
+//     B: lane l holds col (l % 32), k = (l / 32) * 8 + e, e = 0..7   (8 bf16)
+//     D: lane l, register v holds row (v / 4) * 8 + (l / 32) * 4 + (v % 4), col (l % 32)
+//   ds_read_b64_tr_b16 (LDS transpose read, 4 x bf16 per lane), within each group of
+//     16 lanes: output lane i, element e = input element (i % 4) of the 8 bytes that
+//     lane 4 * e + i / 4 of the same group addressed.
+//   v_permlane32_swap(x, x): lane l < 32 gets {x[l], x[l + 32]}, lane l >= 32 gets
+//     {x[l - 32], x[l]}; the two halves of a wave exchange values in one instruction.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace attn {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// ---------------------------------------------------------------------------------
+// exp2.  The softmax evaluates every exponential as a power of two (the scale is
+// folded into c = |scale| * log2(e)).  Two evaluations exist:
+//  * the hardware transcendental, v_exp_f32;
+//  * a cubic polynomial on the FMA units: the software exponential the FA4 pages
+//    describe ("NVIDIA's FlashAttention-4", section "The Technical Edge": cubic
+//    polynomials on ordinary cores instead of the special-function units; gist.science
+//    summary, section 2.B).  The pages give no coefficients or range, so this one is
+//    derived here: x is clamped to >= -127, split as x = n + f with n = round(x)
+//    (the 1.5 * 2^23 addition trick) and f in [-1/2, 1/2]; 2^f is a degree-3
+//    polynomial with p(0) = 1 whose coefficients minimise the maximum relative error
+//    on [-1/2, 1/2] (a linear-programming minimax fit, fit_exp2_poly.py beside this
+//    file); 2^n is applied by adding n to the exponent field.  Max relative error
+//    1.02e-4 over the whole range, far below bf16's half-ulp (2^-9), and exactly
+//    2^0 = 1 and 2^-inf = 0.  Valid for x <= 64 (the kernels feed x <= tau <= 30).
+// ---------------------------------------------------------------------------------
+constexpr float kExp2C1 = 0x1.62f5fap-1f;
+constexpr float kExp2C2 = 0x1.f00c4cp-3f;
+constexpr float kExp2C3 = 0x1.c2a216p-5f;
+
+__host__ __device__ inline float exp2_poly3(float x) {
+  x = fmaxf(x, -127.0f);
+  const float t = x + 12582912.0f;  // 1.5 * 2^23: rounds x to an integer in the low mantissa bits
+  const float n = t - 12582912.0f;
+  const float f = x - n;
+  const float p = fmaf(fmaf(fmaf(kExp2C3, f, kExp2C2), f, kExp2C1), f, 1.0f);
+  const uint32_t ti = __builtin_bit_cast(uint32_t, t);
+  return __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, p) + (ti << 23));
+}
+
+template <int EXPMODE>
+__device__ __forceinline__ float exp2_sm(float x) {
+  if constexpr (EXPMODE == 0) {
+    return __builtin_amdgcn_exp2f(x);
+  } else {
+    return exp2_poly3(x);
+  }
+}
+
+// ---------------------------------------------------------------------------------
+// Cross-lane helpers.
+// ---------------------------------------------------------------------------------
+// Value held by lane l ^ 32 (the other half of the wave).
+__device__ __forceinline__ float other_half(float x) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, x);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  const uint32_t lo = r[0], hi = r[1];
+  return __builtin_bit_cast(float, (threadIdx.x & 32) ? lo : hi);
+}
+
+// max(x, value of lane l ^ 32) without a select: {r0, r1} is {own, other} in some order.
+__device__ __forceinline__ float max_halves(float x) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, x);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return fmaxf(__builtin_bit_cast(float, (uint32_t)r[0]), __builtin_bit_cast(float, (uint32_t)r[1]));
+}
+
+__device__ __forceinline__ float sum_halves(float x) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, x);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return __builtin_bit_cast(float, (uint32_t)r[0]) + __builtin_bit_cast(float, (uint32_t)r[1]);
+}
+
+__device__ __forceinline__ bool wave_any(bool p) { return __builtin_amdgcn_ballot_w64(p) != 0; }
+
+// ---------------------------------------------------------------------------------
+// MFMA and LDS access.
+// ---------------------------------------------------------------------------------
+__device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ i16x4 lds_read_tr16(const uint16_t* p) {
+  typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p));
+}
+
+__device__ __forceinline__ bf16x8 join(const i16x4& lo, const i16x4& hi) {
+  typedef short i16x8 __attribute__((ext_vector_type(8)));
+  i16x8 r = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  return __builtin_bit_cast(bf16x8, r);
+}
+
+// Tiles of D bf16 per row are stored in LDS with their 16-byte chunks permuted per row,
+// chunk' = chunk ^ f(row).  f is chosen so that the two LDS access patterns of the
+// kernels are free of bank conflicts (64 banks x 4 bytes):
+//   * 16-byte MFMA-operand reads of 16 consecutive rows at one chunk, and
+//   * 8-byte transpose reads of 4 consecutive rows x 4 consecutive chunks per 32 lanes.
+template <int D>
+__device__ __forceinline__ int swz_chunk(int r, int c) {
+  if constexpr (D == 128) {
+    return c ^ (((r & 3) << 2) | ((r >> 2) & 3));
+  } else {
+    return c ^ ((((r >> 1) & 1) << 2) | ((r >> 2) & 3));
+  }
+}
+
+// Element offset of (row r, column col) in a swizzled [rows][D] bf16 LDS tile.
+template <int D>
+__device__ __forceinline__ int swz(int r, int col) {
+  return r * D + (swz_chunk<D>(r, col >> 3) << 3) + (col & 7);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  bf16x2 r;
+  r[0] = (__bf16)a;
+  r[1] = (__bf16)b;
+  return __builtin_bit_cast(uint32_t, r);
+}
+
+}  // namespace attn

@@ -1,0 +1,48 @@
+// attn_kernels.h - launch interface between the C ABI (attn_api.hip) and the kernels.
+// Arguments here are already validated; launchers only pick a kernel and a grid.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace attn {
+
+// Scores are s = c_sign * <q, k> * scale.  The kernels keep c = |scale| * log2(e) > 0 and
+// apply the sign (or a zero scale) to Q as it is loaded: every 32-bit word of Q is
+// transformed as (w & q_and) ^ q_xor, which negates (q_xor = 0x80008000) or zeroes
+// (q_and = 0) bf16 pairs exactly.  A zero scale is run as Q = 0 with c = 1.
+struct FwdArgs {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  uint16_t* o;
+  float* lse;
+  int B, Hq, Hkv, S;
+  float c;
+  uint32_t q_and, q_xor;
+  float tau;
+};
+
+struct BwdArgs {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  const uint16_t* o;
+  const float* lse;
+  const uint16_t* dO;
+  uint16_t* dq;
+  uint16_t* dk;
+  uint16_t* dv;
+  float* dq_acc;  // [B,Hq,S,d] fp32 workspace
+  float* delta;   // [B,Hq,S] fp32 workspace: D_i = <dO_i, O_i>
+  int B, Hq, Hkv, S;
+  float c;        // |scale| * log2(e) (1 for a zero scale)
+  float scale;    // the caller's scale (dQ and dK carry it)
+  uint32_t q_and, q_xor;
+};
+
+hipError_t launch_fwd(const FwdArgs& a, int d, bool causal, int exp_mode, hipStream_t stream);
+hipError_t launch_bwd(const BwdArgs& a, int d, bool causal, int exp_mode, hipStream_t stream);
+hipError_t launch_exp2_eval(const float* x, float* y, long n, int exp_mode, hipStream_t stream);
+
+}  // namespace attn

@@ -1,0 +1,132 @@
+"""The C ABI without a GPU: the library loads, exports every declared symbol, and
+rejects invalid arguments with the documented status before launching anything."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import exact_attention_27_amd as ea
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "attn.h")
+
+OK, NULL, SHAPE, UNSUP, ALIGN, WS, HIP, VALUE = range(8)
+A = ctypes.c_void_p(0x10000)  # aligned fake device pointers: never dereferenced on error paths
+A2 = ctypes.c_void_p(0x20000)
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(attn_\w+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ea.lib()
+    names = declared_functions()
+    assert len(names) >= 9
+    for n in names:
+        assert hasattr(lib, n), f"libattn.so does not export {n}"
+
+
+def test_python_binding_has_the_c_names():
+    for n in declared_functions():
+        assert hasattr(ea, n), f"binding lacks {n}"
+
+
+def test_default_options():
+    o = ea.attn_default_options()
+    assert o.exp_mode in (ea.ATTN_EXP_HW, ea.ATTN_EXP_POLY3)
+    assert 0.0 <= o.tau <= 30.0 and o.variant == 0
+
+
+def test_status_strings():
+    for s in range(8):
+        assert ea.attn_status_string(s).startswith("ATTN_")
+    assert "unknown" in ea.attn_status_string(99)
+
+
+def fwd(q=A, k=A, v=A, o=A, lse=A, B=1, Hq=2, Hkv=1, S=8, d=64, scale=0.125, causal=0, opt=None):
+    lib = ea.lib()
+    if opt is None:
+        return lib.attn_fwd(q, k, v, o, lse, B, Hq, Hkv, S, d, scale, causal, None)
+    return lib.attn_fwd_ex(q, k, v, o, lse, B, Hq, Hkv, S, d, scale, causal, ctypes.byref(opt), None)
+
+
+def bwd(ptrs=None, B=1, Hq=2, Hkv=1, S=8, d=64, scale=0.125, causal=0, ws=A2, wsb=None, opt=None):
+    lib = ea.lib()
+    p = [A] * 9 if ptrs is None else ptrs
+    if wsb is None:
+        wsb = ea.attn_bwd_workspace_bytes(B, Hq, Hkv, S, d)
+    args = p + [B, Hq, Hkv, S, d, scale, causal, ws, wsb]
+    if opt is None:
+        return lib.attn_bwd(*args, None)
+    return lib.attn_bwd_ex(*args, ctypes.byref(opt), None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), NULL), (dict(k=None), NULL), (dict(v=None), NULL), (dict(o=None), NULL), (dict(lse=None), NULL),
+    (dict(Hq=3, Hkv=2), SHAPE), (dict(Hkv=0), SHAPE), (dict(Hq=0), SHAPE), (dict(S=-1), SHAPE), (dict(B=-2), SHAPE),
+    (dict(d=96), UNSUP), (dict(d=256), UNSUP), (dict(d=0), UNSUP),
+    (dict(q=ctypes.c_void_p(0x10008)), ALIGN), (dict(lse=ctypes.c_void_p(0x10004)), ALIGN),
+    (dict(scale=float("nan")), VALUE), (dict(scale=float("inf")), VALUE),
+    (dict(S=1 << 30, B=1 << 10, Hq=64, Hkv=64), SHAPE),
+])
+def test_fwd_rejects(kw, status):
+    assert fwd(**kw) == status
+
+
+@pytest.mark.parametrize("kw", [dict(B=0), dict(S=0), dict(B=0, q=None, k=None, v=None, o=None, lse=None)])
+def test_fwd_empty_is_ok_without_launch(kw):
+    assert fwd(**kw) == OK
+
+
+@pytest.mark.parametrize("opt,status", [
+    (ea.attn_options(5, 8.0, 0), UNSUP), (ea.attn_options(0, 8.0, 3), UNSUP),
+    (ea.attn_options(0, -1.0, 0), VALUE), (ea.attn_options(0, float("nan"), 0), VALUE), (ea.attn_options(1, 31.0, 0), VALUE),
+])
+def test_fwd_rejects_options(opt, status):
+    assert fwd(opt=opt) == status
+
+
+def test_workspace_bytes():
+    B, Hq, Hkv, S, d = 2, 4, 2, 100, 128
+    rows = B * Hq * S
+    rup = lambda x: (x + 255) // 256 * 256
+    assert ea.attn_bwd_workspace_bytes(B, Hq, Hkv, S, d) == rup(rows * d * 4) + rup(rows * 4)
+    assert ea.attn_bwd_workspace_bytes(0, Hq, Hkv, S, d) == 0
+    assert ea.attn_bwd_workspace_bytes(B, 3, 2, S, d) == 0
+    assert ea.attn_bwd_workspace_bytes(B, Hq, Hkv, S, 80) == 0
+
+
+@pytest.mark.parametrize("i", range(9))
+def test_bwd_rejects_null(i):
+    p = [A] * 9
+    p[i] = None
+    assert bwd(ptrs=p) == NULL
+
+
+@pytest.mark.parametrize("i", range(9))
+def test_bwd_rejects_misaligned(i):
+    p = [A] * 9
+    p[i] = ctypes.c_void_p(0x10002)
+    assert bwd(ptrs=p) == ALIGN
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(ws=None), WS), (dict(wsb=16), WS), (dict(ws=ctypes.c_void_p(0x20010)), WS),
+    (dict(Hq=4, Hkv=3), SHAPE), (dict(d=32), UNSUP), (dict(scale=float("-inf")), VALUE),
+    (dict(opt=ea.attn_options(0, 100.0, 0)), VALUE), (dict(B=0, ws=None), OK), (dict(S=0), OK),
+])
+def test_bwd_rejects(kw, status):
+    assert bwd(**kw) == status
+
+
+def test_exp2_eval_rejects():
+    lib = ea.lib()
+    assert lib.attn_exp2_eval(A, A, -1, 0, None) == SHAPE
+    assert lib.attn_exp2_eval(A, A, 4, 7, None) == UNSUP
+    assert lib.attn_exp2_eval(None, A, 4, 0, None) == NULL
+    assert lib.attn_exp2_eval(None, None, 0, 0, None) == OK
