@@ -12,9 +12,9 @@
 //                 run.  The workgroup walks the query tiles (64 queries) of every query
 //                 head of the GQA group that can see its keys (causal: only tiles at or
 //                 below the diagonal).  Per step, with Q, dO, LSE and D staged in LDS:
-//                     S   = Q K^T              (MFMA, K in registers)
-//                     P   = 2^(S c - LSE log2 e), 0 where masked
-//                     dP  = dO V^T             (MFMA, V in registers)
+//                     S   = Q K^T              (MFMA; K and V stay in LDS for the run)
+//                     P   = 2^(S c - LSE log2 e), 0 where masked  (c = scale log2 e)
+//                     dP  = dO V^T             (MFMA)
 //                     dS  = P (dP - D)
 //                     dV^T += dO^T P,  dK^T += Q^T dS   (dO^T and Q^T by LDS transpose reads)
 //                 dS^T is written to LDS, and the 4 waves then compute the step's
@@ -76,6 +76,7 @@ void bwd_main_kernel(BwdArgs a) {
   constexpr int KLOADS = kBwdBN * CPR / 256;
   constexpr int NDB = DBLK / 2;                // dQ d-blocks per wave
   __shared__ __attribute__((aligned(16))) uint16_t k_lds[kBwdBN * D];
+  __shared__ __attribute__((aligned(16))) uint16_t v_lds[kBwdBN * D];
   __shared__ __attribute__((aligned(16))) uint16_t q_lds[QT];
   __shared__ __attribute__((aligned(16))) uint16_t do_lds[QT];
   __shared__ __attribute__((aligned(16))) uint16_t dst_lds[kBwdBN * kBwdBM];  // dS^T [key][query]
@@ -102,25 +103,19 @@ void bwd_main_kernel(BwdArgs a) {
   const int key = kw + col;  // this lane's key (column of S)
   const size_t kvbase = ((size_t)b * a.Hkv + hkv) * (size_t)S * D;
 
-  // K tile -> LDS (for the dQ product), K and V fragments -> registers.
+  // K and V tiles -> LDS for the whole run (rows past the end of the sequence are zero).
 #pragma unroll
   for (int i = 0; i < KLOADS; ++i) {
     const int id = i * 256 + tid;
     const int r = id / CPR, c = id % CPR;
-    u32x4 w = {0u, 0u, 0u, 0u};
-    if (k0 + r < S) w = *(const u32x4*)(a.k + kvbase + (size_t)(k0 + r) * D + c * 8);
-    *(u32x4*)(k_lds + r * D + (swz_chunk<D>(r, c) << 3)) = w;
-  }
-  bf16x8 kf[KSTEPS], vf[KSTEPS];
-#pragma unroll
-  for (int ks = 0; ks < KSTEPS; ++ks) {
     u32x4 wk = {0u, 0u, 0u, 0u}, wv = {0u, 0u, 0u, 0u};
-    if (key < S) {
-      wk = *(const u32x4*)(a.k + kvbase + (size_t)key * D + ks * 16 + half * 8);
-      wv = *(const u32x4*)(a.v + kvbase + (size_t)key * D + ks * 16 + half * 8);
+    if (k0 + r < S) {
+      wk = *(const u32x4*)(a.k + kvbase + (size_t)(k0 + r) * D + c * 8);
+      wv = *(const u32x4*)(a.v + kvbase + (size_t)(k0 + r) * D + c * 8);
     }
-    kf[ks] = __builtin_bit_cast(bf16x8, wk);
-    vf[ks] = __builtin_bit_cast(bf16x8, wv);
+    const int off = r * D + (swz_chunk<D>(r, c) << 3);
+    *(u32x4*)(k_lds + off) = wk;
+    *(u32x4*)(v_lds + off) = wv;
   }
 
   const int nqt = (S + kBwdBM - 1) / kBwdBM;
@@ -144,7 +139,6 @@ void bwd_main_kernel(BwdArgs a) {
       u32x4 wq = {0u, 0u, 0u, 0u}, wd = {0u, 0u, 0u, 0u};
       if (q0 + r < S) {
         wq = *(const u32x4*)(a.q + (rbase + q0 + r) * D + c * 8);
-        wq = (wq & a.q_and) ^ a.q_xor;
         wd = *(const u32x4*)(a.dO + (rbase + q0 + r) * D + c * 8);
       }
       qreg[i] = wq;
@@ -181,7 +175,7 @@ void bwd_main_kernel(BwdArgs a) {
     dk_acc[db] = f32x16{};
     dv_acc[db] = f32x16{};
   }
-  const float c = a.c;
+  const float c = a.scale * kLog2e;  // signed: no running maximum is needed here
 
   if (steps > 0) gload(0);
   for (int step = 0; step < steps; ++step) {
@@ -197,35 +191,20 @@ void bwd_main_kernel(BwdArgs a) {
       f32x16 s[2] = {f32x16{}, f32x16{}}, dp[2] = {f32x16{}, f32x16{}};
 #pragma unroll
       for (int ks = 0; ks < KSTEPS; ++ks) {
+        const int koff = swz<D>(wave * 32 + col, ks * 16 + half * 8);
+        const bf16x8 kf = *(const bf16x8*)(k_lds + koff);
+        const bf16x8 vf = *(const bf16x8*)(v_lds + koff);
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb) {
           const int off = swz<D>(qb * 32 + col, ks * 16 + half * 8);
-          s[qb] = mfma32(*(const bf16x8*)(q_lds + off), kf[ks], s[qb]);
-          dp[qb] = mfma32(*(const bf16x8*)(do_lds + off), vf[ks], dp[qb]);
+          s[qb] = mfma32(*(const bf16x8*)(q_lds + off), kf, s[qb]);
+          dp[qb] = mfma32(*(const bf16x8*)(do_lds + off), vf, dp[qb]);
         }
       }
       const bool need_mask = (kw + 32 > S) || (q0 + kBwdBM > S) || (CAUSAL && kw + 31 > q0);
-      float pv[2][16], dsv[2][16];
-#pragma unroll
-      for (int qb = 0; qb < 2; ++qb) {
-#pragma unroll
-        for (int g4 = 0; g4 < 4; ++g4) {
-          const int qr = qb * 32 + g4 * 8 + half * 4;
-          const f32x4 l4 = *(const f32x4*)(lse_lds + qr);
-          const f32x4 d4 = *(const f32x4*)(dd_lds + qr);
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int v = g4 * 4 + r;
-            float p = exp2_sm<EXPMODE>(fmaf(s[qb][v], c, -l4[r]));
-            if (need_mask) {
-              const int q = q0 + qr + r;
-              if (key >= S || q >= S || (CAUSAL && key > q)) p = 0.0f;
-            }
-            pv[qb][v] = p;
-            dsv[qb][v] = p * (dp[qb][v] - d4[r]);
-          }
-        }
-      }
+      // P and dS, packed to bf16 as soon as they are formed.  Register v of query block
+      // qb holds query qb*32 + (v/4)*8 + half*4 + v%4; pb[qb][t] / sb[qb][t] hold
+      // registers v = 8t .. 8t+7, the B operand layout of the dV^T and dK^T products.
       bf16x8 pb[2][2], sb[2][2];
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb) {
@@ -233,12 +212,36 @@ void bwd_main_kernel(BwdArgs a) {
         for (int t = 0; t < 2; ++t) {
           u32x4 wp, wsd;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            wp[e] = pack_bf16x2(pv[qb][t * 8 + 2 * e], pv[qb][t * 8 + 2 * e + 1]);
-            wsd[e] = pack_bf16x2(dsv[qb][t * 8 + 2 * e], dsv[qb][t * 8 + 2 * e + 1]);
+          for (int gg = 0; gg < 2; ++gg) {
+            const int g4 = 2 * t + gg;
+            const int qr = qb * 32 + g4 * 8 + half * 4;
+            const f32x4 l4 = *(const f32x4*)(lse_lds + qr);
+            const f32x4 d4 = *(const f32x4*)(dd_lds + qr);
+            float pv[4], dsv[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const int v = g4 * 4 + r;
+              float p = exp2_sm<EXPMODE>(fmaf(s[qb][v], c, -l4[r]));
+              if (need_mask) {
+                const int q = q0 + qr + r;
+                if (key >= S || q >= S || (CAUSAL && key > q)) p = 0.0f;
+              }
+              pv[r] = p;
+              dsv[r] = p * (dp[qb][v] - d4[r]);
+            }
+            wp[2 * gg] = pack_bf16x2(pv[0], pv[1]);
+            wp[2 * gg + 1] = pack_bf16x2(pv[2], pv[3]);
+            wsd[2 * gg] = pack_bf16x2(dsv[0], dsv[1]);
+            wsd[2 * gg + 1] = pack_bf16x2(dsv[2], dsv[3]);
           }
           pb[qb][t] = __builtin_bit_cast(bf16x8, wp);
           sb[qb][t] = __builtin_bit_cast(bf16x8, wsd);
+          // dS^T -> LDS: row = this lane's key, 4 consecutive queries per 8-byte store.
+#pragma unroll
+          for (int gg = 0; gg < 2; ++gg) {
+            const u32x2 w = {wsd[2 * gg], wsd[2 * gg + 1]};
+            *(u32x2*)(dst_lds + swz<kBwdBM>(wave * 32 + col, qb * 32 + (2 * t + gg) * 8 + half * 4)) = w;
+          }
         }
       }
       // dV^T += dO^T P and dK^T += Q^T dS
@@ -253,17 +256,6 @@ void bwd_main_kernel(BwdArgs a) {
             dv_acc[db] = mfma32(join(lds_read_tr16(do_lds + o0), lds_read_tr16(do_lds + o1)), pb[qb][t], dv_acc[db]);
             dk_acc[db] = mfma32(join(lds_read_tr16(q_lds + o0), lds_read_tr16(q_lds + o1)), sb[qb][t], dk_acc[db]);
           }
-        }
-      }
-      // dS^T -> LDS, row = this lane's key, 4 consecutive queries per 8-byte store.
-#pragma unroll
-      for (int qb = 0; qb < 2; ++qb) {
-#pragma unroll
-        for (int g4 = 0; g4 < 4; ++g4) {
-          u32x2 w;
-          w[0] = pack_bf16x2(dsv[qb][g4 * 4 + 0], dsv[qb][g4 * 4 + 1]);
-          w[1] = pack_bf16x2(dsv[qb][g4 * 4 + 2], dsv[qb][g4 * 4 + 3]);
-          *(u32x2*)(dst_lds + swz<kBwdBM>(wave * 32 + col, qb * 32 + g4 * 8 + half * 4)) = w;
         }
       }
     } else {
@@ -308,9 +300,9 @@ void bwd_main_kernel(BwdArgs a) {
     }
   }
 
-  // dK = |scale| dK_acc (Q was loaded with the scale's sign), dV = dV_acc.
+  // dK = scale dK_acc, dV = dV_acc.
   if (key < S) {
-    const float ks = c * kLn2 * (a.q_and ? 1.0f : 0.0f);  // |scale|; a zero scale gives dK = 0
+    const float ks = a.scale;
     uint16_t* dkr = a.dk + kvbase + (size_t)key * D;
     uint16_t* dvr = a.dv + kvbase + (size_t)key * D;
 #pragma unroll

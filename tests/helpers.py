@@ -25,9 +25,19 @@ def errors(gpu: torch.Tensor, ref: np.ndarray):
     return float(d.max()) if d.size else 0.0, float(d.mean()) if d.size else 0.0
 
 
+def edge_max_abs(ref: np.ndarray, excess: float = 1e-2) -> float:
+    """Max-abs bound for edge-shape tests: the 2e-2 bar, or, where bf16 output rounding
+    alone already takes most of it (values of magnitude >= 4), that rounding floor plus
+    ``excess`` of accumulated error.  The workload-config tests use the plain 2e-2 bar."""
+    return max(BF16_MAX, bf16_floor(ref) + excess)
+
+
 def assert_bf16_close(name: str, gpu: torch.Tensor, ref: np.ndarray, max_abs=BF16_MAX, mean_abs=BF16_MEAN):
+    if max_abs == "edge":
+        max_abs = edge_max_abs(ref)
     mx, mn = errors(gpu, ref)
-    msg = f"{name}: max_abs={mx:.3e} mean_abs={mn:.3e} bf16_floor={bf16_floor(ref):.3e} max|ref|={np.abs(ref).max():.3f}"
+    msg = (f"{name}: max_abs={mx:.3e} mean_abs={mn:.3e} bf16_floor={bf16_floor(ref):.3e} "
+           f"max|ref|={np.abs(ref).max() if ref.size else 0.0:.3f} bound={max_abs:.3e}")
     print(msg, flush=True)
     assert np.isfinite(f64(gpu)).all(), name + ": non-finite values"
     assert mx <= max_abs and mn <= mean_abs, msg

@@ -12,7 +12,7 @@ import torch
 import exact_attention_27_amd as ea
 import oracle
 import workloads
-from helpers import assert_bf16_close, assert_lse_close, f64
+from helpers import assert_bf16_close, assert_lse_close, edge_max_abs, f64
 
 pytestmark = pytest.mark.gpu
 
@@ -45,7 +45,7 @@ def test_fwd_edge_shapes(case, causal):
     o, lse = ea.attn_fwd(t["q"], t["k"], t["v"], scale, causal)
     torch.cuda.synchronize()
     ro, rlse = oracle_fwd(t, scale, causal)
-    assert_bf16_close("o", o, ro)
+    assert_bf16_close("o", o, ro, max_abs="edge")
     assert_lse_close(lse, rlse)
     if causal:  # query 0 sees key 0 only: O_0 is V_0 bit for bit
         G = Hq // Hkv
@@ -63,7 +63,7 @@ def test_fwd_options(exp_mode, tau, causal):
     o, lse = ea.attn_fwd_ex(t["q"], t["k"], t["v"], d ** -0.5, causal, exp_mode=exp_mode, tau=tau)
     torch.cuda.synchronize()
     ro, rlse = oracle_fwd(t, d ** -0.5, causal)
-    assert_bf16_close("o", o, ro)
+    assert_bf16_close("o", o, ro, max_abs="edge")
     assert_lse_close(lse, rlse)
 
 
@@ -79,7 +79,7 @@ def test_fwd_rescale_with_growing_scores(tau):
     o, lse = ea.attn_fwd_ex(t["q"], t["k"], t["v"], d ** -0.5, True, tau=tau)
     torch.cuda.synchronize()
     ro, rlse = oracle_fwd(t, d ** -0.5, True)
-    assert_bf16_close("o", o, ro)
+    assert_bf16_close("o", o, ro, max_abs="edge")
     assert_lse_close(lse, rlse)
 
 
@@ -92,7 +92,7 @@ def test_fwd_scales(scale):
     o, lse = ea.attn_fwd(t["q"], t["k"], t["v"], scale, True)
     torch.cuda.synchronize()
     ro, rlse = oracle_fwd(t, scale, True)
-    assert_bf16_close("o", o, ro)
+    assert_bf16_close("o", o, ro, max_abs="edge")
     assert_lse_close(lse, rlse, max_abs=1e-3 * max(1.0, abs(scale) * 4))
 
 
@@ -114,3 +114,99 @@ def test_fwd_empty():
     q = torch.empty((1, 2, 0, 64), dtype=torch.bfloat16, device=DEV)
     o, lse = ea.attn_fwd(q, q, q)
     assert o.numel() == 0
+
+
+# ------------------------------------------------------------------ backward
+
+def oracle_bwd(t, scale, causal):
+    return oracle.attention_backward(f64(t["q"]), f64(t["k"]), f64(t["v"]), f64(t["do"]), scale, causal)
+
+
+BWD_CASES = [
+    (1, 1, 1, 1, 64), (1, 2, 1, 17, 128), (1, 2, 2, 64, 64), (1, 1, 1, 127, 128), (2, 2, 2, 128, 128),
+    (1, 4, 2, 129, 64), (1, 4, 1, 257, 128), (1, 8, 1, 200, 64), (1, 8, 2, 384, 128), (1, 2, 2, 700, 128),
+]
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("case", BWD_CASES, ids=lambda c: "B%dHq%dHkv%dS%dd%d" % c)
+def test_bwd_edge_shapes(case, causal):
+    """GPU forward then GPU backward (as in training), against the oracle's fp64 gradients."""
+    B, Hq, Hkv, S, d = case
+    print(f"\n[bwd] {case} causal={causal}", flush=True)
+    t = inputs(B, Hq, Hkv, S, d, seed=100 + sum(case))
+    scale = d ** -0.5
+    o, lse = ea.attn_fwd(t["q"], t["k"], t["v"], scale, causal)
+    dq, dk, dv = ea.attn_bwd(t["q"], t["k"], t["v"], o, lse, t["do"], scale, causal)
+    torch.cuda.synchronize()
+    rdq, rdk, rdv = oracle_bwd(t, scale, causal)
+    assert_bf16_close("dq", dq, rdq, max_abs="edge")
+    assert_bf16_close("dk", dk, rdk, max_abs="edge")
+    assert_bf16_close("dv", dv, rdv, max_abs="edge")
+
+
+@pytest.mark.parametrize("exp_mode", [ea.ATTN_EXP_HW, ea.ATTN_EXP_POLY3])
+@pytest.mark.parametrize("causal", [False, True])
+def test_bwd_from_oracle_forward(exp_mode, causal):
+    """Backward fed with the oracle's O (bf16) and LSE (fp32): isolates the backward's error."""
+    B, Hq, Hkv, S, d = 1, 4, 2, 300, 128
+    print(f"\n[bwd oracle-fwd] exp_mode={exp_mode} causal={causal}", flush=True)
+    t = inputs(B, Hq, Hkv, S, d, seed=21)
+    scale = d ** -0.5
+    ro, rlse = oracle_fwd(t, scale, causal)
+    o = torch.from_numpy(ro).to(torch.bfloat16).to(DEV)
+    lse = torch.from_numpy(rlse).float().to(DEV)
+    dq, dk, dv = ea.attn_bwd_ex(t["q"], t["k"], t["v"], o, lse, t["do"], scale, causal, exp_mode=exp_mode)
+    torch.cuda.synchronize()
+    rdq, rdk, rdv = oracle_bwd(t, scale, causal)
+    assert_bf16_close("dq", dq, rdq, max_abs="edge")
+    assert_bf16_close("dk", dk, rdk, max_abs="edge")
+    assert_bf16_close("dv", dv, rdv, max_abs="edge")
+
+
+@pytest.mark.parametrize("scale", [-0.2, 0.0, 0.4])
+def test_bwd_scales(scale):
+    """Negative, zero and large scales.  The gradients' bf16 rounding error grows with the
+    scale (dS and dQ scale with it), so the allowance above the rounding floor is scaled
+    by |scale| / (1/sqrt(d)); a wrong sign or a missing scale factor gives O(1) errors."""
+    B, Hq, Hkv, S, d = 1, 2, 1, 150, 64
+    print(f"\n[bwd scale] {scale}", flush=True)
+    t = inputs(B, Hq, Hkv, S, d, seed=23)
+    o, lse = ea.attn_fwd(t["q"], t["k"], t["v"], scale, True)
+    dq, dk, dv = ea.attn_bwd(t["q"], t["k"], t["v"], o, lse, t["do"], scale, True)
+    torch.cuda.synchronize()
+    rdq, rdk, rdv = oracle_bwd(t, scale, True)
+    ratio = max(1.0, abs(scale) * d ** 0.5)
+    for name, g, r in (("dq", dq, rdq), ("dk", dk, rdk), ("dv", dv, rdv)):
+        assert_bf16_close(name, g, r, max_abs=edge_max_abs(r, 1e-2 * ratio), mean_abs=2e-3 * ratio)
+
+
+def test_bwd_gradient_identities_and_determinism():
+    """sum_j dK_j = 0 and sum_j dV_j = sum over the group of sum_i dO_i hold for the GPU
+    gradients (to bf16 accumulation error); dK and dV are bitwise deterministic."""
+    B, Hq, Hkv, S, d = 2, 4, 2, 256, 128
+    t = inputs(B, Hq, Hkv, S, d, seed=29)
+    o, lse = ea.attn_fwd(t["q"], t["k"], t["v"], None, True)
+    g1 = ea.attn_bwd(t["q"], t["k"], t["v"], o, lse, t["do"], None, True)
+    g2 = ea.attn_bwd(t["q"], t["k"], t["v"], o, lse, t["do"], None, True)
+    torch.cuda.synchronize()
+    assert torch.equal(g1[1], g2[1]) and torch.equal(g1[2], g2[2])
+    dq, dk, dv = (f64(x) for x in g1)
+    G = Hq // Hkv
+    assert np.abs(dk.sum(2)).max() < 0.05 * np.sqrt(S)
+    want = f64(t["do"]).reshape(B, Hkv, G, S, d).sum((2, 3))
+    assert np.abs(dv.sum(2) - want).max() < 0.05 * np.sqrt(S * G)
+
+
+def test_bwd_workspace_contents_do_not_matter():
+    B, Hq, Hkv, S, d = 1, 2, 2, 190, 64
+    t = inputs(B, Hq, Hkv, S, d, seed=31)
+    o, lse = ea.attn_fwd(t["q"], t["k"], t["v"], None, False)
+    n = ea.attn_bwd_workspace_bytes(B, Hq, Hkv, S, d)
+    ws = torch.full((n,), 0x7f, dtype=torch.uint8, device=DEV)  # large garbage floats
+    dq, dk, dv = ea.attn_bwd(t["q"], t["k"], t["v"], o, lse, t["do"], None, False, workspace=ws)
+    torch.cuda.synchronize()
+    rdq, rdk, rdv = oracle_bwd(t, d ** -0.5, False)
+    assert_bf16_close("dq", dq, rdq, max_abs="edge")
+    assert_bf16_close("dk", dk, rdk, max_abs="edge")
+    assert_bf16_close("dv", dv, rdv, max_abs="edge")
