@@ -1,0 +1,186 @@
+"""Benchmark: exact attention forward + backward on one MI355X.
+
+One step is one pass of the whole path over one batch of seeded synthetic inputs
+already resident in device memory: attn_fwd (O, LSE) then the three backward launches
+(preprocess, main, dQ convert) giving dQ, dK, dV.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+
+Prints one JSON line.  value = algorithmic TFLOP/s of the step, where a step's flop
+count is fwd + bwd with fwd = 4*B*Hq*S^2*d (halved when causal) and bwd = 2.5 * fwd.
+The roofline object is for the dominant kernel (the backward main kernel, timed with
+HIP events on the stream it runs on, inside the timed region).  cpu_baseline is the
+fp64 oracle timed on this host on a bounded sample of the same workload.
+"""
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "attention fwd/bwd bf16 TFLOPS and % of MI355X MFMA peak, S=2k–32k, d=128"
+PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA, published (256 CU x 4096 flop/clk x 2.4 GHz)
+
+NAMES = {"tiny_fwd": 1, "prefill_fwd": 2, "long_context_fwd": 3, "bwd": 4, "gqa_fwd_bwd": 5}
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="gqa_fwd_bwd", choices=sorted(NAMES))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target oracle sample time")
+    ap.add_argument("--exp-mode", type=int, default=None)
+    ap.add_argument("--tau", type=float, default=None)
+    return ap.parse_args()
+
+
+def cpu_baseline(w, inputs, target_s):
+    """The fp64 oracle (fwd + bwd of one (batch, query head) pair at a time, at the
+    workload's full S) on this host, until about target_s seconds have passed."""
+    import numpy as np
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+    except Exception:  # noqa: BLE001
+        threads = os.cpu_count() or 1
+    x = {n: inputs[n] for n in ("q", "k", "v", "do")}
+    heads, flop, t0 = 0, 0.0, time.perf_counter()
+    per_head_fwd = w.fwd_flop() / (w.B * w.Hq)
+    do_bwd = "bwd" in w.passes
+    for b in range(w.B):
+        for h in range(w.Hq):
+            hk = oracle.kv_head_of(h, w.Hq, w.Hkv)
+            q = x["q"][b, h].float().numpy().astype(np.float64)
+            k = x["k"][b, hk].float().numpy().astype(np.float64)
+            v = x["v"][b, hk].float().numpy().astype(np.float64)
+            oracle.head_forward(q, k, v, w.scale, w.causal)
+            flop += per_head_fwd
+            if do_bwd:
+                do = x["do"][b, h].float().numpy().astype(np.float64)
+                oracle.head_backward(q, k, v, do, w.scale, w.causal)
+                flop += 2.5 * per_head_fwd
+            heads += 1
+            if time.perf_counter() - t0 >= target_s:
+                break
+        if time.perf_counter() - t0 >= target_s:
+            break
+    dt = time.perf_counter() - t0
+    return {
+        "value": flop / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+        "sample": f"fp64 numpy oracle, {'fwd+bwd' if do_bwd else 'fwd'} of {heads} of {w.B * w.Hq} "
+                  f"(batch, query head) pairs at full S={w.S}, d={w.d}, {dt:.1f} s; algorithmic flop",
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this library has no multi-GPU path "
+              "(see DESIGN.md for how attention would shard); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import exact_attention_27_amd as ea
+    import workloads
+
+    w = workloads.WORKLOADS[NAMES[args.workload]]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    host = workloads.make_inputs(w)
+    t = {n: x.to(dev) for n, x in host.items()}
+    q, k, v, do = t["q"], t["k"], t["v"], t["do"]
+    opt = ea.attn_default_options()
+    if args.exp_mode is not None:
+        opt.exp_mode = args.exp_mode
+    if args.tau is not None:
+        opt.tau = args.tau
+    o = torch.empty_like(q)
+    lse = torch.empty((w.B, w.Hq, w.S), dtype=torch.float32, device=dev)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws = torch.empty(max(1, ea.attn_bwd_workspace_bytes(w.B, w.Hq, w.Hkv, w.S, w.d)), dtype=torch.uint8, device=dev)
+    do_bwd = "bwd" in w.passes
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        if ev:
+            ev[0].record(stream)
+        ea.attn_fwd_ex(q, k, v, w.scale, w.causal, o, lse, opt=opt, stream=stream)
+        if ev:
+            ev[1].record(stream)
+        if do_bwd:
+            for ph, e in ((ea.ATTN_BWD_PREPROCESS, 2), (ea.ATTN_BWD_MAIN, 3), (ea.ATTN_BWD_DQ_CONVERT, 4)):
+                ea.attn_bwd_phase(ph, q, k, v, o, lse, do, w.scale, w.causal, dq, dk, dv, ws, opt=opt, stream=stream)
+                if ev:
+                    ev[e].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+
+    ms_step = elapsed * 1e3 / args.steps
+    fwd_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
+    phase_ms = {}
+    if do_bwd:
+        phase_ms["bwd_pre"] = sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps
+        phase_ms["bwd_main"] = sum(e[2].elapsed_time(e[3]) for e in evs) / args.steps
+        phase_ms["dq_convert"] = sum(e[3].elapsed_time(e[4]) for e in evs) / args.steps
+    fwd_tf = w.fwd_flop() / (fwd_ms * 1e-3) / 1e12
+    flop = w.fwd_flop() + (w.bwd_flop() if do_bwd else 0.0)
+    value = flop / (ms_step * 1e-3) / 1e12
+
+    if do_bwd:
+        main_ms = phase_ms["bwd_main"]
+        achieved = w.bwd_flop() / (main_ms * 1e-3) / 1e12
+        dominant = "bwd_main_kernel"
+    else:
+        main_ms = fwd_ms
+        achieved = fwd_tf
+        dominant = "fwd_kernel"
+    roofline = {"kernel": dominant, "bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                "avg_launch_ms": round(main_ms, 4)}
+    breakdown = {"fwd_ms": round(fwd_ms, 4), "fwd_tflops": round(fwd_tf, 2),
+                 "fwd_frac_of_peak": round(fwd_tf / PEAK_BF16_TFLOPS, 4)}
+    if do_bwd:
+        bwd_ms = sum(phase_ms.values())
+        bwd_tf = w.bwd_flop() / (bwd_ms * 1e-3) / 1e12
+        breakdown.update({k + "_ms": round(v, 4) for k, v in phase_ms.items()})
+        breakdown.update({"bwd_ms": round(bwd_ms, 4), "bwd_tflops": round(bwd_tf, 2),
+                          "bwd_frac_of_peak": round(bwd_tf / PEAK_BF16_TFLOPS, 4)})
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(w, host, args.cpu_seconds)
+
+    line = {
+        "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "S": w.S, "d": w.d,
+                   "causal": w.causal, "passes": "+".join(w.passes), "exp_mode": int(opt.exp_mode),
+                   "tau": float(opt.tau), "step_flop": flop},
+        "frac_of_peak": round(value / PEAK_BF16_TFLOPS, 4),
+        "roofline": roofline, "breakdown": breakdown, "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -5,7 +5,7 @@ kernels.  torch supplies device memory and the current stream.  There is no fall
 if libattn.so is missing or fails to load, every call raises.
 
 The functions carry the C names:
-    attn_fwd, attn_fwd_ex, attn_bwd, attn_bwd_ex, attn_bwd_workspace_bytes,
+    attn_fwd, attn_fwd_ex, attn_bwd, attn_bwd_ex, attn_bwd_phase, attn_bwd_workspace_bytes,
     attn_default_options, attn_status_string, attn_exp2_eval, attn_exp2_poly_host
 """
 
@@ -20,7 +20,7 @@ import torch
 
 __all__ = [
     "AttnError", "attn_options", "library_path", "lib",
-    "attn_fwd", "attn_fwd_ex", "attn_bwd", "attn_bwd_ex", "attn_bwd_workspace_bytes",
+    "attn_fwd", "attn_fwd_ex", "attn_bwd", "attn_bwd_ex", "attn_bwd_phase", "attn_bwd_workspace_bytes",
     "attn_default_options", "attn_status_string", "attn_exp2_eval", "attn_exp2_poly_host",
     "ATTN_EXP_HW", "ATTN_EXP_POLY3",
 ]
@@ -78,6 +78,9 @@ def lib() -> ctypes.CDLL:
         L.attn_bwd_ex.restype = _I
         L.attn_bwd_ex.argtypes = [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I,
                                   _P, ctypes.c_size_t, ctypes.POINTER(attn_options), _P]
+        L.attn_bwd_phase.restype = _I
+        L.attn_bwd_phase.argtypes = [_I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I,
+                                     _P, ctypes.c_size_t, ctypes.POINTER(attn_options), _P]
         L.attn_exp2_eval.restype = _I
         L.attn_exp2_eval.argtypes = [_P, _P, ctypes.c_long, _I, _P]
         L.attn_exp2_poly_host.restype = None
@@ -178,12 +181,24 @@ def attn_bwd_workspace_bytes(B: int, Hq: int, Hkv: int, S: int, d: int) -> int:
     return int(lib().attn_bwd_workspace_bytes(B, Hq, Hkv, S, d))
 
 
+ATTN_BWD_ALL, ATTN_BWD_PREPROCESS, ATTN_BWD_MAIN, ATTN_BWD_DQ_CONVERT = 0, 1, 2, 3
+
+
 def attn_bwd_ex(q, k, v, o, lse, do, scale: Optional[float] = None, causal: bool = False,
                 dq=None, dk=None, dv=None, workspace: Optional[torch.Tensor] = None,
                 opt: Optional[attn_options] = None, exp_mode: Optional[int] = None,
                 tau: Optional[float] = None, stream=None):
     """Backward pass; returns (dq, dk, dv).  workspace (uint8, >= attn_bwd_workspace_bytes)
     is allocated with torch when not given."""
+    return attn_bwd_phase(ATTN_BWD_ALL, q, k, v, o, lse, do, scale, causal, dq, dk, dv, workspace,
+                          opt, exp_mode, tau, stream)
+
+
+def attn_bwd_phase(phase: int, q, k, v, o, lse, do, scale: Optional[float] = None, causal: bool = False,
+                   dq=None, dk=None, dv=None, workspace: Optional[torch.Tensor] = None,
+                   opt: Optional[attn_options] = None, exp_mode: Optional[int] = None,
+                   tau: Optional[float] = None, stream=None):
+    """One phase of the backward (ATTN_BWD_*); the phases share ``workspace``."""
     B, Hq, Hkv, S, d = _dims(q, k)
     _need(q, "q", torch.bfloat16, (B, Hq, S, d))
     _need(k, "k", torch.bfloat16, (B, Hkv, S, d))
@@ -205,7 +220,7 @@ def attn_bwd_ex(q, k, v, o, lse, do, scale: Optional[float] = None, causal: bool
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
     op = _options(opt, exp_mode, tau)
     with torch.cuda.device(q.device):
-        st = lib().attn_bwd_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(do),
+        st = lib().attn_bwd_phase(int(phase), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(do),
                                _ptr(dq), _ptr(dk), _ptr(dv), B, Hq, Hkv, S, d, scale,
                                int(bool(causal)), _ptr(workspace),
                                workspace.numel() * workspace.element_size(),

@@ -119,10 +119,18 @@ size_t attn_bwd_workspace_bytes(int B, int Hq, int Hkv, int S, int d) {
   return round_up(rows * d * sizeof(float)) + round_up(rows * sizeof(float));
 }
 
-int attn_bwd_ex(const void* q, const void* k, const void* v, const void* o, const float* lse,
-                const void* dO, void* dq, void* dk, void* dv,
-                int B, int Hq, int Hkv, int S, int d, float scale, int causal,
-                void* workspace, size_t workspace_bytes, const attn_options* opt, void* stream) {
+int attn_bwd_phase(int phase, const void* q, const void* k, const void* v, const void* o, const float* lse,
+                   const void* dO, void* dq, void* dk, void* dv,
+                   int B, int Hq, int Hkv, int S, int d, float scale, int causal,
+                   void* workspace, size_t workspace_bytes, const attn_options* opt, void* stream) {
+  int phases;
+  switch (phase) {
+    case ATTN_BWD_ALL: phases = 7; break;
+    case ATTN_BWD_PREPROCESS: phases = 1; break;
+    case ATTN_BWD_MAIN: phases = 2; break;
+    case ATTN_BWD_DQ_CONVERT: phases = 4; break;
+    default: return ATTN_ERR_UNSUPPORTED;
+  }
   bool empty = false;
   int st = check_sizes(B, Hq, Hkv, S, d, &empty);
   if (st != ATTN_OK) return st;
@@ -155,7 +163,15 @@ int attn_bwd_ex(const void* q, const void* k, const void* v, const void* o, cons
   a.scale = scale;
   scale_setup(scale, &a.c, &a.q_and, &a.q_xor);
   (void)hipGetLastError();
-  return hip_status(attn::launch_bwd(a, d, causal != 0, o_.exp_mode, static_cast<hipStream_t>(stream)));
+  return hip_status(attn::launch_bwd(a, d, causal != 0, o_.exp_mode, phases, static_cast<hipStream_t>(stream)));
+}
+
+int attn_bwd_ex(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                const void* dO, void* dq, void* dk, void* dv,
+                int B, int Hq, int Hkv, int S, int d, float scale, int causal,
+                void* workspace, size_t workspace_bytes, const attn_options* opt, void* stream) {
+  return attn_bwd_phase(ATTN_BWD_ALL, q, k, v, o, lse, dO, dq, dk, dv, B, Hq, Hkv, S, d, scale, causal,
+                        workspace, workspace_bytes, opt, stream);
 }
 
 int attn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,

@@ -337,36 +337,43 @@ __global__ __launch_bounds__(256) void dq_convert_kernel(const float* __restrict
 }
 
 template <int D, bool CAUSAL, int EXPMODE>
-hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t stream) {
+hipError_t launch_bwd_t(const BwdArgs& a, int phases, hipStream_t stream) {
   const long rows = (long)a.B * a.Hq * a.S;
-  const long pre_threads = rows * (D / 8);
-  hipLaunchKernelGGL(bwd_pre_kernel<D>, dim3((unsigned)((pre_threads + 255) / 256)), dim3(256), 0, stream,
-                     a.o, a.dO, a.delta, a.dq_acc, rows);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  const int nkt = (a.S + kBwdBN - 1) / kBwdBN;
-  hipLaunchKernelGGL((bwd_main_kernel<D, CAUSAL, EXPMODE>), dim3((unsigned)(nkt * a.B * a.Hkv)), dim3(256), 0,
-                     stream, a);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  const long n8 = rows * D / 8;
-  hipLaunchKernelGGL(dq_convert_kernel, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, stream,
-                     a.dq_acc, a.dq, n8, a.scale);
-  return hipGetLastError();
+  hipError_t e = hipSuccess;
+  if (phases & 1) {
+    const long pre_threads = rows * (D / 8);
+    hipLaunchKernelGGL(bwd_pre_kernel<D>, dim3((unsigned)((pre_threads + 255) / 256)), dim3(256), 0, stream,
+                       a.o, a.dO, a.delta, a.dq_acc, rows);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  if (phases & 2) {
+    const int nkt = (a.S + kBwdBN - 1) / kBwdBN;
+    hipLaunchKernelGGL((bwd_main_kernel<D, CAUSAL, EXPMODE>), dim3((unsigned)(nkt * a.B * a.Hkv)), dim3(256), 0,
+                       stream, a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  if (phases & 4) {
+    const long n8 = rows * D / 8;
+    hipLaunchKernelGGL(dq_convert_kernel, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, stream,
+                       a.dq_acc, a.dq, n8, a.scale);
+    e = hipGetLastError();
+  }
+  return e;
 }
 
 template <int D>
-hipError_t launch_bwd_d(const BwdArgs& a, bool causal, int exp_mode, hipStream_t stream) {
+hipError_t launch_bwd_d(const BwdArgs& a, bool causal, int exp_mode, int phases, hipStream_t stream) {
   if (causal) {
-    return exp_mode == 0 ? launch_bwd_t<D, true, 0>(a, stream) : launch_bwd_t<D, true, 1>(a, stream);
+    return exp_mode == 0 ? launch_bwd_t<D, true, 0>(a, phases, stream) : launch_bwd_t<D, true, 1>(a, phases, stream);
   }
-  return exp_mode == 0 ? launch_bwd_t<D, false, 0>(a, stream) : launch_bwd_t<D, false, 1>(a, stream);
+  return exp_mode == 0 ? launch_bwd_t<D, false, 0>(a, phases, stream) : launch_bwd_t<D, false, 1>(a, phases, stream);
 }
 
 }  // namespace
 
-hipError_t launch_bwd(const BwdArgs& a, int d, bool causal, int exp_mode, hipStream_t stream) {
-  return d == 64 ? launch_bwd_d<64>(a, causal, exp_mode, stream) : launch_bwd_d<128>(a, causal, exp_mode, stream);
+hipError_t launch_bwd(const BwdArgs& a, int d, bool causal, int exp_mode, int phases, hipStream_t stream) {
+  return d == 64 ? launch_bwd_d<64>(a, causal, exp_mode, phases, stream)
+                 : launch_bwd_d<128>(a, causal, exp_mode, phases, stream);
 }
 
 }  // namespace attn

@@ -42,7 +42,9 @@ struct BwdArgs {
 };
 
 hipError_t launch_fwd(const FwdArgs& a, int d, bool causal, int exp_mode, hipStream_t stream);
-hipError_t launch_bwd(const BwdArgs& a, int d, bool causal, int exp_mode, hipStream_t stream);
+// phases: bit 0 = preprocess (D and zeroed dQ accumulator), bit 1 = main kernel,
+// bit 2 = dQ conversion.  7 runs the whole backward.
+hipError_t launch_bwd(const BwdArgs& a, int d, bool causal, int exp_mode, int phases, hipStream_t stream);
 hipError_t launch_exp2_eval(const float* x, float* y, long n, int exp_mode, hipStream_t stream);
 
 }  // namespace attn

