@@ -40,7 +40,21 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target oracle sample time")
     ap.add_argument("--exp-mode", type=int, default=None)
     ap.add_argument("--tau", type=float, default=None)
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="instead of the benchmark, run a plain device copy of MIB MiB (3 times): the "
+                         "reference kernel that scales rocprofv3 FETCH_SIZE/WRITE_SIZE into bytes")
     return ap.parse_args()
+
+
+def copy_calibration(mib: int) -> None:
+    import torch
+    n = mib * (1 << 20)
+    src = torch.ones(n, dtype=torch.uint8, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes_read": n, "copy_calibration_bytes_written": n, "calls": 3}), flush=True)
 
 
 def cpu_baseline(w, inputs, target_s):
@@ -84,6 +98,9 @@ def cpu_baseline(w, inputs, target_s):
 
 def main():
     args = parse()
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this library has no multi-GPU path "
               "(see DESIGN.md for how attention would shard); run with --gpus 1", file=sys.stderr)

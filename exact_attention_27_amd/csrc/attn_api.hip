@@ -116,7 +116,8 @@ size_t attn_bwd_workspace_bytes(int B, int Hq, int Hkv, int S, int d) {
   bool empty = false;
   if (check_sizes(B, Hq, Hkv, S, d, &empty) != ATTN_OK || empty) return 0;
   const size_t rows = (size_t)B * Hq * S;
-  return round_up(rows * d * sizeof(float)) + round_up(rows * sizeof(float));
+  const size_t prows = (size_t)B * Hq * (((size_t)S + 63) / 64 * 64);
+  return round_up(rows * d * sizeof(float)) + 2 * round_up(prows * sizeof(float));
 }
 
 int attn_bwd_phase(int phase, const void* q, const void* k, const void* v, const void* o, const float* lse,
@@ -157,8 +158,10 @@ int attn_bwd_phase(int phase, const void* q, const void* k, const void* v, const
   a.dk = static_cast<uint16_t*>(dk);
   a.dv = static_cast<uint16_t*>(dv);
   const size_t rows = (size_t)B * Hq * S;
+  const size_t prows = (size_t)B * Hq * (((size_t)S + 63) / 64 * 64);
   a.dq_acc = static_cast<float*>(workspace);
   a.delta = reinterpret_cast<float*>(static_cast<char*>(workspace) + round_up(rows * d * sizeof(float)));
+  a.lse2 = reinterpret_cast<float*>(reinterpret_cast<char*>(a.delta) + round_up(prows * sizeof(float)));
   a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.S = S;
   a.scale = scale;
   scale_setup(scale, &a.c, &a.q_and, &a.q_xor);

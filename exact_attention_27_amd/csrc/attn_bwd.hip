@@ -5,13 +5,13 @@
 // FlashAttention-4 story; "NVIDIA Blackwell: FlashAttention-4 Overcomes Memory
 // Bottlenecks", body paragraph).  Three launches on the caller's stream:
 //
-//  1. bwd_pre:    D_i = <dO_i, O_i> in fp32 from the stored bf16 O and dO, and the fp32
-//                 dQ accumulator is zeroed.  Bound by HBM bandwidth.
+//  1. bwd_pre:    D_i = <dO_i, O_i> in fp32 from the stored bf16 O and dO, LSE_i log2(e),
+//                 and a zeroed fp32 dQ accumulator.  Bound by HBM bandwidth.
 //  2. bwd_main:   one workgroup per (batch, KV head, tile of 128 keys); each of its 4 waves
 //                 owns 32 keys and keeps dK and dV for them in registers for the whole
-//                 run.  The workgroup walks the query tiles (64 queries) of every query
-//                 head of the GQA group that can see its keys (causal: only tiles at or
-//                 below the diagonal).  Per step, with Q, dO, LSE and D staged in LDS:
+//                 run.  The workgroup walks the query tiles (64 queries) that can see its
+//                 keys (causal: only tiles at or below the diagonal), from the last one
+//                 down, for every query head of the GQA group.  Per step, with Q, dO, LSE and D staged in LDS:
 //                     S   = Q K^T              (MFMA; K and V stay in LDS for the run)
 //                     P   = 2^(S c - LSE log2 e), 0 where masked  (c = scale log2 e)
 //                     dP  = dO V^T             (MFMA)
@@ -37,15 +37,25 @@ constexpr int kBwdBN = 128;  // keys per workgroup (4 waves x 32)
 constexpr int kBwdBM = 64;   // queries per step
 
 // ------------------------------------------------------------------ preprocess
+// Rows are taken in the padded layout [B*Hq][S_pad] (S_pad = S rounded up to a multiple
+// of the 64-query step): D_i = <dO_i, O_i> and LSE_i log2(e) go to the workspace there,
+// padding rows get 0, and the fp32 dQ accumulator rows [B*Hq][S] are zeroed.  The main
+// kernel then moves whole 64-row blocks of D and LSE into LDS with no bounds checks.
 template <int D>
 __global__ __launch_bounds__(256) void bwd_pre_kernel(const uint16_t* __restrict__ o, const uint16_t* __restrict__ dO,
-                                                      float* __restrict__ delta, float* __restrict__ dq_acc, long rows) {
+                                                      const float* __restrict__ lse, float* __restrict__ delta,
+                                                      float* __restrict__ lse2, float* __restrict__ dq_acc,
+                                                      long prows, int S, int S_pad) {
   constexpr int LPR = D / 8;  // lanes per row, 8 bf16 each
   const long gid = (long)blockIdx.x * 256 + threadIdx.x;
-  const long row = gid / LPR;
+  const long prow = gid / LPR;
   const int part = (int)(gid % LPR);
+  const long bhr = prow / S_pad;
+  const int srow = (int)(prow - bhr * S_pad);
+  const bool real = prow < prows && srow < S;
+  const long row = bhr * S + srow;  // row in the unpadded [B*Hq][S] tensors
   float acc = 0.0f;
-  if (row < rows) {
+  if (real) {
     const u32x4 ov = *(const u32x4*)(o + row * D + part * 8);
     const u32x4 dv = *(const u32x4*)(dO + row * D + part * 8);
 #pragma unroll
@@ -61,33 +71,53 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const uint16_t* __restrict
   }
 #pragma unroll
   for (int off = LPR / 2; off >= 1; off >>= 1) acc += __shfl_xor(acc, off);
-  if (row < rows && part == 0) delta[row] = acc;
+  if (prow < prows && part == 0) {
+    delta[prow] = acc;
+    lse2[prow] = real ? lse[row] * kLog2e : 0.0f;
+  }
 }
 
 // ------------------------------------------------------------------ main
+
+// Vector memory operations of a wave complete in issue order, and no-return atomics
+// count in vmcnt like loads.  Each backward step ends with exactly kDqAtomics atomic adds
+// per wave; waiting for vmcnt <= kDqAtomics at the next step therefore waits for every
+// earlier DMA without waiting for those atomics to drain.
+constexpr int kDqAtomics = 16;
+__device__ __forceinline__ void wait_dma_behind_atomics() {
+  static_assert(kDqAtomics == 16, "the immediate below");
+  __asm__ volatile("s_waitcnt vmcnt(16)" ::: "memory");
+}
+
+// Workgroup of 8 waves (two per SIMD) on a tile of 128 keys.  Wave w owns key block
+// kq = w % 4 (32 keys) for query half qh = w / 4 of every 64-query step: waves w and
+// w + 4 accumulate partial dK and dV for the same keys over different queries, and
+// the two partials are added through LDS at the end.
 template <int D, bool CAUSAL, int EXPMODE>
-__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
+__global__ __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_per_eu(2, 2)))
 void bwd_main_kernel(BwdArgs a) {
   constexpr int KSTEPS = D / 16;
   constexpr int DBLK = D / 32;
   constexpr int CPR = D / 8;
-  constexpr int QT = kBwdBM * D;               // elements of one Q or dO tile
-  constexpr int QLOADS = kBwdBM * CPR / 256;   // 16-byte chunks per thread per tile
-  constexpr int KLOADS = kBwdBN * CPR / 256;
-  constexpr int NDB = DBLK / 2;                // dQ d-blocks per wave
-  __shared__ __attribute__((aligned(16))) uint16_t k_lds[kBwdBN * D];
-  __shared__ __attribute__((aligned(16))) uint16_t v_lds[kBwdBN * D];
-  __shared__ __attribute__((aligned(16))) uint16_t q_lds[QT];
-  __shared__ __attribute__((aligned(16))) uint16_t do_lds[QT];
-  __shared__ __attribute__((aligned(16))) uint16_t dst_lds[kBwdBN * kBwdBM];  // dS^T [key][query]
-  __shared__ __attribute__((aligned(16))) float lse_lds[kBwdBM];
-  __shared__ __attribute__((aligned(16))) float dd_lds[kBwdBM];
+  constexpr int KT = kBwdBN * D;               // elements of the K (or V) tile
+  constexpr int QT = kBwdBM * D;               // elements of one Q (or dO) tile
+  constexpr int KDMAS = kBwdBN * CPR / 512;    // 16-byte chunks per thread, K or V tile
+  constexpr int QDMAS = kBwdBM * CPR / 512;    // 16-byte chunks per thread, Q or dO tile
+  __shared__ __attribute__((aligned(1024))) uint16_t k_lds[KT];
+  __shared__ __attribute__((aligned(1024))) uint16_t v_lds[KT];
+  __shared__ __attribute__((aligned(1024))) uint16_t q_lds[2][QT];
+  __shared__ __attribute__((aligned(1024))) uint16_t do_lds[2][QT];
+  __shared__ __attribute__((aligned(1024))) uint16_t dst_lds[kBwdBN * kBwdBM];  // dS^T [key][query]
+  __shared__ __attribute__((aligned(1024))) float sd_lds[2][2 * kBwdBM];  // [stage][LSE log2e | D]
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
+  const int kq = wave & 3;   // key block of this wave
+  const int qh = wave >> 2;  // query half of each step
   const int col = lane & 31;
   const int half = lane >> 5;
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
   const int S = a.S;
   const int G = a.Hq / a.Hkv;
 
@@ -99,23 +129,19 @@ void bwd_main_kernel(BwdArgs a) {
   const int b = bh / a.Hkv;
   const int hkv = bh - b * a.Hkv;
   const int k0 = kt * kBwdBN;
-  const int kw = k0 + wave * 32;
+  const int kw = k0 + kq * 32;
   const int key = kw + col;  // this lane's key (column of S)
   const size_t kvbase = ((size_t)b * a.Hkv + hkv) * (size_t)S * D;
 
-  // K and V tiles -> LDS for the whole run (rows past the end of the sequence are zero).
+  // K and V tiles -> LDS for the whole run (rows past the end are clamped to a real
+  // row; their probabilities are masked to 0).
 #pragma unroll
-  for (int i = 0; i < KLOADS; ++i) {
-    const int id = i * 256 + tid;
-    const int r = id / CPR, c = id % CPR;
-    u32x4 wk = {0u, 0u, 0u, 0u}, wv = {0u, 0u, 0u, 0u};
-    if (k0 + r < S) {
-      wk = *(const u32x4*)(a.k + kvbase + (size_t)(k0 + r) * D + c * 8);
-      wv = *(const u32x4*)(a.v + kvbase + (size_t)(k0 + r) * D + c * 8);
-    }
-    const int off = r * D + (swz_chunk<D>(r, c) << 3);
-    *(u32x4*)(k_lds + off) = wk;
-    *(u32x4*)(v_lds + off) = wv;
+  for (int i = 0; i < KDMAS; ++i) {
+    const int pch = (i * 8 + wave) * 64 + lane;
+    const int r = pch / CPR;
+    const int src = (min(k0 + r, S - 1)) * D + swz_chunk<D>(r, pch % CPR) * 8;
+    dma16(a.k + kvbase + src, k_lds + (i * 8 + wave_u) * 512);
+    dma16(a.v + kvbase + src, v_lds + (i * 8 + wave_u) * 512);
   }
 
   const int nqt = (S + kBwdBM - 1) / kBwdBM;
@@ -123,45 +149,37 @@ void bwd_main_kernel(BwdArgs a) {
   const int per_head = nqt - q_first;
   const int steps = G * per_head;
 
-  // Register staging of the next step's Q, dO, LSE (log2 units) and D.
-  u32x4 qreg[QLOADS], doreg[QLOADS];
-  float lse_r = 0.0f, dd_r = 0.0f;
-  auto gload = [&](int step) {
-    const int g = step / per_head;
-    const int qt = q_first + step - g * per_head;
+  // Q, dO, LSE (log2 units) and D of a step -> LDS stage, all by DMA (LSE and D come
+  // from the padded workspace rows written by the preprocess kernel).
+  int qdma_row[QDMAS], qdma_off[QDMAS];
+#pragma unroll
+  for (int i = 0; i < QDMAS; ++i) {
+    const int pch = (i * 8 + wave) * 64 + lane;
+    qdma_row[i] = pch / CPR;
+    qdma_off[i] = swz_chunk<D>(qdma_row[i], pch % CPR) * 8;
+  }
+  const int S_pad = (S + kBwdBM - 1) / kBwdBM * kBwdBM;
+  // Step order: query tiles from the last one down, the group's heads innermost.  All
+  // workgroups of one (batch, KV head) start on the last query tile together and move
+  // down in step, so their fp32 atomic adds into dQ hit the same few rows at the same
+  // time and stay in L2 (the workgroups of one KV head share an XCD when B*Hkv is a
+  // multiple of 8).
+  auto stage_in = [&](int step, int st) {
+    const int g = step % G;
+    const int qt = nqt - 1 - step / G;
     const int hq = hkv * G + g;
     const size_t rbase = ((size_t)b * a.Hq + hq) * (size_t)S;
     const int q0 = qt * kBwdBM;
 #pragma unroll
-    for (int i = 0; i < QLOADS; ++i) {
-      const int id = i * 256 + tid;
-      const int r = id / CPR, c = id % CPR;
-      u32x4 wq = {0u, 0u, 0u, 0u}, wd = {0u, 0u, 0u, 0u};
-      if (q0 + r < S) {
-        wq = *(const u32x4*)(a.q + (rbase + q0 + r) * D + c * 8);
-        wd = *(const u32x4*)(a.dO + (rbase + q0 + r) * D + c * 8);
-      }
-      qreg[i] = wq;
-      doreg[i] = wd;
+    for (int i = 0; i < QDMAS; ++i) {
+      const size_t src = (rbase + min(q0 + qdma_row[i], S - 1)) * D + qdma_off[i];
+      dma16(a.q + src, q_lds[st] + (i * 8 + wave_u) * 512);
+      dma16(a.dO + src, do_lds[st] + (i * 8 + wave_u) * 512);
     }
-    if (tid < kBwdBM) {
-      const bool in = q0 + tid < S;
-      lse_r = in ? a.lse[rbase + q0 + tid] * kLog2e : 0.0f;
-      dd_r = in ? a.delta[rbase + q0 + tid] : 0.0f;
-    }
-  };
-  auto sstore = [&]() {
-#pragma unroll
-    for (int i = 0; i < QLOADS; ++i) {
-      const int id = i * 256 + tid;
-      const int r = id / CPR, c = id % CPR;
-      const int off = r * D + (swz_chunk<D>(r, c) << 3);
-      *(u32x4*)(q_lds + off) = qreg[i];
-      *(u32x4*)(do_lds + off) = doreg[i];
-    }
-    if (tid < kBwdBM) {
-      lse_lds[tid] = lse_r;
-      dd_lds[tid] = dd_r;
+    if (wave == 0 && lane < 32) {
+      const size_t pbase = ((size_t)b * a.Hq + hq) * (size_t)S_pad + q0;
+      const float* src = lane < 16 ? a.lse2 + pbase + 4 * lane : a.delta + pbase + 4 * (lane - 16);
+      dma16(reinterpret_cast<const uint16_t*>(src), reinterpret_cast<uint16_t*>(&sd_lds[st][0]));
     }
   };
 
@@ -177,131 +195,146 @@ void bwd_main_kernel(BwdArgs a) {
   }
   const float c = a.scale * kLog2e;  // signed: no running maximum is needed here
 
-  if (steps > 0) gload(0);
+  if (steps > 0) stage_in(0, 0);
   for (int step = 0; step < steps; ++step) {
-    sstore();
-    __syncthreads();  // this step's tiles are in LDS; the previous dQ product is done
-    const int g = step / per_head;
-    const int qt = q_first + step - g * per_head;
+    const int st = step & 1;
+    if (step == 0) {
+      wait_dma();
+    } else {
+      wait_dma_behind_atomics();
+    }
+    __syncthreads();  // this step's Q, dO, LSE, D are in LDS; the previous dQ product is done
+    const int g = step % G;
+    const int qt = nqt - 1 - step / G;
     const int hq = hkv * G + g;
     const int q0 = qt * kBwdBM;
-    if (step + 1 < steps) gload(step + 1);
+    const int qs = q0 + qh * 32;  // first query of this wave's half
+    if (step + 1 < steps) stage_in(step + 1, st ^ 1);
 
-    if (!CAUSAL || kw <= q0 + kBwdBM - 1) {
-      f32x16 s[2] = {f32x16{}, f32x16{}}, dp[2] = {f32x16{}, f32x16{}};
+    const uint16_t* Qs = q_lds[st];
+    const uint16_t* Os = do_lds[st];
+    if (!CAUSAL || kw <= qs + 31) {
+      // S = Q K^T and dP = dO V^T, 32 queries x 32 keys: register v holds query
+      // qs + (v/4)*8 + half*4 + v%4 of this lane's key column.
+      f32x16 sacc = f32x16{}, dpacc = f32x16{};
 #pragma unroll
       for (int ks = 0; ks < KSTEPS; ++ks) {
-        const int koff = swz<D>(wave * 32 + col, ks * 16 + half * 8);
-        const bf16x8 kf = *(const bf16x8*)(k_lds + koff);
-        const bf16x8 vf = *(const bf16x8*)(v_lds + koff);
-#pragma unroll
-        for (int qb = 0; qb < 2; ++qb) {
-          const int off = swz<D>(qb * 32 + col, ks * 16 + half * 8);
-          s[qb] = mfma32(*(const bf16x8*)(q_lds + off), kf, s[qb]);
-          dp[qb] = mfma32(*(const bf16x8*)(do_lds + off), vf, dp[qb]);
-        }
+        const int aoff = swz<D>(qh * 32 + col, ks * 16 + half * 8);
+        const int boff = swz<D>(kq * 32 + col, ks * 16 + half * 8);
+        sacc = mfma32(*(const bf16x8*)(Qs + aoff), *(const bf16x8*)(k_lds + boff), sacc);
+        dpacc = mfma32(*(const bf16x8*)(Os + aoff), *(const bf16x8*)(v_lds + boff), dpacc);
       }
-      const bool need_mask = (kw + 32 > S) || (q0 + kBwdBM > S) || (CAUSAL && kw + 31 > q0);
-      // P and dS, packed to bf16 as soon as they are formed.  Register v of query block
-      // qb holds query qb*32 + (v/4)*8 + half*4 + v%4; pb[qb][t] / sb[qb][t] hold
-      // registers v = 8t .. 8t+7, the B operand layout of the dV^T and dK^T products.
-      bf16x8 pb[2][2], sb[2][2];
+      const bool need_mask = (kw + 32 > S) || (qs + 32 > S) || (CAUSAL && kw + 31 > qs);
+      // P and dS packed to bf16: pb[t] / sb[t] hold registers v = 8t .. 8t+7, the B-operand
+      // layout of the dV^T and dK^T products; dS^T also goes to LDS for the dQ product.
+      bf16x8 pb[2], sb[2];
 #pragma unroll
-      for (int qb = 0; qb < 2; ++qb) {
+      for (int t = 0; t < 2; ++t) {
+        u32x4 wp, wsd;
 #pragma unroll
-        for (int t = 0; t < 2; ++t) {
-          u32x4 wp, wsd;
+        for (int gg = 0; gg < 2; ++gg) {
+          const int g4 = 2 * t + gg;
+          const int qr = qh * 32 + g4 * 8 + half * 4;
+          const f32x4 l4 = *(const f32x4*)(&sd_lds[st][qr]);
+          const f32x4 d4 = *(const f32x4*)(&sd_lds[st][kBwdBM + qr]);
+          float pv[4], dsv[4];
 #pragma unroll
-          for (int gg = 0; gg < 2; ++gg) {
-            const int g4 = 2 * t + gg;
-            const int qr = qb * 32 + g4 * 8 + half * 4;
-            const f32x4 l4 = *(const f32x4*)(lse_lds + qr);
-            const f32x4 d4 = *(const f32x4*)(dd_lds + qr);
-            float pv[4], dsv[4];
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              const int v = g4 * 4 + r;
-              float p = exp2_sm<EXPMODE>(fmaf(s[qb][v], c, -l4[r]));
-              if (need_mask) {
-                const int q = q0 + qr + r;
-                if (key >= S || q >= S || (CAUSAL && key > q)) p = 0.0f;
-              }
-              pv[r] = p;
-              dsv[r] = p * (dp[qb][v] - d4[r]);
+          for (int r = 0; r < 4; ++r) {
+            const int v = g4 * 4 + r;
+            float p = exp2_sm<EXPMODE>(fmaf(sacc[v], c, -l4[r]));
+            if (need_mask) {
+              const int q = q0 + qr + r;
+              if (key >= S || q >= S || (CAUSAL && key > q)) p = 0.0f;
             }
-            wp[2 * gg] = pack_bf16x2(pv[0], pv[1]);
-            wp[2 * gg + 1] = pack_bf16x2(pv[2], pv[3]);
-            wsd[2 * gg] = pack_bf16x2(dsv[0], dsv[1]);
-            wsd[2 * gg + 1] = pack_bf16x2(dsv[2], dsv[3]);
+            pv[r] = p;
+            dsv[r] = p * (dpacc[v] - d4[r]);
           }
-          pb[qb][t] = __builtin_bit_cast(bf16x8, wp);
-          sb[qb][t] = __builtin_bit_cast(bf16x8, wsd);
-          // dS^T -> LDS: row = this lane's key, 4 consecutive queries per 8-byte store.
-#pragma unroll
-          for (int gg = 0; gg < 2; ++gg) {
-            const u32x2 w = {wsd[2 * gg], wsd[2 * gg + 1]};
-            *(u32x2*)(dst_lds + swz<kBwdBM>(wave * 32 + col, qb * 32 + (2 * t + gg) * 8 + half * 4)) = w;
-          }
+          wp[2 * gg] = pack_bf16x2(pv[0], pv[1]);
+          wp[2 * gg + 1] = pack_bf16x2(pv[2], pv[3]);
+          wsd[2 * gg] = pack_bf16x2(dsv[0], dsv[1]);
+          wsd[2 * gg + 1] = pack_bf16x2(dsv[2], dsv[3]);
+          const u32x2 w2 = {wsd[2 * gg], wsd[2 * gg + 1]};
+          *(u32x2*)(dst_lds + swz<kBwdBM>(kq * 32 + col, qr)) = w2;
         }
+        pb[t] = __builtin_bit_cast(bf16x8, wp);
+        sb[t] = __builtin_bit_cast(bf16x8, wsd);
       }
-      // dV^T += dO^T P and dK^T += Q^T dS
+      // dV^T += dO^T P and dK^T += Q^T dS over this wave's 32 queries.
 #pragma unroll
-      for (int qb = 0; qb < 2; ++qb) {
+      for (int t = 0; t < 2; ++t) {
+        const int row = qh * 32 + t * 16 + trow;
 #pragma unroll
-        for (int t = 0; t < 2; ++t) {
-          const int row = qb * 32 + t * 16 + trow;
-#pragma unroll
-          for (int db = 0; db < DBLK; ++db) {
-            const int o0 = swz<D>(row, db * 32 + tcol), o1 = swz<D>(row + 8, db * 32 + tcol);
-            dv_acc[db] = mfma32(join(lds_read_tr16(do_lds + o0), lds_read_tr16(do_lds + o1)), pb[qb][t], dv_acc[db]);
-            dk_acc[db] = mfma32(join(lds_read_tr16(q_lds + o0), lds_read_tr16(q_lds + o1)), sb[qb][t], dk_acc[db]);
-          }
+        for (int db = 0; db < DBLK; ++db) {
+          const int o0 = swz<D>(row, db * 32 + tcol), o1 = swz<D>(row + 8, db * 32 + tcol);
+          dv_acc[db] = mfma32(join(lds_read_tr16(Os + o0), lds_read_tr16(Os + o1)), pb[t], dv_acc[db]);
+          dk_acc[db] = mfma32(join(lds_read_tr16(Qs + o0), lds_read_tr16(Qs + o1)), sb[t], dk_acc[db]);
         }
       }
     } else {
-      // All of this wave's keys lie above the tile's last query: its dS^T rows are zero.
+      // All of this wave's keys lie above its queries: its block of dS^T is zero.
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int id = i * 64 + lane;
-        *(u32x4*)(dst_lds + (wave * 32 + id / 8) * kBwdBM + (id % 8) * 8) = u32x4{0u, 0u, 0u, 0u};
+      for (int i = 0; i < 2; ++i) {
+        const int id = i * 64 + lane;  // 128 chunks of 16 bytes: 32 rows x 4 chunks
+        const int r = kq * 32 + id / 4;
+        *(u32x4*)(dst_lds + r * kBwdBM + (swz_chunk<kBwdBM>(r, qh * 4 + id % 4) << 3)) = u32x4{0u, 0u, 0u, 0u};
       }
     }
     __syncthreads();  // dS^T complete
 
-    // dQ[64 x D] += dS[64 x 128] K[128 x D]; wave -> query block (wave / 2) and NDB d-blocks.
+    // dQ[64 x D] += dS[64 x 128] K[128 x D]: wave -> (query block qh, d-block kq) for
+    // D = 128; for D = 64 the four waves of query half qh split 2 d-blocks x 2 key halves
+    // and the key halves add into the accumulator separately.
     {
-      const int qbw = wave >> 1;
-      f32x16 dq[NDB];
+      constexpr int KK = DBLK == 4 ? 8 : 4;  // 16-key steps per wave
+      const int db = DBLK == 4 ? kq : (kq & 1);
+      const int kk0 = DBLK == 4 ? 0 : (kq >> 1) * 4;
+      f32x16 dq = f32x16{};
 #pragma unroll
-      for (int n = 0; n < NDB; ++n) dq[n] = f32x16{};
-#pragma unroll
-      for (int kk = 0; kk < kBwdBN / 16; ++kk) {
-        const int row = kk * 16 + trow;
-        const bf16x8 sa = join(lds_read_tr16(dst_lds + swz<kBwdBM>(row, qbw * 32 + tcol)),
-                               lds_read_tr16(dst_lds + swz<kBwdBM>(row + 8, qbw * 32 + tcol)));
-#pragma unroll
-        for (int n = 0; n < NDB; ++n) {
-          const int db = (wave & 1) * NDB + n;
-          const bf16x8 kb = join(lds_read_tr16(k_lds + swz<D>(row, db * 32 + tcol)),
-                                 lds_read_tr16(k_lds + swz<D>(row + 8, db * 32 + tcol)));
-          dq[n] = mfma32(sa, kb, dq[n]);
-        }
+      for (int i = 0; i < KK; ++i) {
+        const int row = (kk0 + i) * 16 + trow;
+        const bf16x8 sa = join(lds_read_tr16(dst_lds + swz<kBwdBM>(row, qh * 32 + tcol)),
+                               lds_read_tr16(dst_lds + swz<kBwdBM>(row + 8, qh * 32 + tcol)));
+        const bf16x8 kb = join(lds_read_tr16(k_lds + swz<D>(row, db * 32 + tcol)),
+                               lds_read_tr16(k_lds + swz<D>(row + 8, db * 32 + tcol)));
+        dq = mfma32(sa, kb, dq);
       }
-      float* dqa = a.dq_acc + ((size_t)b * a.Hq + hq) * (size_t)S * D;
+      // Exactly kDqAtomics atomic instructions per wave (see wait_dma_behind_atomics):
+      // rows past the end of the sequence add 0 to the last row instead of branching.
+      float* dqa = a.dq_acc + ((size_t)b * a.Hq + hq) * (size_t)S * D + db * 32 + col;
 #pragma unroll
-      for (int n = 0; n < NDB; ++n) {
-        const int dcol = ((wave & 1) * NDB + n) * 32 + col;
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int q = q0 + qbw * 32 + (v >> 2) * 8 + half * 4 + (v & 3);
-          if (q < S) atomicAdd(dqa + (size_t)q * D + dcol, dq[n][v]);
-        }
+      for (int v = 0; v < kDqAtomics; ++v) {
+        const int q = qs + (v >> 2) * 8 + half * 4 + (v & 3);
+        atomicAdd(dqa + (size_t)min(q, S - 1) * D, q < S ? dq[v] : 0.0f);
       }
     }
   }
 
-  // dK = scale dK_acc, dV = dV_acc.
-  if (key < S) {
+  // Add the two query halves' partial dK, dV through LDS (the Q/dO stages are free now),
+  // then dK = scale dK_acc, dV = dV_acc.
+  float* red = reinterpret_cast<float*>(&q_lds[0][0]);  // 4 waves x DBLK x 16 x 64 floats
+  static_assert(sizeof(q_lds) + sizeof(do_lds) >= 4 * DBLK * 16 * 64 * sizeof(float), "reduction space");
+  __syncthreads();
+#pragma unroll
+  for (int pass = 0; pass < 2; ++pass) {
+    f32x16* acc = pass == 0 ? dv_acc : dk_acc;
+    if (qh == 1) {
+#pragma unroll
+      for (int db = 0; db < DBLK; ++db) {
+#pragma unroll
+        for (int v = 0; v < 16; ++v) red[((kq * DBLK + db) * 16 + v) * 64 + lane] = acc[db][v];
+      }
+    }
+    __syncthreads();
+    if (qh == 0) {
+#pragma unroll
+      for (int db = 0; db < DBLK; ++db) {
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[db][v] += red[((kq * DBLK + db) * 16 + v) * 64 + lane];
+      }
+    }
+    __syncthreads();
+  }
+  if (qh == 0 && key < S) {
     const float ks = a.scale;
     uint16_t* dkr = a.dk + kvbase + (size_t)key * D;
     uint16_t* dvr = a.dv + kvbase + (size_t)key * D;
@@ -341,14 +374,16 @@ hipError_t launch_bwd_t(const BwdArgs& a, int phases, hipStream_t stream) {
   const long rows = (long)a.B * a.Hq * a.S;
   hipError_t e = hipSuccess;
   if (phases & 1) {
-    const long pre_threads = rows * (D / 8);
+    const int S_pad = (a.S + kBwdBM - 1) / kBwdBM * kBwdBM;
+    const long prows = (long)a.B * a.Hq * S_pad;
+    const long pre_threads = prows * (D / 8);
     hipLaunchKernelGGL(bwd_pre_kernel<D>, dim3((unsigned)((pre_threads + 255) / 256)), dim3(256), 0, stream,
-                       a.o, a.dO, a.delta, a.dq_acc, rows);
+                       a.o, a.dO, a.lse, a.delta, a.lse2, a.dq_acc, prows, a.S, S_pad);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   if (phases & 2) {
     const int nkt = (a.S + kBwdBN - 1) / kBwdBN;
-    hipLaunchKernelGGL((bwd_main_kernel<D, CAUSAL, EXPMODE>), dim3((unsigned)(nkt * a.B * a.Hkv)), dim3(256), 0,
+    hipLaunchKernelGGL((bwd_main_kernel<D, CAUSAL, EXPMODE>), dim3((unsigned)(nkt * a.B * a.Hkv)), dim3(512), 0,
                        stream, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }

@@ -132,6 +132,37 @@ __device__ __forceinline__ int swz(int r, int col) {
   return r * D + (swz_chunk<D>(r, col >> 3) << 3) + (col & 7);
 }
 
+// ---------------------------------------------------------------------------------
+// Global -> LDS DMA (global_load_lds_dwordx4): lane l of the wave copies 16 bytes from
+// its global address g to LDS bytes [lds_wave_base + 16 l, +16).  It is issued from an
+// asm block so that the compiler, which cannot tell which LDS bytes the DMA writes, does
+// not make every later LDS read wait for it.  The block has no register outputs; the
+// LDS it writes is read only after wait_dma()/vmcnt waits and a barrier, which the
+// kernels place explicitly.  lds_wave_base must be the same for all lanes of the wave.
+// ---------------------------------------------------------------------------------
+__device__ __forceinline__ void dma16(const void* g, const void* lds_wave_base) {
+  const uint32_t l = (uint32_t)(size_t)(const __attribute__((address_space(3))) void*)lds_wave_base;
+  const uint32_t ls = __builtin_amdgcn_readfirstlane(l);
+  __asm__ volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
+                   :
+                   : "s"(ls), "v"(g)
+                   : "memory", "m0");
+}
+
+// The same with a scalar (wave-uniform) 64-bit base and a 32-bit per-lane byte offset:
+// no per-lane address arithmetic when the offsets stay fixed across a loop.
+__device__ __forceinline__ void dma16_s(const void* sbase, uint32_t voff, const void* lds_wave_base) {
+  const uint32_t l = (uint32_t)(size_t)(const __attribute__((address_space(3))) void*)lds_wave_base;
+  const uint32_t ls = __builtin_amdgcn_readfirstlane(l);
+  __asm__ volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
+                   :
+                   : "s"(ls), "v"(voff), "s"(sbase)
+                   : "memory", "m0");
+}
+
+// Wait until every DMA (and every other vector memory operation) of the wave is done.
+__device__ __forceinline__ void wait_dma() { __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
   bf16x2 r;

@@ -38,19 +38,25 @@ namespace attn {
 namespace {
 
 constexpr int kFwdWaves = 4;
-constexpr int kFwdBM = 32 * kFwdWaves;  // queries per workgroup
-constexpr int kFwdBN = 64;              // keys per LDS tile
+constexpr int kFwdBN = 64;  // keys per LDS tile
 
-template <int D, bool CAUSAL, int EXPMODE>
-__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(2, 2)))
+
+// NQB = 32-query column blocks per wave.  NQB = 2 reuses every K and V operand read
+// from LDS for two MFMAs (half the LDS traffic per MFMA) at twice the registers, so it
+// runs one wave per SIMD; NQB = 1 runs two.
+template <int D, bool CAUSAL, int EXPMODE, int NQB>
+__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(NQB == 1 ? 2 : 1, NQB == 1 ? 2 : 1)))
 void fwd_kernel(FwdArgs a) {
   constexpr int BN = kFwdBN;
-  constexpr int KSTEPS = D / 16;  // MFMA k-steps of S^T = K Q^T
-  constexpr int DBLK = D / 32;    // 32-row blocks of O^T
-  constexpr int CPR = D / 8;      // 16-byte chunks per row
-  constexpr int TILE = BN * D;    // bf16 elements of one K or V tile
-  constexpr int LOADS = BN * CPR / 256;
-  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * 2 * TILE];  // [stage][K|V][BN][D]
+  constexpr int WQ = 32 * NQB;          // queries per wave
+  constexpr int BM = WQ * kFwdWaves;    // queries per workgroup
+  constexpr int KSTEPS = D / 16;        // MFMA k-steps of S^T = K Q^T
+  constexpr int DBLK = D / 32;          // 32-row blocks of O^T
+  constexpr int CPR = D / 8;            // 16-byte chunks per row
+  constexpr int TILE = BN * D;          // bf16 elements of one K or V tile
+  constexpr int DMAS = BN * CPR / 256;  // 16-byte chunks per thread per tile
+  // K ring (2 tiles) then V ring (2 tiles), each tile [BN][D] with swizzled chunks.
+  __shared__ __attribute__((aligned(1024))) uint16_t smem[4 * TILE];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -59,7 +65,7 @@ void fwd_kernel(FwdArgs a) {
   const int half = lane >> 5;
 
   const int nbh = a.B * a.Hq;
-  const int nqt = (a.S + kFwdBM - 1) / kFwdBM;
+  const int nqt = (a.S + BM - 1) / BM;
   const int bid = blockIdx.x;
   const int qt = CAUSAL ? (nqt - 1 - bid / nbh) : (bid / nbh);
   const int bh = bid % nbh;
@@ -67,59 +73,63 @@ void fwd_kernel(FwdArgs a) {
   const int hq = bh - b * a.Hq;
   const int hkv = hq / (a.Hq / a.Hkv);
   const int S = a.S;
-  const int q0 = qt * kFwdBM;
-  const int qw = q0 + wave * 32;
-  const int qi = qw + col;  // this lane's query
+  const int q0 = qt * BM;
+  const int qw = q0 + wave * WQ;  // first query of this wave; block qb holds qw + 32 qb ..
   const size_t qbase = ((size_t)b * a.Hq + hq) * (size_t)S * D;
   const size_t kvbase = ((size_t)b * a.Hkv + hkv) * (size_t)S * D;
   const uint16_t* __restrict__ Kg = a.k + kvbase;
   const uint16_t* __restrict__ Vg = a.v + kvbase;
 
-  // Q^T fragments (B operand): query qi, d = ks*16 + half*8 .. +7.
-  bf16x8 qf[KSTEPS];
+  // Q^T fragments (B operand): query qw + 32 qb + col, d = ks*16 + half*8 .. +7.
+  bf16x8 qf[NQB][KSTEPS];
 #pragma unroll
-  for (int ks = 0; ks < KSTEPS; ++ks) {
-    u32x4 w = {0u, 0u, 0u, 0u};
-    if (qi < S) {
-      w = *(const u32x4*)(a.q + qbase + (size_t)qi * D + ks * 16 + half * 8);
-      w = (w & a.q_and) ^ a.q_xor;
+  for (int qb = 0; qb < NQB; ++qb) {
+    const int qi = qw + qb * 32 + col;
+    // Rows past the end of the sequence load the last row instead (their outputs are
+    // never stored); no branch, so all the loads are in flight together.
+    const u32x4* qrow = (const u32x4*)(a.q + qbase + (size_t)min(qi, S - 1) * D + half * 8);
+#pragma unroll
+    for (int ks = 0; ks < KSTEPS; ++ks) {
+      const u32x4 w = (qrow[ks * 2] & a.q_and) ^ a.q_xor;
+      qf[qb][ks] = __builtin_bit_cast(bf16x8, w);
     }
-    qf[ks] = __builtin_bit_cast(bf16x8, w);
   }
 
-  const int kv_end = CAUSAL ? min(S, q0 + kFwdBM) : S;
+  const int kv_end = CAUSAL ? min(S, q0 + BM) : S;
   const int nkv = (kv_end + BN - 1) / BN;
 
-  // Global -> register staging of one K tile and one V tile (16-byte chunks, rows past
-  // the end of the sequence are zero so that masked probabilities meet finite values).
-  u32x4 kreg[LOADS], vreg[LOADS];
-  auto gload = [&](int j) {
+  // DMA of one tile into a ring slot.  Thread tid, chunk i covers LDS chunk
+  // p = (i * 4 + wave) * 64 + lane = (row, physical chunk); it fetches the logical chunk
+  // physical ^ f(row) of key row j*BN + row.  The per-lane byte offsets within a tile
+  // are fixed, the tile base is a scalar; only the last tile, if it runs past the end of
+  // the sequence, clamps its rows to a real row (their scores are masked, so any finite
+  // data will do).
+  uint32_t dma_off[DMAS];
 #pragma unroll
-    for (int i = 0; i < LOADS; ++i) {
-      const int id = i * 256 + tid;
-      const int r = id / CPR, c = id % CPR;
-      const int key = j * BN + r;
-      if (key < S) {
-        kreg[i] = *(const u32x4*)(Kg + (size_t)key * D + c * 8);
-        vreg[i] = *(const u32x4*)(Vg + (size_t)key * D + c * 8);
-      } else {
-        kreg[i] = u32x4{0u, 0u, 0u, 0u};
-        vreg[i] = u32x4{0u, 0u, 0u, 0u};
+  for (int i = 0; i < DMAS; ++i) {
+    const int pch = (i * 4 + wave) * 64 + lane;
+    const int r = pch / CPR;
+    dma_off[i] = (uint32_t)(r * D + swz_chunk<D>(r, pch % CPR) * 8) * 2u;
+  }
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  auto dma_tile = [&](const uint16_t* __restrict__ src, int j, uint16_t* slot) {
+    const uint16_t* base = src + (size_t)j * BN * D;
+    if (j * BN + BN <= S) {
+#pragma unroll
+      for (int i = 0; i < DMAS; ++i) dma16_s(base, dma_off[i], slot + (i * 4 + wave_u) * 512);
+    } else {
+#pragma unroll
+      for (int i = 0; i < DMAS; ++i) {
+        const int pch = (i * 4 + wave) * 64 + lane;
+        const int r = pch / CPR;
+        const int rc = min(j * BN + r, S - 1) - j * BN;
+        const uint32_t off = (uint32_t)(rc * D + swz_chunk<D>(r, pch % CPR) * 8) * 2u;
+        dma16_s(base, off, slot + (i * 4 + wave_u) * 512);
       }
     }
   };
-  auto sstore = [&](int stage) {
-    uint16_t* Ks = smem + stage * 2 * TILE;
-    uint16_t* Vs = Ks + TILE;
-#pragma unroll
-    for (int i = 0; i < LOADS; ++i) {
-      const int id = i * 256 + tid;
-      const int r = id / CPR, c = id % CPR;
-      const int off = r * D + (swz_chunk<D>(r, c) << 3);
-      *(u32x4*)(Ks + off) = kreg[i];
-      *(u32x4*)(Vs + off) = vreg[i];
-    }
-  };
+  uint16_t* const Kring = smem;
+  uint16_t* const Vring = smem + 2 * TILE;
 
   // Per-lane parts of the V^T transpose-read addresses (see attn_device.h): source
   // lane s reads 4 d-values of key row (s / 32) * 4 + (s % 16) / 4 (+ 8 for the second
@@ -127,135 +137,194 @@ void fwd_kernel(FwdArgs a) {
   const int vrow = (lane >> 5) * 4 + ((lane >> 2) & 3);
   const int vcol = ((lane >> 4) & 1) * 16 + (lane & 3) * 4;
 
-  f32x16 oacc[DBLK];
+  f32x16 oacc[NQB][DBLK];
+  float m_ref[NQB], l_run[NQB];
 #pragma unroll
-  for (int db = 0; db < DBLK; ++db) oacc[db] = f32x16{};
-  float m_ref = -INFINITY;  // reference row maximum, log2 units (scaled scores)
-  float l_part = 0.0f;      // this lane's part of the running row sum
+  for (int qb = 0; qb < NQB; ++qb) {
+#pragma unroll
+    for (int db = 0; db < DBLK; ++db) oacc[qb][db] = f32x16{};
+    m_ref[qb] = -INFINITY;  // reference row maximum, log2 units (scaled scores)
+    l_run[qb] = 0.0f;       // this lane's part of the running row sum
+  }
   const float c = a.c;
   const float tau = a.tau;
 
-  gload(0);
-  sstore(0);
-  __syncthreads();
-
-  for (int j = 0; j < nkv; ++j) {
-    const int stage = j & 1;
-    if (j + 1 < nkv) gload(j + 1);
-    const int k0 = j * BN;
-    // A wave skips tiles whose keys all lie above its last query (causal).
-    if (!CAUSAL || k0 <= qw + 31) {
-      const uint16_t* Ks = smem + stage * 2 * TILE;
-      const uint16_t* Vs = Ks + TILE;
-
-      f32x16 s[2] = {f32x16{}, f32x16{}};
+  // S^T = K Q^T for every query block: each K fragment read from LDS feeds NQB MFMAs.
+  auto qk = [&](const uint16_t* Ks, f32x16 (*s)[2]) {
 #pragma unroll
-      for (int ks = 0; ks < KSTEPS; ++ks) {
+    for (int qb = 0; qb < NQB; ++qb) s[qb][0] = s[qb][1] = f32x16{};
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-          const bf16x8 ka = *(const bf16x8*)(Ks + swz<D>(kb * 32 + col, ks * 16 + half * 8));
-          s[kb] = mfma32(ka, qf[ks], s[kb]);
-        }
+    for (int ks = 0; ks < KSTEPS; ++ks) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const bf16x8 ka = *(const bf16x8*)(Ks + swz<D>(kb * 32 + col, ks * 16 + half * 8));
+#pragma unroll
+        for (int qb = 0; qb < NQB; ++qb) s[qb][kb] = mfma32(ka, qf[qb][ks], s[qb][kb]);
       }
-
-      const bool need_mask = (k0 + BN > S) || (CAUSAL && k0 + BN - 1 > qw);
-      if (need_mask) {
+    }
+  };
+  auto mask = [&](f32x16 (*s)[2], int k0) {
+    if ((k0 + BN > S) || (CAUSAL && k0 + BN - 1 > qw)) {
+#pragma unroll
+      for (int qb = 0; qb < NQB; ++qb) {
+        const int qi = qw + qb * 32 + col;
+        const int lim_s = S - 1 - k0 - half * 4;               // key <= S - 1
+        const int lim = CAUSAL ? min(lim_s, qi - k0 - half * 4) : lim_s;  // key <= query
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
           for (int v = 0; v < 16; ++v) {
-            const int key = k0 + kb * 32 + (v >> 2) * 8 + half * 4 + (v & 3);
-            if (key >= S || (CAUSAL && key > qi)) s[kb][v] = -INFINITY;
+            const int e = kb * 32 + (v >> 2) * 8 + (v & 3);  // key - k0 - half*4
+            s[qb][kb][v] = e > lim ? -INFINITY : s[qb][kb][v];
           }
         }
       }
+    }
+  };
+  // P = 2^(s c - m) packed to bf16 in the B-operand layout of O^T += V^T P^T.
+  auto softmax_exp = [&](const f32x16* s, float m, bf16x8 (*pf)[2]) {
+    float lt = 0.0f;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        u32x4 w;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float p0 = exp2_sm<EXPMODE>(fmaf(s[kb][t * 8 + 2 * e], c, -m));
+          const float p1 = exp2_sm<EXPMODE>(fmaf(s[kb][t * 8 + 2 * e + 1], c, -m));
+          lt += p0 + p1;
+          w[e] = pack_bf16x2(p0, p1);
+        }
+        pf[kb][t] = __builtin_bit_cast(bf16x8, w);
+      }
+    }
+    return lt;
+  };
 
+  // Prologue: K_0, V_0, K_1 in flight; S_0 computed.
+  dma_tile(Kg, 0, Kring);
+  dma_tile(Vg, 0, Vring);
+  if (nkv > 1) dma_tile(Kg, 1, Kring + TILE);
+  wait_dma();
+  __syncthreads();
+  f32x16 sc[NQB][2];
+  qk(Kring, sc);
+  mask(sc, 0);
+
+  for (int j = 0; j < nkv; ++j) {
+    // Free slots: K_j's (read by the previous step's QK) and V_{j-1}'s (read by its PV).
+    if (j + 2 < nkv) dma_tile(Kg, j + 2, Kring + (j & 1) * TILE);
+    if (j + 1 < nkv) dma_tile(Vg, j + 1, Vring + ((j + 1) & 1) * TILE);
+    // Free slots: K_j's (read by the previous step's QK) and V_{j-1}'s (read by its PV).
+
+    // Running maximum and the (rare) rescale, before the step's main block.  One
+    // wave-uniform branch covers every query block of the wave.
+    float mt[NQB];
+    bool grow = false;
+#pragma unroll
+    for (int qb = 0; qb < NQB; ++qb) {
       float mx = -INFINITY;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
-        for (int v = 0; v < 16; ++v) mx = fmaxf(mx, s[kb][v]);
+        for (int v = 0; v < 16; ++v) mx = fmaxf(mx, sc[qb][kb][v]);
       }
-      mx = max_halves(mx);
-      const float mt = mx * c;
-      if (wave_any(mt > m_ref + tau)) {
-        const float m_new = fmaxf(m_ref, mt);
-        const float alpha = (m_new == -INFINITY) ? 1.0f : exp2_sm<0>(m_ref - m_new);
+      mt[qb] = max_halves(mx) * c;
+      grow = grow || (mt[qb] > m_ref[qb] + tau);
+    }
+    if (wave_any(grow)) {
 #pragma unroll
-        for (int db = 0; db < DBLK; ++db) oacc[db] *= alpha;
-        l_part *= alpha;
-        m_ref = m_new;
-      }
-      const float mu = (m_ref == -INFINITY) ? 0.0f : m_ref;
-
-      bf16x8 pf[2][2];
+      for (int qb = 0; qb < NQB; ++qb) {
+        const float m_new = fmaxf(m_ref[qb], mt[qb]);
+        const float alpha = (m_new == -INFINITY) ? 1.0f : exp2_sm<0>(m_ref[qb] - m_new);
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-          u32x4 w;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const float p0 = exp2_sm<EXPMODE>(fmaf(s[kb][t * 8 + 2 * e], c, -mu));
-            const float p1 = exp2_sm<EXPMODE>(fmaf(s[kb][t * 8 + 2 * e + 1], c, -mu));
-            l_part += p0 + p1;
-            w[e] = pack_bf16x2(p0, p1);
-          }
-          pf[kb][t] = __builtin_bit_cast(bf16x8, w);
-        }
-      }
-
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-          const int row = kb * 32 + t * 16 + vrow;
-#pragma unroll
-          for (int db = 0; db < DBLK; ++db) {
-            const i16x4 lo = lds_read_tr16(Vs + swz<D>(row, db * 32 + vcol));
-            const i16x4 hi = lds_read_tr16(Vs + swz<D>(row + 8, db * 32 + vcol));
-            oacc[db] = mfma32(join(lo, hi), pf[kb][t], oacc[db]);
-          }
-        }
+        for (int db = 0; db < DBLK; ++db) oacc[qb][db] *= alpha;
+        l_run[qb] *= alpha;
+        m_ref[qb] = m_new;
       }
     }
-    if (j + 1 < nkv) sstore(stage ^ 1);
+
+    // Main block, free of branches: S_{j+1} = K_{j+1} Q^T on the matrix cores (its slot
+    // holds stale data on the last step; the result is then unused) while the vector
+    // units exponentiate S_j; then O^T += V_j^T P_j^T.
+    f32x16 sn[NQB][2];
+    qk(Kring + ((j + 1) & 1) * TILE, sn);
+    bf16x8 pf[NQB][2][2];
+#pragma unroll
+    for (int qb = 0; qb < NQB; ++qb)
+      l_run[qb] += softmax_exp(sc[qb], m_ref[qb] == -INFINITY ? 0.0f : m_ref[qb], pf[qb]);
+
+    const uint16_t* Vs = Vring + (j & 1) * TILE;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const int row = kb * 32 + t * 16 + vrow;
+#pragma unroll
+        for (int db = 0; db < DBLK; ++db) {
+          const bf16x8 va = join(lds_read_tr16(Vs + swz<D>(row, db * 32 + vcol)),
+                                 lds_read_tr16(Vs + swz<D>(row + 8, db * 32 + vcol)));
+#pragma unroll
+          for (int qb = 0; qb < NQB; ++qb) oacc[qb][db] = mfma32(va, pf[qb][kb][t], oacc[qb][db]);
+        }
+        // Bound the transpose reads in flight to one 16-key sub-block (register budget).
+        if (kb * 2 + t < 3) __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    wait_dma();
     __syncthreads();
+#pragma unroll
+    for (int qb = 0; qb < NQB; ++qb) {
+      sc[qb][0] = sn[qb][0];
+      sc[qb][1] = sn[qb][1];
+    }
+    if (j + 1 < nkv) mask(sc, (j + 1) * BN);
   }
 
   // Epilogue: O = O_acc / l (bf16, round to nearest even) and LSE in natural log.
-  const float l = sum_halves(l_part);
-  const float inv = 1.0f / l;
-  if (qi < S) {
-    uint16_t* orow = a.o + qbase + (size_t)qi * D;
 #pragma unroll
-    for (int db = 0; db < DBLK; ++db) {
+  for (int qb = 0; qb < NQB; ++qb) {
+    const int qi = qw + qb * 32 + col;
+    const float l = sum_halves(l_run[qb]);
+    const float inv = 1.0f / l;
+    if (qi < S) {
+      uint16_t* orow = a.o + qbase + (size_t)qi * D;
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        u32x2 w;
-        w[0] = pack_bf16x2(oacc[db][g * 4 + 0] * inv, oacc[db][g * 4 + 1] * inv);
-        w[1] = pack_bf16x2(oacc[db][g * 4 + 2] * inv, oacc[db][g * 4 + 3] * inv);
-        *(u32x2*)(orow + db * 32 + g * 8 + half * 4) = w;
+      for (int db = 0; db < DBLK; ++db) {
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          u32x2 w;
+          w[0] = pack_bf16x2(oacc[qb][db][g * 4 + 0] * inv, oacc[qb][db][g * 4 + 1] * inv);
+          w[1] = pack_bf16x2(oacc[qb][db][g * 4 + 2] * inv, oacc[qb][db][g * 4 + 3] * inv);
+          *(u32x2*)(orow + db * 32 + g * 8 + half * 4) = w;
+        }
       }
+      if (half == 0) a.lse[((size_t)b * a.Hq + hq) * S + qi] = (m_ref[qb] + log2f(l)) * kLn2;
     }
-    if (half == 0) a.lse[((size_t)b * a.Hq + hq) * S + qi] = (m_ref + log2f(l)) * kLn2;
   }
 }
 
-template <int D, bool CAUSAL, int EXPMODE>
+template <int D, bool CAUSAL, int EXPMODE, int NQB>
 hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t stream) {
-  const int nqt = (a.S + kFwdBM - 1) / kFwdBM;
+  constexpr int BM = 32 * NQB * kFwdWaves;
+  const int nqt = (a.S + BM - 1) / BM;
   const dim3 grid((unsigned)(nqt * a.B * a.Hq));
-  hipLaunchKernelGGL((fwd_kernel<D, CAUSAL, EXPMODE>), grid, dim3(256), 0, stream, a);
+  hipLaunchKernelGGL((fwd_kernel<D, CAUSAL, EXPMODE, NQB>), grid, dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 
+#ifndef FWD_NQB
+#define FWD_NQB 1
+#endif
+
 template <int D>
 hipError_t launch_fwd_d(const FwdArgs& a, bool causal, int exp_mode, hipStream_t stream) {
+  constexpr int N = FWD_NQB;
   if (causal) {
-    return exp_mode == 0 ? launch_fwd_t<D, true, 0>(a, stream) : launch_fwd_t<D, true, 1>(a, stream);
+    return exp_mode == 0 ? launch_fwd_t<D, true, 0, N>(a, stream) : launch_fwd_t<D, true, 1, N>(a, stream);
   }
-  return exp_mode == 0 ? launch_fwd_t<D, false, 0>(a, stream) : launch_fwd_t<D, false, 1>(a, stream);
+  return exp_mode == 0 ? launch_fwd_t<D, false, 0, N>(a, stream) : launch_fwd_t<D, false, 1, N>(a, stream);
 }
 
 __global__ void exp2_eval_kernel(const float* x, float* y, long n, int mode) {

@@ -34,7 +34,8 @@ struct BwdArgs {
   uint16_t* dk;
   uint16_t* dv;
   float* dq_acc;  // [B,Hq,S,d] fp32 workspace
-  float* delta;   // [B,Hq,S] fp32 workspace: D_i = <dO_i, O_i>
+  float* delta;   // [B*Hq][S_pad] fp32 workspace: D_i = <dO_i, O_i> (S_pad = S rounded up to 64)
+  float* lse2;    // [B*Hq][S_pad] fp32 workspace: LSE_i * log2(e)
   int B, Hq, Hkv, S;
   float c;        // |scale| * log2(e) (1 for a zero scale)
   float scale;    // the caller's scale (dQ and dK carry it)

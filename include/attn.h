@@ -108,8 +108,9 @@ int attn_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse
 
 /*
  * Bytes of device workspace attn_bwd needs for these sizes: an fp32 dQ
- * accumulator [B,Hq,S,d] and the fp32 row terms D_i = <dO_i, O_i> [B,Hq,S],
- * each rounded up to 256 bytes.  Returns 0 for invalid or empty sizes.
+ * accumulator [B,Hq,S,d], then two fp32 row arrays [B*Hq][S_pad] (the row terms
+ * D_i = <dO_i, O_i> and LSE_i log2(e), S_pad = S rounded up to a multiple of 64),
+ * each part rounded up to 256 bytes.  Returns 0 for invalid or empty sizes.
  */
 size_t attn_bwd_workspace_bytes(int B, int Hq, int Hkv, int S, int d);
 
@@ -138,8 +139,10 @@ int attn_bwd_ex(const void* q, const void* k, const void* v, const void* o, cons
  * separately.  Running ATTN_BWD_PREPROCESS, ATTN_BWD_MAIN and ATTN_BWD_DQ_CONVERT in
  * that order on one stream, with the same arguments and workspace, is exactly
  * attn_bwd_ex (ATTN_BWD_ALL).  The phases communicate through the workspace:
- *   PREPROCESS  reads o, dO; writes D = rowsum(dO * O) and zeroes the dQ accumulator;
- *   MAIN        reads q, k, v, lse, dO and D; writes dk, dv; adds into the accumulator;
+ *   PREPROCESS  reads o, dO, lse; writes D = rowsum(dO * O), LSE log2(e) and a zeroed
+ *               dQ accumulator;
+ *   MAIN        reads q, k, v, dO, D and LSE log2(e); writes dk, dv; adds into the
+ *               accumulator;
  *   DQ_CONVERT  reads the accumulator; writes dq.
  * Arguments are validated as for attn_bwd_ex; an unknown phase is ATTN_ERR_UNSUPPORTED.
  */

@@ -95,7 +95,8 @@ def test_workspace_bytes():
     B, Hq, Hkv, S, d = 2, 4, 2, 100, 128
     rows = B * Hq * S
     rup = lambda x: (x + 255) // 256 * 256
-    assert ea.attn_bwd_workspace_bytes(B, Hq, Hkv, S, d) == rup(rows * d * 4) + rup(rows * 4)
+    prows = B * Hq * ((S + 63) // 64 * 64)
+    assert ea.attn_bwd_workspace_bytes(B, Hq, Hkv, S, d) == rup(rows * d * 4) + 2 * rup(prows * 4)
     assert ea.attn_bwd_workspace_bytes(0, Hq, Hkv, S, d) == 0
     assert ea.attn_bwd_workspace_bytes(B, 3, 2, S, d) == 0
     assert ea.attn_bwd_workspace_bytes(B, Hq, Hkv, S, 80) == 0
