@@ -2,14 +2,15 @@
 
 One step is one pass of the whole path over one batch of seeded synthetic inputs
 already resident in device memory: attn_fwd (O, LSE) then the three backward launches
-(preprocess, main, dQ convert) giving dQ, dK, dV.
+(preprocess, dK/dV main kernel, dQ kernel) giving dQ, dK, dV.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
 
 Prints one JSON line.  value = algorithmic TFLOP/s of the step, where a step's flop
 count is fwd + bwd with fwd = 4*B*Hq*S^2*d (halved when causal) and bwd = 2.5 * fwd.
-The roofline object is for the dominant kernel (the backward main kernel, timed with
-HIP events on the stream it runs on, inside the timed region).  cpu_baseline is the
+The roofline object is for the dominant kernel (the backward dK/dV kernel, timed with
+HIP events on the stream it runs on, inside the timed region; its algorithmic flop is
+the four products it performs, 2.0x the forward's).  cpu_baseline is the
 fp64 oracle timed on this host on a bounded sample of the same workload.
 """
 
@@ -135,7 +136,7 @@ def main():
         if ev:
             ev[1].record(stream)
         if do_bwd:
-            for ph, e in ((ea.ATTN_BWD_PREPROCESS, 2), (ea.ATTN_BWD_MAIN, 3), (ea.ATTN_BWD_DQ_CONVERT, 4)):
+            for ph, e in ((ea.ATTN_BWD_PREPROCESS, 2), (ea.ATTN_BWD_MAIN, 3), (ea.ATTN_BWD_DQ, 4)):
                 ea.attn_bwd_phase(ph, q, k, v, o, lse, do, w.scale, w.causal, dq, dk, dv, ws, opt=opt, stream=stream)
                 if ev:
                     ev[e].record(stream)
@@ -157,14 +158,17 @@ def main():
     if do_bwd:
         phase_ms["bwd_pre"] = sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps
         phase_ms["bwd_main"] = sum(e[2].elapsed_time(e[3]) for e in evs) / args.steps
-        phase_ms["dq_convert"] = sum(e[3].elapsed_time(e[4]) for e in evs) / args.steps
+        phase_ms["bwd_dq"] = sum(e[3].elapsed_time(e[4]) for e in evs) / args.steps
     fwd_tf = w.fwd_flop() / (fwd_ms * 1e-3) / 1e12
     flop = w.fwd_flop() + (w.bwd_flop() if do_bwd else 0.0)
     value = flop / (ms_step * 1e-3) / 1e12
 
     if do_bwd:
+        # The dK/dV kernel performs four of the backward's five counted products (S, dP,
+        # dV, dK): 2.0x the forward's flop; the dQ kernel does the fifth (plus recomputing S
+        # and dP, which the flop convention does not count).
         main_ms = phase_ms["bwd_main"]
-        achieved = w.bwd_flop() / (main_ms * 1e-3) / 1e12
+        achieved = 2.0 * w.fwd_flop() / (main_ms * 1e-3) / 1e12
         dominant = "bwd_main_kernel"
     else:
         main_ms = fwd_ms

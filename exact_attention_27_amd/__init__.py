@@ -181,7 +181,7 @@ def attn_bwd_workspace_bytes(B: int, Hq: int, Hkv: int, S: int, d: int) -> int:
     return int(lib().attn_bwd_workspace_bytes(B, Hq, Hkv, S, d))
 
 
-ATTN_BWD_ALL, ATTN_BWD_PREPROCESS, ATTN_BWD_MAIN, ATTN_BWD_DQ_CONVERT = 0, 1, 2, 3
+ATTN_BWD_ALL, ATTN_BWD_PREPROCESS, ATTN_BWD_MAIN, ATTN_BWD_DQ = 0, 1, 2, 3
 
 
 def attn_bwd_ex(q, k, v, o, lse, do, scale: Optional[float] = None, causal: bool = False,

@@ -115,9 +115,8 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
 size_t attn_bwd_workspace_bytes(int B, int Hq, int Hkv, int S, int d) {
   bool empty = false;
   if (check_sizes(B, Hq, Hkv, S, d, &empty) != ATTN_OK || empty) return 0;
-  const size_t rows = (size_t)B * Hq * S;
   const size_t prows = (size_t)B * Hq * (((size_t)S + 63) / 64 * 64);
-  return round_up(rows * d * sizeof(float)) + 2 * round_up(prows * sizeof(float));
+  return 2 * round_up(prows * sizeof(float));
 }
 
 int attn_bwd_phase(int phase, const void* q, const void* k, const void* v, const void* o, const float* lse,
@@ -129,7 +128,7 @@ int attn_bwd_phase(int phase, const void* q, const void* k, const void* v, const
     case ATTN_BWD_ALL: phases = 7; break;
     case ATTN_BWD_PREPROCESS: phases = 1; break;
     case ATTN_BWD_MAIN: phases = 2; break;
-    case ATTN_BWD_DQ_CONVERT: phases = 4; break;
+    case ATTN_BWD_DQ: phases = 4; break;
     default: return ATTN_ERR_UNSUPPORTED;
   }
   bool empty = false;
@@ -157,11 +156,9 @@ int attn_bwd_phase(int phase, const void* q, const void* k, const void* v, const
   a.dq = static_cast<uint16_t*>(dq);
   a.dk = static_cast<uint16_t*>(dk);
   a.dv = static_cast<uint16_t*>(dv);
-  const size_t rows = (size_t)B * Hq * S;
   const size_t prows = (size_t)B * Hq * (((size_t)S + 63) / 64 * 64);
-  a.dq_acc = static_cast<float*>(workspace);
-  a.delta = reinterpret_cast<float*>(static_cast<char*>(workspace) + round_up(rows * d * sizeof(float)));
-  a.lse2 = reinterpret_cast<float*>(reinterpret_cast<char*>(a.delta) + round_up(prows * sizeof(float)));
+  a.delta = static_cast<float*>(workspace);
+  a.lse2 = reinterpret_cast<float*>(static_cast<char*>(workspace) + round_up(prows * sizeof(float)));
   a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.S = S;
   a.scale = scale;
   scale_setup(scale, &a.c, &a.q_and, &a.q_xor);

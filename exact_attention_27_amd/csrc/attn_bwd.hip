@@ -5,28 +5,24 @@
 // FlashAttention-4 story; "NVIDIA Blackwell: FlashAttention-4 Overcomes Memory
 // Bottlenecks", body paragraph).  Three launches on the caller's stream:
 //
-//  1. bwd_pre:    D_i = <dO_i, O_i> in fp32 from the stored bf16 O and dO, LSE_i log2(e),
-//                 and a zeroed fp32 dQ accumulator.  Bound by HBM bandwidth.
-//  2. bwd_main:   one workgroup per (batch, KV head, tile of 128 keys); each of its 4 waves
-//                 owns 32 keys and keeps dK and dV for them in registers for the whole
-//                 run.  The workgroup walks the query tiles (64 queries) that can see its
-//                 keys (causal: only tiles at or below the diagonal), from the last one
-//                 down, for every query head of the GQA group.  Per step, with Q, dO, LSE and D staged in LDS:
-//                     S   = Q K^T              (MFMA; K and V stay in LDS for the run)
-//                     P   = 2^(S c - LSE log2 e), 0 where masked  (c = scale log2 e)
-//                     dP  = dO V^T             (MFMA)
-//                     dS  = P (dP - D)
-//                     dV^T += dO^T P,  dK^T += Q^T dS   (dO^T and Q^T by LDS transpose reads)
-//                 dS^T is written to LDS, and the 4 waves then compute the step's
-//                 dQ = dS K over all 128 keys together (dS and K^T by transpose reads)
-//                 and add it to the fp32 accumulator with hardware float atomics.
-//                 Because the group's query heads loop inside the workgroup, dK and dV
-//                 are summed over the group without atomics.
-//  3. dq_convert: dQ = bf16(scale * accumulator).
+//  1. bwd_pre:  D_i = <dO_i, O_i> in fp32 from the stored bf16 O and dO, and LSE_i log2(e),
+//               into the workspace.  Bound by HBM bandwidth.
+//  2. bwd_main: dK and dV.  One workgroup per (batch, KV head, tile of 128 keys) keeps dK
+//               and dV for its keys in registers for the whole run and walks the query
+//               tiles (64 queries) that can see its keys (causal: only tiles at or below
+//               the diagonal), from the last one down, for every query head of the GQA
+//               group.  Per step, with Q, dO, LSE and D staged in LDS:
+//                   S   = Q K^T,  dP = dO V^T     (MFMA; K and V stay in LDS for the run)
+//                   P   = 2^(S c - LSE log2 e), 0 where masked  (c = scale log2 e)
+//                   dS  = P (dP - D)
+//                   dV^T += dO^T P,  dK^T += Q^T dS   (dO^T and Q^T by LDS transpose reads)
+//               Because the group's query heads loop inside the workgroup, dK and dV are
+//               summed over the group without atomics.
+//  3. bwd_dq:   dQ, per query tile, recomputing S and dP (see below); no atomics.
 //
-// In the S accumulator layout (v_mfma_f32_32x32x16_bf16, A = Q rows, B = K^T) a lane
-// holds one key column and 16 query rows; P and dS are packed to bf16 in registers and
-// used directly as the B operand of the dV^T and dK^T products.
+// In the S accumulator layout of bwd_main (v_mfma_f32_32x32x16_bf16, A = Q rows, B = K^T)
+// a lane holds one key column and 16 query rows; P and dS are packed to bf16 in registers
+// and used directly as the B operand of the dV^T and dK^T products.
 #include "attn_device.h"
 #include "attn_kernels.h"
 
@@ -38,14 +34,13 @@ constexpr int kBwdBM = 64;   // queries per step
 
 // ------------------------------------------------------------------ preprocess
 // Rows are taken in the padded layout [B*Hq][S_pad] (S_pad = S rounded up to a multiple
-// of the 64-query step): D_i = <dO_i, O_i> and LSE_i log2(e) go to the workspace there,
-// padding rows get 0, and the fp32 dQ accumulator rows [B*Hq][S] are zeroed.  The main
-// kernel then moves whole 64-row blocks of D and LSE into LDS with no bounds checks.
+// of the 64-query step): D_i = <dO_i, O_i> and LSE_i log2(e) go to the workspace there and
+// padding rows get 0.  The main kernel then moves whole 64-row blocks of D and LSE into
+// LDS with no bounds checks; the dQ kernel reads one of each per lane.
 template <int D>
 __global__ __launch_bounds__(256) void bwd_pre_kernel(const uint16_t* __restrict__ o, const uint16_t* __restrict__ dO,
                                                       const float* __restrict__ lse, float* __restrict__ delta,
-                                                      float* __restrict__ lse2, float* __restrict__ dq_acc,
-                                                      long prows, int S, int S_pad) {
+                                                      float* __restrict__ lse2, long prows, int S, int S_pad) {
   constexpr int LPR = D / 8;  // lanes per row, 8 bf16 each
   const long gid = (long)blockIdx.x * 256 + threadIdx.x;
   const long prow = gid / LPR;
@@ -65,9 +60,6 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const uint16_t* __restrict
       acc = fmaf(o0, d0, acc);
       acc = fmaf(o1, d1, acc);
     }
-    f32x4* z = (f32x4*)(dq_acc + row * D + part * 8);
-    z[0] = f32x4{0.f, 0.f, 0.f, 0.f};
-    z[1] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 #pragma unroll
   for (int off = LPR / 2; off >= 1; off >>= 1) acc += __shfl_xor(acc, off);
@@ -78,16 +70,6 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const uint16_t* __restrict
 }
 
 // ------------------------------------------------------------------ main
-
-// Vector memory operations of a wave complete in issue order, and no-return atomics
-// count in vmcnt like loads.  Each backward step ends with exactly kDqAtomics atomic adds
-// per wave; waiting for vmcnt <= kDqAtomics at the next step therefore waits for every
-// earlier DMA without waiting for those atomics to drain.
-constexpr int kDqAtomics = 16;
-__device__ __forceinline__ void wait_dma_behind_atomics() {
-  static_assert(kDqAtomics == 16, "the immediate below");
-  __asm__ volatile("s_waitcnt vmcnt(16)" ::: "memory");
-}
 
 // Workgroup of 8 waves (two per SIMD) on a tile of 128 keys.  Wave w owns key block
 // kq = w % 4 (32 keys) for query half qh = w / 4 of every 64-query step: waves w and
@@ -107,7 +89,6 @@ void bwd_main_kernel(BwdArgs a) {
   __shared__ __attribute__((aligned(1024))) uint16_t v_lds[KT];
   __shared__ __attribute__((aligned(1024))) uint16_t q_lds[2][QT];
   __shared__ __attribute__((aligned(1024))) uint16_t do_lds[2][QT];
-  __shared__ __attribute__((aligned(1024))) uint16_t dst_lds[kBwdBN * kBwdBM];  // dS^T [key][query]
   __shared__ __attribute__((aligned(1024))) float sd_lds[2][2 * kBwdBM];  // [stage][LSE log2e | D]
 
   const int tid = threadIdx.x;
@@ -159,11 +140,9 @@ void bwd_main_kernel(BwdArgs a) {
     qdma_off[i] = swz_chunk<D>(qdma_row[i], pch % CPR) * 8;
   }
   const int S_pad = (S + kBwdBM - 1) / kBwdBM * kBwdBM;
-  // Step order: query tiles from the last one down, the group's heads innermost.  All
-  // workgroups of one (batch, KV head) start on the last query tile together and move
-  // down in step, so their fp32 atomic adds into dQ hit the same few rows at the same
-  // time and stay in L2 (the workgroups of one KV head share an XCD when B*Hkv is a
-  // multiple of 8).
+  // Step order: query tiles from the last one down, the group's heads innermost, so the
+  // workgroups of one (batch, KV head), which share an XCD when B*Hkv is a multiple of
+  // 8, read the same Q/dO rows at about the same time.
   auto stage_in = [&](int step, int st) {
     const int g = step % G;
     const int qt = nqt - 1 - step / G;
@@ -198,12 +177,8 @@ void bwd_main_kernel(BwdArgs a) {
   if (steps > 0) stage_in(0, 0);
   for (int step = 0; step < steps; ++step) {
     const int st = step & 1;
-    if (step == 0) {
-      wait_dma();
-    } else {
-      wait_dma_behind_atomics();
-    }
-    __syncthreads();  // this step's Q, dO, LSE, D are in LDS; the previous dQ product is done
+    wait_dma();
+    __syncthreads();  // this step's Q, dO, LSE, D are in LDS; every wave is done with the previous stage
     const int g = step % G;
     const int qt = nqt - 1 - step / G;
     const int hq = hkv * G + g;
@@ -226,7 +201,7 @@ void bwd_main_kernel(BwdArgs a) {
       }
       const bool need_mask = (kw + 32 > S) || (qs + 32 > S) || (CAUSAL && kw + 31 > qs);
       // P and dS packed to bf16: pb[t] / sb[t] hold registers v = 8t .. 8t+7, the B-operand
-      // layout of the dV^T and dK^T products; dS^T also goes to LDS for the dQ product.
+      // layout of the dV^T and dK^T products.
       bf16x8 pb[2], sb[2];
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
@@ -253,8 +228,6 @@ void bwd_main_kernel(BwdArgs a) {
           wp[2 * gg + 1] = pack_bf16x2(pv[2], pv[3]);
           wsd[2 * gg] = pack_bf16x2(dsv[0], dsv[1]);
           wsd[2 * gg + 1] = pack_bf16x2(dsv[2], dsv[3]);
-          const u32x2 w2 = {wsd[2 * gg], wsd[2 * gg + 1]};
-          *(u32x2*)(dst_lds + swz<kBwdBM>(kq * 32 + col, qr)) = w2;
         }
         pb[t] = __builtin_bit_cast(bf16x8, wp);
         sb[t] = __builtin_bit_cast(bf16x8, wsd);
@@ -269,42 +242,6 @@ void bwd_main_kernel(BwdArgs a) {
           dv_acc[db] = mfma32(join(lds_read_tr16(Os + o0), lds_read_tr16(Os + o1)), pb[t], dv_acc[db]);
           dk_acc[db] = mfma32(join(lds_read_tr16(Qs + o0), lds_read_tr16(Qs + o1)), sb[t], dk_acc[db]);
         }
-      }
-    } else {
-      // All of this wave's keys lie above its queries: its block of dS^T is zero.
-#pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const int id = i * 64 + lane;  // 128 chunks of 16 bytes: 32 rows x 4 chunks
-        const int r = kq * 32 + id / 4;
-        *(u32x4*)(dst_lds + r * kBwdBM + (swz_chunk<kBwdBM>(r, qh * 4 + id % 4) << 3)) = u32x4{0u, 0u, 0u, 0u};
-      }
-    }
-    __syncthreads();  // dS^T complete
-
-    // dQ[64 x D] += dS[64 x 128] K[128 x D]: wave -> (query block qh, d-block kq) for
-    // D = 128; for D = 64 the four waves of query half qh split 2 d-blocks x 2 key halves
-    // and the key halves add into the accumulator separately.
-    {
-      constexpr int KK = DBLK == 4 ? 8 : 4;  // 16-key steps per wave
-      const int db = DBLK == 4 ? kq : (kq & 1);
-      const int kk0 = DBLK == 4 ? 0 : (kq >> 1) * 4;
-      f32x16 dq = f32x16{};
-#pragma unroll
-      for (int i = 0; i < KK; ++i) {
-        const int row = (kk0 + i) * 16 + trow;
-        const bf16x8 sa = join(lds_read_tr16(dst_lds + swz<kBwdBM>(row, qh * 32 + tcol)),
-                               lds_read_tr16(dst_lds + swz<kBwdBM>(row + 8, qh * 32 + tcol)));
-        const bf16x8 kb = join(lds_read_tr16(k_lds + swz<D>(row, db * 32 + tcol)),
-                               lds_read_tr16(k_lds + swz<D>(row + 8, db * 32 + tcol)));
-        dq = mfma32(sa, kb, dq);
-      }
-      // Exactly kDqAtomics atomic instructions per wave (see wait_dma_behind_atomics):
-      // rows past the end of the sequence add 0 to the last row instead of branching.
-      float* dqa = a.dq_acc + ((size_t)b * a.Hq + hq) * (size_t)S * D + db * 32 + col;
-#pragma unroll
-      for (int v = 0; v < kDqAtomics; ++v) {
-        const int q = qs + (v >> 2) * 8 + half * 4 + (v & 3);
-        atomicAdd(dqa + (size_t)min(q, S - 1) * D, q < S ? dq[v] : 0.0f);
       }
     }
   }
@@ -354,31 +291,201 @@ void bwd_main_kernel(BwdArgs a) {
   }
 }
 
-// ------------------------------------------------------------------ dQ convert
-__global__ __launch_bounds__(256) void dq_convert_kernel(const float* __restrict__ acc, uint16_t* __restrict__ dq,
-                                                         long n8, float scale) {
-  const long i = (long)blockIdx.x * 256 + threadIdx.x;
-  if (i >= n8) return;
-  const f32x4 x0 = ((const f32x4*)acc)[2 * i];
-  const f32x4 x1 = ((const f32x4*)acc)[2 * i + 1];
-  u32x4 w;
-  w[0] = pack_bf16x2(x0[0] * scale, x0[1] * scale);
-  w[1] = pack_bf16x2(x0[2] * scale, x0[3] * scale);
-  w[2] = pack_bf16x2(x1[0] * scale, x1[1] * scale);
-  w[3] = pack_bf16x2(x1[2] * scale, x1[3] * scale);
-  ((u32x4*)dq)[i] = w;
+// ------------------------------------------------------------------ dQ
+// dQ without atomics: one workgroup of 4 waves owns 128 queries of one (batch, query
+// head) and walks the key tiles (64 keys, staged in LDS by DMA, double-buffered) that its
+// queries can see, like the forward.  Per tile, with one query per lane (the transposed
+// score layout of the forward):
+//     S^T  = K Q^T,   dP^T = V dO^T                 (Q^T, dO^T held in registers)
+//     dS^T = P^T (dP^T - D),  P^T = 2^(S^T c - LSE log2 e)   (LSE and D: one value per lane)
+//     dQ^T += K^T dS^T                              (K^T by LDS transpose reads)
+// It recomputes S and dP (two of the backward's five products) instead of adding
+// partial dQ blocks from every key tile with fp32 atomics, and it is deterministic.
+constexpr int kDqBM = 128;  // queries per workgroup
+constexpr int kDqBN = 64;   // keys per tile
+
+template <int D, bool CAUSAL, int EXPMODE>
+__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(2, 2)))
+void bwd_dq_kernel(BwdArgs a) {
+  constexpr int BN = kDqBN;
+  constexpr int KSTEPS = D / 16;
+  constexpr int DBLK = D / 32;
+  constexpr int CPR = D / 8;
+  constexpr int TILE = BN * D;
+  constexpr int DMAS = BN * CPR / 256;
+  __shared__ __attribute__((aligned(1024))) uint16_t smem[4 * TILE];  // K ring (2 tiles), V ring (2 tiles)
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int col = lane & 31;
+  const int half = lane >> 5;
+  const int S = a.S;
+  const int S_pad = (S + kBwdBM - 1) / kBwdBM * kBwdBM;
+
+  const int nbh = a.B * a.Hq;
+  const int nqt = (S + kDqBM - 1) / kDqBM;
+  const int bid = blockIdx.x;
+  const int qt = CAUSAL ? (nqt - 1 - bid / nbh) : (bid / nbh);
+  const int bh = bid % nbh;
+  const int b = bh / a.Hq;
+  const int hq = bh - b * a.Hq;
+  const int hkv = hq / (a.Hq / a.Hkv);
+  const int q0 = qt * kDqBM;
+  const int qw = q0 + wave * 32;
+  const int qi = qw + col;  // this lane's query
+  const int qc = min(qi, S - 1);  // rows past the end read the last row; never stored
+  const size_t qbase = ((size_t)b * a.Hq + hq) * (size_t)S * D;
+  const size_t kvbase = ((size_t)b * a.Hkv + hkv) * (size_t)S * D;
+  const uint16_t* __restrict__ Kg = a.k + kvbase;
+  const uint16_t* __restrict__ Vg = a.v + kvbase;
+
+  // Q^T and dO^T fragments (B operands): query qc, d = ks*16 + half*8 .. +7.
+  bf16x8 qf[KSTEPS], of[KSTEPS];
+  {
+    const u32x4* qrow = (const u32x4*)(a.q + qbase + (size_t)qc * D + half * 8);
+    const u32x4* orow = (const u32x4*)(a.dO + qbase + (size_t)qc * D + half * 8);
+#pragma unroll
+    for (int ks = 0; ks < KSTEPS; ++ks) {
+      qf[ks] = __builtin_bit_cast(bf16x8, qrow[ks * 2]);
+      of[ks] = __builtin_bit_cast(bf16x8, orow[ks * 2]);
+    }
+  }
+  const size_t prow = ((size_t)b * a.Hq + hq) * (size_t)S_pad + qc;
+  const float lse2 = a.lse2[prow];
+  const float dd = a.delta[prow];
+  const float c = a.scale * kLog2e;  // signed: no running maximum is needed here
+
+  const int kv_end = CAUSAL ? min(S, q0 + kDqBM) : S;
+  const int nkv = (kv_end + BN - 1) / BN;
+
+  uint32_t dma_off[DMAS];
+#pragma unroll
+  for (int i = 0; i < DMAS; ++i) {
+    const int pch = (i * 4 + wave) * 64 + lane;
+    const int r = pch / CPR;
+    dma_off[i] = (uint32_t)(r * D + swz_chunk<D>(r, pch % CPR) * 8) * 2u;
+  }
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  auto dma_tile = [&](const uint16_t* __restrict__ src, int j, uint16_t* slot) {
+    const uint16_t* base = src + (size_t)j * BN * D;
+    if (j * BN + BN <= S) {
+#pragma unroll
+      for (int i = 0; i < DMAS; ++i) dma16_s(base, dma_off[i], slot + (i * 4 + wave_u) * 512);
+    } else {
+#pragma unroll
+      for (int i = 0; i < DMAS; ++i) {
+        const int pch = (i * 4 + wave) * 64 + lane;
+        const int r = pch / CPR;
+        const int rc = min(j * BN + r, S - 1) - j * BN;
+        const uint32_t off = (uint32_t)(rc * D + swz_chunk<D>(r, pch % CPR) * 8) * 2u;
+        dma16_s(base, off, slot + (i * 4 + wave_u) * 512);
+      }
+    }
+  };
+  uint16_t* const Kring = smem;
+  uint16_t* const Vring = smem + 2 * TILE;
+
+  const int trow = (lane >> 5) * 4 + ((lane >> 2) & 3);
+  const int tcol = ((lane >> 4) & 1) * 16 + (lane & 3) * 4;
+
+  f32x16 dq[DBLK];
+#pragma unroll
+  for (int db = 0; db < DBLK; ++db) dq[db] = f32x16{};
+
+  dma_tile(Kg, 0, Kring);
+  dma_tile(Vg, 0, Vring);
+  wait_dma();
+  __syncthreads();
+
+  for (int j = 0; j < nkv; ++j) {
+    const int st = j & 1;
+    if (j + 1 < nkv) {
+      dma_tile(Kg, j + 1, Kring + (st ^ 1) * TILE);
+      dma_tile(Vg, j + 1, Vring + (st ^ 1) * TILE);
+    }
+    const int k0 = j * BN;
+    if (!CAUSAL || k0 <= qw + 31) {
+      const uint16_t* Ks = Kring + st * TILE;
+      const uint16_t* Vs = Vring + st * TILE;
+      f32x16 s[2] = {f32x16{}, f32x16{}}, dp[2] = {f32x16{}, f32x16{}};
+#pragma unroll
+      for (int ks = 0; ks < KSTEPS; ++ks) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          const int off = swz<D>(kb * 32 + col, ks * 16 + half * 8);
+          s[kb] = mfma32(*(const bf16x8*)(Ks + off), qf[ks], s[kb]);
+          dp[kb] = mfma32(*(const bf16x8*)(Vs + off), of[ks], dp[kb]);
+        }
+      }
+      const bool need_mask = (k0 + BN > S) || (CAUSAL && k0 + BN - 1 > qw);
+      const int lim_s = S - 1 - k0 - half * 4;
+      const int lim = CAUSAL ? min(lim_s, qi - k0 - half * 4) : lim_s;
+      bf16x8 dsf[2][2];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          u32x4 w;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            float d2[2];
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+              const int v = t * 8 + 2 * e + u;
+              float p = exp2_sm<EXPMODE>(fmaf(s[kb][v], c, -lse2));
+              if (need_mask && kb * 32 + (v >> 2) * 8 + (v & 3) > lim) p = 0.0f;
+              d2[u] = p * (dp[kb][v] - dd);
+            }
+            w[e] = pack_bf16x2(d2[0], d2[1]);
+          }
+          dsf[kb][t] = __builtin_bit_cast(bf16x8, w);
+        }
+      }
+      // dQ^T += K^T dS^T
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          const int row = kb * 32 + t * 16 + trow;
+#pragma unroll
+          for (int db = 0; db < DBLK; ++db) {
+            const bf16x8 kt = join(lds_read_tr16(Ks + swz<D>(row, db * 32 + tcol)),
+                                   lds_read_tr16(Ks + swz<D>(row + 8, db * 32 + tcol)));
+            dq[db] = mfma32(kt, dsf[kb][t], dq[db]);
+          }
+        }
+      }
+    }
+    wait_dma();
+    __syncthreads();
+  }
+
+  if (qi < S) {
+    uint16_t* dqr = a.dq + qbase + (size_t)qi * D;
+    const float sc = a.scale;
+#pragma unroll
+    for (int db = 0; db < DBLK; ++db) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        u32x2 w;
+        w[0] = pack_bf16x2(dq[db][g * 4 + 0] * sc, dq[db][g * 4 + 1] * sc);
+        w[1] = pack_bf16x2(dq[db][g * 4 + 2] * sc, dq[db][g * 4 + 3] * sc);
+        *(u32x2*)(dqr + db * 32 + g * 8 + half * 4) = w;
+      }
+    }
+  }
 }
 
 template <int D, bool CAUSAL, int EXPMODE>
 hipError_t launch_bwd_t(const BwdArgs& a, int phases, hipStream_t stream) {
-  const long rows = (long)a.B * a.Hq * a.S;
   hipError_t e = hipSuccess;
   if (phases & 1) {
     const int S_pad = (a.S + kBwdBM - 1) / kBwdBM * kBwdBM;
     const long prows = (long)a.B * a.Hq * S_pad;
     const long pre_threads = prows * (D / 8);
     hipLaunchKernelGGL(bwd_pre_kernel<D>, dim3((unsigned)((pre_threads + 255) / 256)), dim3(256), 0, stream,
-                       a.o, a.dO, a.lse, a.delta, a.lse2, a.dq_acc, prows, a.S, S_pad);
+                       a.o, a.dO, a.lse, a.delta, a.lse2, prows, a.S, S_pad);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   if (phases & 2) {
@@ -388,9 +495,9 @@ hipError_t launch_bwd_t(const BwdArgs& a, int phases, hipStream_t stream) {
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   if (phases & 4) {
-    const long n8 = rows * D / 8;
-    hipLaunchKernelGGL(dq_convert_kernel, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, stream,
-                       a.dq_acc, a.dq, n8, a.scale);
+    const int nqt = (a.S + kDqBM - 1) / kDqBM;
+    hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL, EXPMODE>), dim3((unsigned)(nqt * a.B * a.Hq)), dim3(256), 0,
+                       stream, a);
     e = hipGetLastError();
   }
   return e;

@@ -33,7 +33,6 @@ struct BwdArgs {
   uint16_t* dq;
   uint16_t* dk;
   uint16_t* dv;
-  float* dq_acc;  // [B,Hq,S,d] fp32 workspace
   float* delta;   // [B*Hq][S_pad] fp32 workspace: D_i = <dO_i, O_i> (S_pad = S rounded up to 64)
   float* lse2;    // [B*Hq][S_pad] fp32 workspace: LSE_i * log2(e)
   int B, Hq, Hkv, S;
@@ -43,8 +42,8 @@ struct BwdArgs {
 };
 
 hipError_t launch_fwd(const FwdArgs& a, int d, bool causal, int exp_mode, hipStream_t stream);
-// phases: bit 0 = preprocess (D and zeroed dQ accumulator), bit 1 = main kernel,
-// bit 2 = dQ conversion.  7 runs the whole backward.
+// phases: bit 0 = preprocess (D, LSE log2 e), bit 1 = dK/dV kernel, bit 2 = dQ kernel.
+// 7 runs the whole backward.
 hipError_t launch_bwd(const BwdArgs& a, int d, bool causal, int exp_mode, int phases, hipStream_t stream);
 hipError_t launch_exp2_eval(const float* x, float* y, long n, int exp_mode, hipStream_t stream);
 

@@ -107,10 +107,10 @@ int attn_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse
                 const attn_options* opt, void* stream);
 
 /*
- * Bytes of device workspace attn_bwd needs for these sizes: an fp32 dQ
- * accumulator [B,Hq,S,d], then two fp32 row arrays [B*Hq][S_pad] (the row terms
- * D_i = <dO_i, O_i> and LSE_i log2(e), S_pad = S rounded up to a multiple of 64),
- * each part rounded up to 256 bytes.  Returns 0 for invalid or empty sizes.
+ * Bytes of device workspace attn_bwd needs for these sizes: two fp32 row arrays
+ * [B*Hq][S_pad] (the row terms D_i = <dO_i, O_i> and LSE_i log2(e), S_pad = S rounded
+ * up to a multiple of 64), each rounded up to 256 bytes.  Returns 0 for invalid or
+ * empty sizes.
  */
 size_t attn_bwd_workspace_bytes(int B, int Hq, int Hkv, int S, int d);
 
@@ -119,9 +119,8 @@ size_t attn_bwd_workspace_bytes(int B, int Hq, int Hkv, int S, int d);
  * attn_fwd, or any consistent pair), and the upstream gradient dO.  Outputs dq,
  * dk, dv are written in full.  workspace: device memory of at least
  * attn_bwd_workspace_bytes(...) bytes, 256-byte aligned, owned by the caller;
- * its contents on entry do not matter and on exit are unspecified.  dq is
- * accumulated with fp32 atomics, so its last bits may differ between runs;
- * dk and dv are deterministic.
+ * its contents on entry do not matter and on exit are unspecified.  All outputs
+ * are deterministic (no atomics).
  */
 int attn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
              const void* dO, void* dq, void* dk, void* dv,
@@ -136,21 +135,20 @@ int attn_bwd_ex(const void* q, const void* k, const void* v, const void* o, cons
 
 /*
  * One phase of attn_bwd_ex, for callers that schedule or time the backward's launches
- * separately.  Running ATTN_BWD_PREPROCESS, ATTN_BWD_MAIN and ATTN_BWD_DQ_CONVERT in
- * that order on one stream, with the same arguments and workspace, is exactly
- * attn_bwd_ex (ATTN_BWD_ALL).  The phases communicate through the workspace:
- *   PREPROCESS  reads o, dO, lse; writes D = rowsum(dO * O), LSE log2(e) and a zeroed
- *               dQ accumulator;
- *   MAIN        reads q, k, v, dO, D and LSE log2(e); writes dk, dv; adds into the
- *               accumulator;
- *   DQ_CONVERT  reads the accumulator; writes dq.
+ * separately.  Running ATTN_BWD_PREPROCESS, ATTN_BWD_MAIN and ATTN_BWD_DQ in that
+ * order on one stream, with the same arguments and workspace, is exactly attn_bwd_ex
+ * (ATTN_BWD_ALL); MAIN and DQ are independent of each other.  The phases communicate
+ * through the workspace:
+ *   PREPROCESS  reads o, dO, lse; writes D = rowsum(dO * O) and LSE log2(e);
+ *   MAIN        reads q, k, v, dO, D and LSE log2(e); writes dk, dv;
+ *   DQ          reads q, k, v, dO, D and LSE log2(e); writes dq.
  * Arguments are validated as for attn_bwd_ex; an unknown phase is ATTN_ERR_UNSUPPORTED.
  */
 enum {
     ATTN_BWD_ALL = 0,
     ATTN_BWD_PREPROCESS = 1,
     ATTN_BWD_MAIN = 2,
-    ATTN_BWD_DQ_CONVERT = 3
+    ATTN_BWD_DQ = 3
 };
 int attn_bwd_phase(int phase, const void* q, const void* k, const void* v, const void* o, const float* lse,
                    const void* dO, void* dq, void* dk, void* dv,

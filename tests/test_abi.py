@@ -93,10 +93,9 @@ def test_fwd_rejects_options(opt, status):
 
 def test_workspace_bytes():
     B, Hq, Hkv, S, d = 2, 4, 2, 100, 128
-    rows = B * Hq * S
     rup = lambda x: (x + 255) // 256 * 256
     prows = B * Hq * ((S + 63) // 64 * 64)
-    assert ea.attn_bwd_workspace_bytes(B, Hq, Hkv, S, d) == rup(rows * d * 4) + 2 * rup(prows * 4)
+    assert ea.attn_bwd_workspace_bytes(B, Hq, Hkv, S, d) == 2 * rup(prows * 4)
     assert ea.attn_bwd_workspace_bytes(0, Hq, Hkv, S, d) == 0
     assert ea.attn_bwd_workspace_bytes(B, 3, 2, S, d) == 0
     assert ea.attn_bwd_workspace_bytes(B, Hq, Hkv, S, 80) == 0
