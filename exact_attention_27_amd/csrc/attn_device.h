@@ -132,6 +132,36 @@ __device__ __forceinline__ int swz(int r, int col) {
   return r * D + (swz_chunk<D>(r, col >> 3) << 3) + (col & 7);
 }
 
+// Blocked tile layouts (no swizzle).  A [rows][D] bf16 tile is cut into blocks of 16 rows
+// x 4 chunks (a chunk is 16 bytes = 8 bf16): 64 chunks, 1024 bytes, exactly what one
+// LDS DMA instruction writes.  Block (r / 16, c / 4) sits at byte
+// ((r / 16) * (D / 32) + c / 4) * 1024 of the tile.  Inside a block the chunks are in
+// one of two orders:
+//   * row-inner, unit (c % 4) * 16 + r % 16: an MFMA-operand read of 16 consecutive rows
+//     at one chunk is 256 contiguous bytes, free of bank conflicts;
+//   * chunk-inner, unit (r % 16) * 4 + c % 4: a transpose read of 4 consecutive rows x
+//     4 consecutive chunks (32 lanes) is 256 contiguous bytes, free of bank conflicts;
+//   * chunk-inner with the chunk XORed by (r % 16) / 4, unit
+//     (r % 16) * 4 + ((c % 4) ^ ((r % 16) / 4)): an MFMA-operand read of 16 consecutive
+//     rows at one chunk touches every bank once.
+// The DMA that fills a block gives lane l unit l, so in the two chunk-inner orders each
+// group of 4 consecutive lanes fetches one aligned 64-byte piece of a row (the
+// row-inner order scatters them over 4 rows).  The offsets are sums of a row part and
+// a chunk part (for the XOR order: per parity of c / 2), so an address that a lane
+// keeps in a register reaches every other block and row group by an immediate offset.
+template <int D>
+__host__ __device__ constexpr int blk_row_inner(int r, int c) {
+  return ((r >> 4) * (D / 32) + (c >> 2)) * 1024 + ((c & 3) * 16 + (r & 15)) * 16;
+}
+template <int D>
+__host__ __device__ constexpr int blk_chunk_inner(int r, int c) {
+  return ((r >> 4) * (D / 32) + (c >> 2)) * 1024 + ((r & 15) * 4 + (c & 3)) * 16;
+}
+template <int D>
+__host__ __device__ constexpr int blk_chunk_inner_x(int r, int c) {
+  return ((r >> 4) * (D / 32) + (c >> 2)) * 1024 + ((r & 15) * 4 + ((c & 3) ^ ((r >> 2) & 3))) * 16;
+}
+
 // ---------------------------------------------------------------------------------
 // Global -> LDS DMA (global_load_lds_dwordx4): lane l of the wave copies 16 bytes from
 // its global address g to LDS bytes [lds_wave_base + 16 l, +16).  It is issued from an
@@ -140,8 +170,13 @@ __device__ __forceinline__ int swz(int r, int col) {
 // LDS it writes is read only after wait_dma()/vmcnt waits and a barrier, which the
 // kernels place explicitly.  lds_wave_base must be the same for all lanes of the wave.
 // ---------------------------------------------------------------------------------
+// LDS byte address of a generic pointer into LDS: a generic LDS address is the LDS
+// aperture in the upper 32 bits and the LDS byte address in the lower 32, so truncation
+// gives it without the null-pointer check that an address-space cast emits.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) { return (uint32_t)(uintptr_t)p; }
+
 __device__ __forceinline__ void dma16(const void* g, const void* lds_wave_base) {
-  const uint32_t l = (uint32_t)(size_t)(const __attribute__((address_space(3))) void*)lds_wave_base;
+  const uint32_t l = lds_addr(lds_wave_base);
   const uint32_t ls = __builtin_amdgcn_readfirstlane(l);
   __asm__ volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
                    :
@@ -152,7 +187,7 @@ __device__ __forceinline__ void dma16(const void* g, const void* lds_wave_base) 
 // The same with a scalar (wave-uniform) 64-bit base and a 32-bit per-lane byte offset:
 // no per-lane address arithmetic when the offsets stay fixed across a loop.
 __device__ __forceinline__ void dma16_s(const void* sbase, uint32_t voff, const void* lds_wave_base) {
-  const uint32_t l = (uint32_t)(size_t)(const __attribute__((address_space(3))) void*)lds_wave_base;
+  const uint32_t l = lds_addr(lds_wave_base);
   const uint32_t ls = __builtin_amdgcn_readfirstlane(l);
   __asm__ volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
                    :

@@ -13,9 +13,9 @@
 // so the running row maximum and row sum of the online softmax are in-lane
 // reductions plus one v_permlane32_swap between the two wave halves.  The
 // probabilities P^T are packed to bf16 straight from the accumulator registers and
-// used as the B operand of O^T += V^T P^T; V^T comes from the row-major V tile
-// through ds_read_b64_tr_b16 (LDS transpose reads).  The output accumulator O^T keeps
-// the same one-query-per-lane layout, so rescaling it by a per-row factor is a plain
+// used as the B operand of O^T += V^T P^T; V^T comes from the V tile through
+// ds_read_b64_tr_b16 (LDS transpose reads).  The output accumulator O^T keeps the
+// same one-query-per-lane layout, so rescaling it by a per-row factor is a plain
 // per-lane multiply.
 //
 // Online softmax with conditional rescaling (the "adaptive online softmax rescaling"
@@ -26,11 +26,21 @@
 // the probabilities 2^(x - m_ref) are used as they are (they stay <= 2^tau).  Since
 // O and the sum always share m_ref, the final O = O_acc / l is exact for every tau.
 //
+// Software pipeline of one key tile j (a "step"), per wave: the products of tile j+1's
+// scores S_{j+1} = K_{j+1} Q^T are issued while the vector units exponentiate S_j
+// (phase 1), then O^T += V_j^T P_j^T while they take the maximum of S_{j+1} (phase 2).
+// Both phases are written out as slots of one matrix product each, fenced so the
+// compiler keeps them: a slot issues the LDS reads of the slot two ahead, its product,
+// and its share of the vector work.  The matrix cores of a SIMD are shared by two
+// waves (of different workgroups), which fill each other's gaps.
+//
 // Causal masking: key tiles above the diagonal of the workgroup are never loaded;
 // only tiles that straddle the diagonal or the end of the sequence are masked.
 // Workgroups are dispatched longest-first (largest query tile index first), and all
 // query tiles of one head are spaced B*Hq workgroups apart so that, when B*Hq is a
 // multiple of 8, they run on one XCD and share its L2 for K and V.
+#include <type_traits>
+
 #include "attn_device.h"
 #include "attn_kernels.h"
 
@@ -38,24 +48,32 @@ namespace attn {
 namespace {
 
 constexpr int kFwdWaves = 4;
-constexpr int kFwdBN = 64;  // keys per LDS tile
+constexpr int kFwdBN = 64;                // keys per LDS tile
+constexpr int kFwdBM = 32 * kFwdWaves;    // queries per workgroup
+#ifndef FWD_PD
+#define FWD_PD 2                          // slots between an LDS read and its product
+#endif
 
-
-// NQB = 32-query column blocks per wave.  NQB = 2 reuses every K and V operand read
-// from LDS for two MFMAs (half the LDS traffic per MFMA) at twice the registers, so it
-// runs one wave per SIMD; NQB = 1 runs two.
-template <int D, bool CAUSAL, int EXPMODE, int NQB>
-__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(NQB == 1 ? 2 : 1, NQB == 1 ? 2 : 1)))
+template <int D, bool CAUSAL, int EXPMODE>
+__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(2, 2)))
 void fwd_kernel(FwdArgs a) {
   constexpr int BN = kFwdBN;
-  constexpr int WQ = 32 * NQB;          // queries per wave
-  constexpr int BM = WQ * kFwdWaves;    // queries per workgroup
+  constexpr int BM = kFwdBM;
+  constexpr int KB = BN / 32;           // 32-key blocks per tile
   constexpr int KSTEPS = D / 16;        // MFMA k-steps of S^T = K Q^T
   constexpr int DBLK = D / 32;          // 32-row blocks of O^T
   constexpr int CPR = D / 8;            // 16-byte chunks per row
   constexpr int TILE = BN * D;          // bf16 elements of one K or V tile
   constexpr int DMAS = BN * CPR / 256;  // 16-byte chunks per thread per tile
-  // K ring (2 tiles) then V ring (2 tiles), each tile [BN][D] with swizzled chunks.
+  constexpr int NQK = KSTEPS * KB;      // phase-1 slots (products of S_{j+1})
+  constexpr int NPV = 2 * KB * DBLK;    // phase-2 slots (products of O^T)
+  constexpr int NE = KB * 16;           // scores per lane per tile
+  constexpr int EPS = NE / NQK;         // exponentials per phase-1 slot
+  constexpr int MAX0 = NPV / 4;         // first phase-2 slot that takes part of the maximum
+  constexpr int PD = FWD_PD;
+  static_assert(NE % NQK == 0 && EPS % 2 == 0, "exponentials must pair up per slot");
+  static_assert(BN % 32 == 0 && DMAS * 256 == BN * CPR, "tile must split evenly over 256 threads");
+  // K ring (2 tiles) then V ring (2 tiles), each tile [BN][D] in 1024-byte blocks.
   __shared__ __attribute__((aligned(1024))) uint16_t smem[4 * TILE];
 
   const int tid = threadIdx.x;
@@ -74,257 +92,252 @@ void fwd_kernel(FwdArgs a) {
   const int hkv = hq / (a.Hq / a.Hkv);
   const int S = a.S;
   const int q0 = qt * BM;
-  const int qw = q0 + wave * WQ;  // first query of this wave; block qb holds qw + 32 qb ..
+  const int qw = q0 + wave * 32;  // first query of this wave
+  const int qi = qw + col;        // this lane's query
   const size_t qbase = ((size_t)b * a.Hq + hq) * (size_t)S * D;
   const size_t kvbase = ((size_t)b * a.Hkv + hkv) * (size_t)S * D;
   const uint16_t* __restrict__ Kg = a.k + kvbase;
   const uint16_t* __restrict__ Vg = a.v + kvbase;
 
-  // Q^T fragments (B operand): query qw + 32 qb + col, d = ks*16 + half*8 .. +7.
-  bf16x8 qf[NQB][KSTEPS];
-#pragma unroll
-  for (int qb = 0; qb < NQB; ++qb) {
-    const int qi = qw + qb * 32 + col;
-    // Rows past the end of the sequence load the last row instead (their outputs are
-    // never stored); no branch, so all the loads are in flight together.
+  // Q^T fragments (B operand): query qi, d = ks*16 + half*8 .. +7.  Rows past the end
+  // of the sequence load the last row instead (their outputs are never stored); no
+  // branch, so all the loads are in flight together.
+  bf16x8 qf[KSTEPS];
+  {
     const u32x4* qrow = (const u32x4*)(a.q + qbase + (size_t)min(qi, S - 1) * D + half * 8);
 #pragma unroll
-    for (int ks = 0; ks < KSTEPS; ++ks) {
-      const u32x4 w = (qrow[ks * 2] & a.q_and) ^ a.q_xor;
-      qf[qb][ks] = __builtin_bit_cast(bf16x8, w);
-    }
+    for (int ks = 0; ks < KSTEPS; ++ks) qf[ks] = __builtin_bit_cast(bf16x8, (qrow[ks * 2] & a.q_and) ^ a.q_xor);
   }
 
   const int kv_end = CAUSAL ? min(S, q0 + BM) : S;
   const int nkv = (kv_end + BN - 1) / BN;
 
-  // DMA of one tile into a ring slot.  Thread tid, chunk i covers LDS chunk
-  // p = (i * 4 + wave) * 64 + lane = (row, physical chunk); it fetches the logical chunk
-  // physical ^ f(row) of key row j*BN + row.  The per-lane byte offsets within a tile
-  // are fixed, the tile base is a scalar; only the last tile, if it runs past the end of
+  // LDS tiles use the blocked layouts of attn_device.h: K chunk-inner with XOR (read as
+  // MFMA A operands, 16 rows at one chunk), V chunk-inner (read by transpose reads).  A
+  // tile is (BN / 16) x (D / 32) blocks of 1024 bytes; wave w DMAs blocks 4 i + w,
+  // i < DMAS.  Lane l fetches row l / 4 of the block, chunk l % 4 (K: XOR (l / 16) % 4),
+  // so every 4 lanes read one aligned 64-byte piece of a row.  The per-lane global byte offsets are
+  // fixed and the tile base is a scalar; only the last tile, if it runs past the end of
   // the sequence, clamps its rows to a real row (their scores are masked, so any finite
   // data will do).
-  uint32_t dma_off[DMAS];
-#pragma unroll
-  for (int i = 0; i < DMAS; ++i) {
-    const int pch = (i * 4 + wave) * 64 + lane;
-    const int r = pch / CPR;
-    dma_off[i] = (uint32_t)(r * D + swz_chunk<D>(r, pch % CPR) * 8) * 2u;
-  }
+  constexpr int CG = D / 32;    // 4-chunk groups per row
+  constexpr int ROWB = D * 2;   // bytes per K/V row in memory
+  static_assert(4 % CG == 0 && BN * CG == 64 * DMAS, "DMA block assignment");
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
-  auto dma_tile = [&](const uint16_t* __restrict__ src, int j, uint16_t* slot) {
-    const uint16_t* base = src + (size_t)j * BN * D;
+  const int w_rg = wave_u / CG, w_cg = wave_u % CG;  // block (w_rg, w_cg) for i = 0
+  const int k_lr = lane >> 2, k_lc = (lane & 3) ^ ((lane >> 4) & 3);
+  const int v_lr = lane >> 2, v_lc = lane & 3;
+  const uint32_t k_goff = (uint32_t)((w_rg * 16 + k_lr) * ROWB + (w_cg * 4 + k_lc) * 16);
+  const uint32_t v_goff = (uint32_t)((w_rg * 16 + v_lr) * ROWB + (w_cg * 4 + v_lc) * 16);
+  auto dma_tile = [&](const uint16_t* __restrict__ src, int j, uint16_t* slot, int lr, int lc, uint32_t goff) {
+    const char* base = (const char*)(src + (size_t)j * BN * D);
     if (j * BN + BN <= S) {
 #pragma unroll
-      for (int i = 0; i < DMAS; ++i) dma16_s(base, dma_off[i], slot + (i * 4 + wave_u) * 512);
+      for (int i = 0; i < DMAS; ++i)
+        dma16_s(base + i * (4 / CG) * 16 * ROWB, goff, slot + (i * 4 + wave_u) * 512);
     } else {
+      __asm__ volatile("" : "+v"(lr));  // keep this rare path's row arithmetic inside it
 #pragma unroll
       for (int i = 0; i < DMAS; ++i) {
-        const int pch = (i * 4 + wave) * 64 + lane;
-        const int r = pch / CPR;
+        const int r = (i * (4 / CG) + w_rg) * 16 + lr;  // row within the tile
         const int rc = min(j * BN + r, S - 1) - j * BN;
-        const uint32_t off = (uint32_t)(rc * D + swz_chunk<D>(r, pch % CPR) * 8) * 2u;
-        dma16_s(base, off, slot + (i * 4 + wave_u) * 512);
+        dma16_s(base, (uint32_t)(rc * ROWB + (w_cg * 4 + lc) * 16), slot + (i * 4 + wave_u) * 512);
       }
     }
   };
+  auto dma_k = [&](int j, uint16_t* slot) { dma_tile(Kg, j, slot, k_lr, k_lc, k_goff); };
+  auto dma_v = [&](int j, uint16_t* slot) { dma_tile(Vg, j, slot, v_lr, v_lc, v_goff); };
   uint16_t* const Kring = smem;
   uint16_t* const Vring = smem + 2 * TILE;
 
-  // Per-lane parts of the V^T transpose-read addresses (see attn_device.h): source
-  // lane s reads 4 d-values of key row (s / 32) * 4 + (s % 16) / 4 (+ 8 for the second
-  // read), at column 16 * ((s / 16) % 2) + 4 * (s % 4) of a 32-wide d block.
-  const int vrow = (lane >> 5) * 4 + ((lane >> 2) & 3);
-  const int vcol = ((lane >> 4) & 1) * 16 + (lane & 3) * 4;
+  // Per-lane byte offsets of the LDS reads; every other read of a tile adds a constant.
+  // K (A operand of S^T = K Q^T): lane l reads key row l % 32, chunk l / 32 + 2 ks; one
+  // register per parity of ks.
+  const int k_lds0 = blk_chunk_inner_x<D>(col, half), k_lds1 = blk_chunk_inner_x<D>(col, 2 + half);
+  auto k_off = [&](int kb, int ks) { return ((ks & 1) ? k_lds1 : k_lds0) + blk_chunk_inner_x<D>(kb * 32, (ks >> 1) * 4); };
+  // V^T by transpose reads: source lane s reads 4 d-values of key row
+  // (s / 32) * 4 + (s % 16) / 4 (+ 8 for the second read) at column
+  // 16 * ((s / 16) % 2) + 4 * (s % 4) of a 32-wide d block.
+  const int v_lds = blk_chunk_inner<D>((lane >> 5) * 4 + ((lane >> 2) & 3), ((lane >> 4) & 1) * 2 + ((lane >> 1) & 1)) +
+                    (lane & 1) * 8;
 
-  f32x16 oacc[NQB][DBLK];
-  float m_ref[NQB], l_run[NQB];
+  f32x16 oacc[DBLK];
 #pragma unroll
-  for (int qb = 0; qb < NQB; ++qb) {
-#pragma unroll
-    for (int db = 0; db < DBLK; ++db) oacc[qb][db] = f32x16{};
-    m_ref[qb] = -INFINITY;  // reference row maximum, log2 units (scaled scores)
-    l_run[qb] = 0.0f;       // this lane's part of the running row sum
-  }
+  for (int db = 0; db < DBLK; ++db) oacc[db] = f32x16{};
+  float m_ref = -INFINITY;  // reference row maximum, log2 units (scaled scores)
+  float l_run = 0.0f;       // this lane's part of the running row sum
   const float c = a.c;
   const float tau = a.tau;
 
-  // S^T = K Q^T for every query block: each K fragment read from LDS feeds NQB MFMAs.
-  auto qk = [&](const uint16_t* Ks, f32x16 (*s)[2]) {
+  // Tiles that reach past the end of the sequence or (causal) past the wave's first
+  // query: the only ones with masked scores.
+  auto needs_mask = [&](int k0) { return (k0 + BN > S) || (CAUSAL && k0 + BN - 1 > qw); };
+  auto mask = [&](f32x16* s, int k0) {
+    const int lim_s = S - 1 - k0 - half * 4;                          // key <= S - 1
+    int lim = CAUSAL ? min(lim_s, qi - k0 - half * 4) : lim_s;        // key <= query
+    __asm__ volatile("" : "+v"(lim));  // keep the comparisons inside this rare path
 #pragma unroll
-    for (int qb = 0; qb < NQB; ++qb) s[qb][0] = s[qb][1] = f32x16{};
+    for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-    for (int ks = 0; ks < KSTEPS; ++ks) {
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        const bf16x8 ka = *(const bf16x8*)(Ks + swz<D>(kb * 32 + col, ks * 16 + half * 8));
-#pragma unroll
-        for (int qb = 0; qb < NQB; ++qb) s[qb][kb] = mfma32(ka, qf[qb][ks], s[qb][kb]);
+      for (int v = 0; v < 16; ++v) {
+        const int e = kb * 32 + (v >> 2) * 8 + (v & 3);  // key - k0 - half*4
+        s[kb][v] = e > lim ? -INFINITY : s[kb][v];
       }
-    }
   };
-  auto mask = [&](f32x16 (*s)[2], int k0) {
-    if ((k0 + BN > S) || (CAUSAL && k0 + BN - 1 > qw)) {
+  // Scaled row maximum (log2 units) of a score tile, both wave halves combined.
+  auto tile_max = [&](const f32x16* s) {
+    float mx = -INFINITY;
 #pragma unroll
-      for (int qb = 0; qb < NQB; ++qb) {
-        const int qi = qw + qb * 32 + col;
-        const int lim_s = S - 1 - k0 - half * 4;               // key <= S - 1
-        const int lim = CAUSAL ? min(lim_s, qi - k0 - half * 4) : lim_s;  // key <= query
+    for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-          for (int v = 0; v < 16; ++v) {
-            const int e = kb * 32 + (v >> 2) * 8 + (v & 3);  // key - k0 - half*4
-            s[qb][kb][v] = e > lim ? -INFINITY : s[qb][kb][v];
-          }
-        }
-      }
-    }
-  };
-  // P = 2^(s c - m) packed to bf16 in the B-operand layout of O^T += V^T P^T.
-  auto softmax_exp = [&](const f32x16* s, float m, bf16x8 (*pf)[2]) {
-    float lt = 0.0f;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        u32x4 w;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float p0 = exp2_sm<EXPMODE>(fmaf(s[kb][t * 8 + 2 * e], c, -m));
-          const float p1 = exp2_sm<EXPMODE>(fmaf(s[kb][t * 8 + 2 * e + 1], c, -m));
-          lt += p0 + p1;
-          w[e] = pack_bf16x2(p0, p1);
-        }
-        pf[kb][t] = __builtin_bit_cast(bf16x8, w);
-      }
-    }
-    return lt;
+      for (int v = 0; v < 16; ++v) mx = fmaxf(mx, s[kb][v]);
+    return max_halves(mx) * c;
   };
 
   // Prologue: K_0, V_0, K_1 in flight; S_0 computed.
-  dma_tile(Kg, 0, Kring);
-  dma_tile(Vg, 0, Vring);
-  if (nkv > 1) dma_tile(Kg, 1, Kring + TILE);
+  dma_k(0, Kring);
+  dma_v(0, Vring);
+  if (nkv > 1) dma_k(1, Kring + TILE);
   wait_dma();
   __syncthreads();
-  f32x16 sc[NQB][2];
-  qk(Kring, sc);
-  mask(sc, 0);
+  f32x16 sc[KB];
+#pragma unroll
+  for (int kb = 0; kb < KB; ++kb) sc[kb] = f32x16{};
+#pragma unroll
+  for (int ks = 0; ks < KSTEPS; ++ks)
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+      sc[kb] = mfma32(*(const bf16x8*)((const char*)Kring + k_off(kb, ks)), qf[ks], sc[kb]);
+  if (needs_mask(0)) mask(sc, 0);
+  float mt = tile_max(sc);  // scaled maximum of the score tile the next step exponentiates
 
-  for (int j = 0; j < nkv; ++j) {
+  // One key tile: S_j (in cur) -> O; S_{j+1} (into nxt).  P is the ring parity of j;
+  // the loop below is unrolled by two so that every LDS slot offset is a constant and
+  // the score registers swap roles instead of being copied.
+  auto step = [&](const int j, f32x16 (&cur)[KB], f32x16 (&nxt)[KB], auto parity) {
+    constexpr int P = decltype(parity)::value;
+    const char* Ks = (const char*)(Kring + (1 - P) * TILE);          // K_{j+1}
+    const char* Vs = (const char*)(Vring + P * TILE) + v_lds;        // V_j
     // Free slots: K_j's (read by the previous step's QK) and V_{j-1}'s (read by its PV).
-    if (j + 2 < nkv) dma_tile(Kg, j + 2, Kring + (j & 1) * TILE);
-    if (j + 1 < nkv) dma_tile(Vg, j + 1, Vring + ((j + 1) & 1) * TILE);
-    // Free slots: K_j's (read by the previous step's QK) and V_{j-1}'s (read by its PV).
+    if (j + 2 < nkv) dma_k(j + 2, Kring + P * TILE);
+    if (j + 1 < nkv) dma_v(j + 1, Vring + (1 - P) * TILE);
 
-    // Running maximum and the (rare) rescale, before the step's main block.  One
-    // wave-uniform branch covers every query block of the wave.
-    float mt[NQB];
-    bool grow = false;
-#pragma unroll
-    for (int qb = 0; qb < NQB; ++qb) {
-      float mx = -INFINITY;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-        for (int v = 0; v < 16; ++v) mx = fmaxf(mx, sc[qb][kb][v]);
+    // LDS reads of slot i: the K fragment of product i of phase 1, or the two V^T
+    // halves of product i - NQK of phase 2.
+    bf16x8 kfrag[NQK];
+    i16x4 vlo[NPV], vhi[NPV];
+    auto issue = [&](const int i) {
+      if (i < NQK) {
+        kfrag[i] = *(const bf16x8*)(Ks + k_off(i % KB, i / KB));
+      } else if (i < NQK + NPV) {
+        const int p = i - NQK, db = p % DBLK, row = (p / DBLK) * 16;
+        vlo[p] = lds_read_tr16((const uint16_t*)(Vs + blk_chunk_inner<D>(row, db * 4)));
+        vhi[p] = lds_read_tr16((const uint16_t*)(Vs + blk_chunk_inner<D>(row + 8, db * 4)));
       }
-      mt[qb] = max_halves(mx) * c;
-      grow = grow || (mt[qb] > m_ref[qb] + tau);
-    }
-    if (wave_any(grow)) {
+    };
 #pragma unroll
-      for (int qb = 0; qb < NQB; ++qb) {
-        const float m_new = fmaxf(m_ref[qb], mt[qb]);
-        const float alpha = (m_new == -INFINITY) ? 1.0f : exp2_sm<0>(m_ref[qb] - m_new);
-#pragma unroll
-        for (int db = 0; db < DBLK; ++db) oacc[qb][db] *= alpha;
-        l_run[qb] *= alpha;
-        m_ref[qb] = m_new;
-      }
-    }
+    for (int i = 0; i < PD; ++i) issue(i);
 
-    // Main block, free of branches: S_{j+1} = K_{j+1} Q^T on the matrix cores (its slot
-    // holds stale data on the last step; the result is then unused) while the vector
-    // units exponentiate S_j; then O^T += V_j^T P_j^T.
-    f32x16 sn[NQB][2];
-    qk(Kring + ((j + 1) & 1) * TILE, sn);
-    bf16x8 pf[NQB][2][2];
+    // The (rare) rescale.  mt is the scaled maximum of S_j, found while the previous
+    // step's PV products ran; one wave-uniform branch.
+    if (wave_any(mt > m_ref + tau)) {
+      const float m_new = fmaxf(m_ref, mt);
+      const float alpha = (m_new == -INFINITY) ? 1.0f : exp2_sm<0>(m_ref - m_new);
 #pragma unroll
-    for (int qb = 0; qb < NQB; ++qb)
-      l_run[qb] += softmax_exp(sc[qb], m_ref[qb] == -INFINITY ? 0.0f : m_ref[qb], pf[qb]);
+      for (int db = 0; db < DBLK; ++db) oacc[db] *= alpha;
+      l_run *= alpha;
+      m_ref = m_new;
+    }
+    const float mu = m_ref == -INFINITY ? 0.0f : m_ref;
 
-    const uint16_t* Vs = Vring + (j & 1) * TILE;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
+    for (int kb = 0; kb < KB; ++kb) nxt[kb] = f32x16{};
+    uint32_t pw[KB][2][4];  // P_j packed to bf16 pairs: [key block][16-key half][pair]
+    float lt0 = 0.0f, lt1 = 0.0f, mx = -INFINITY;
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        const int row = kb * 32 + t * 16 + vrow;
+    for (int i = 0; i < NQK + NPV; ++i) {
+      issue(i + PD);
+      if (i < NQK) {
+        // Phase 1: one product of S_{j+1}; EPS exponentials of S_j.
+        const int kb = i % KB, ks = i / KB;
+        nxt[kb] = mfma32(kfrag[i], qf[ks], nxt[kb]);
 #pragma unroll
-        for (int db = 0; db < DBLK; ++db) {
-          const bf16x8 va = join(lds_read_tr16(Vs + swz<D>(row, db * 32 + vcol)),
-                                 lds_read_tr16(Vs + swz<D>(row + 8, db * 32 + vcol)));
-#pragma unroll
-          for (int qb = 0; qb < NQB; ++qb) oacc[qb][db] = mfma32(va, pf[qb][kb][t], oacc[qb][db]);
+        for (int e = i * EPS; e < (i + 1) * EPS; e += 2) {
+          const float p0 = exp2_sm<EXPMODE>(fmaf(cur[e >> 4][e & 15], c, -mu));
+          const float p1 = exp2_sm<EXPMODE>(fmaf(cur[e >> 4][(e & 15) + 1], c, -mu));
+          lt0 += p0;
+          lt1 += p1;
+          pw[e >> 4][(e >> 3) & 1][(e & 7) >> 1] = pack_bf16x2(p0, p1);
         }
-        // Bound the transpose reads in flight to one 16-key sub-block (register budget).
-        if (kb * 2 + t < 3) __builtin_amdgcn_sched_barrier(0);
+        // Keep the row-sum additions in this slot (they would otherwise sink below the
+        // barrier, where no matrix product runs beside them).
+        __asm__ volatile("" : "+v"(lt0), "+v"(lt1));
+      } else {
+        // Phase 2: one product of O^T; part of the maximum of S_{j+1} once its last
+        // products have had time to finish.
+        const int p = i - NQK, db = p % DBLK, kb = p / (2 * DBLK), t = (p / DBLK) & 1;
+        const u32x4 w = {pw[kb][t][0], pw[kb][t][1], pw[kb][t][2], pw[kb][t][3]};
+        oacc[db] = mfma32(join(vlo[p], vhi[p]), __builtin_bit_cast(bf16x8, w), oacc[db]);
+        if (p >= MAX0) {
+          const int e0 = (p - MAX0) * NE / (NPV - MAX0), e1 = (p - MAX0 + 1) * NE / (NPV - MAX0);
+#pragma unroll
+          for (int e = e0; e < e1; ++e) mx = fmaxf(mx, nxt[e >> 4][e & 15]);
+        }
       }
+      __builtin_amdgcn_sched_barrier(0);
     }
+    l_run += lt0 + lt1;
+    mt = max_halves(mx) * c;
     wait_dma();
     __syncthreads();
-#pragma unroll
-    for (int qb = 0; qb < NQB; ++qb) {
-      sc[qb][0] = sn[qb][0];
-      sc[qb][1] = sn[qb][1];
+    // S_{j+1} as computed is exact except on tiles that need a mask (at most the last
+    // two of a wave): mask those and take their maximum again.
+    if (j + 1 < nkv && needs_mask((j + 1) * BN)) {
+      mask(nxt, (j + 1) * BN);
+      mt = tile_max(nxt);
     }
-    if (j + 1 < nkv) mask(sc, (j + 1) * BN);
+  };
+
+  f32x16 sn[KB];
+  for (int j = 0; j < nkv; j += 2) {
+    step(j, sc, sn, std::integral_constant<int, 0>{});
+    if (j + 1 < nkv) step(j + 1, sn, sc, std::integral_constant<int, 1>{});
   }
 
   // Epilogue: O = O_acc / l (bf16, round to nearest even) and LSE in natural log.
+  const float l = sum_halves(l_run);
+  const float inv = 1.0f / l;
+  if (qi < S) {
+    uint16_t* orow = a.o + qbase + (size_t)qi * D;
 #pragma unroll
-  for (int qb = 0; qb < NQB; ++qb) {
-    const int qi = qw + qb * 32 + col;
-    const float l = sum_halves(l_run[qb]);
-    const float inv = 1.0f / l;
-    if (qi < S) {
-      uint16_t* orow = a.o + qbase + (size_t)qi * D;
+    for (int db = 0; db < DBLK; ++db) {
 #pragma unroll
-      for (int db = 0; db < DBLK; ++db) {
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          u32x2 w;
-          w[0] = pack_bf16x2(oacc[qb][db][g * 4 + 0] * inv, oacc[qb][db][g * 4 + 1] * inv);
-          w[1] = pack_bf16x2(oacc[qb][db][g * 4 + 2] * inv, oacc[qb][db][g * 4 + 3] * inv);
-          *(u32x2*)(orow + db * 32 + g * 8 + half * 4) = w;
-        }
+      for (int g = 0; g < 4; ++g) {
+        u32x2 w;
+        w[0] = pack_bf16x2(oacc[db][g * 4 + 0] * inv, oacc[db][g * 4 + 1] * inv);
+        w[1] = pack_bf16x2(oacc[db][g * 4 + 2] * inv, oacc[db][g * 4 + 3] * inv);
+        *(u32x2*)(orow + db * 32 + g * 8 + half * 4) = w;
       }
-      if (half == 0) a.lse[((size_t)b * a.Hq + hq) * S + qi] = (m_ref[qb] + log2f(l)) * kLn2;
     }
+    if (half == 0) a.lse[((size_t)b * a.Hq + hq) * S + qi] = (m_ref + log2f(l)) * kLn2;
   }
 }
 
-template <int D, bool CAUSAL, int EXPMODE, int NQB>
+template <int D, bool CAUSAL, int EXPMODE>
 hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t stream) {
-  constexpr int BM = 32 * NQB * kFwdWaves;
-  const int nqt = (a.S + BM - 1) / BM;
+  const int nqt = (a.S + kFwdBM - 1) / kFwdBM;
   const dim3 grid((unsigned)(nqt * a.B * a.Hq));
-  hipLaunchKernelGGL((fwd_kernel<D, CAUSAL, EXPMODE, NQB>), grid, dim3(256), 0, stream, a);
+  hipLaunchKernelGGL((fwd_kernel<D, CAUSAL, EXPMODE>), grid, dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 
-#ifndef FWD_NQB
-#define FWD_NQB 1
-#endif
-
 template <int D>
 hipError_t launch_fwd_d(const FwdArgs& a, bool causal, int exp_mode, hipStream_t stream) {
-  constexpr int N = FWD_NQB;
   if (causal) {
-    return exp_mode == 0 ? launch_fwd_t<D, true, 0, N>(a, stream) : launch_fwd_t<D, true, 1, N>(a, stream);
+    return exp_mode == 0 ? launch_fwd_t<D, true, 0>(a, stream) : launch_fwd_t<D, true, 1>(a, stream);
   }
-  return exp_mode == 0 ? launch_fwd_t<D, false, 0, N>(a, stream) : launch_fwd_t<D, false, 1, N>(a, stream);
+  return exp_mode == 0 ? launch_fwd_t<D, false, 0>(a, stream) : launch_fwd_t<D, false, 1>(a, stream);
 }
 
 __global__ void exp2_eval_kernel(const float* x, float* y, long n, int mode) {
