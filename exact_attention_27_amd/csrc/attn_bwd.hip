@@ -23,6 +23,8 @@
 // In the S accumulator layout of bwd_main (v_mfma_f32_32x32x16_bf16, A = Q rows, B = K^T)
 // a lane holds one key column and 16 query rows; P and dS are packed to bf16 in registers
 // and used directly as the B operand of the dV^T and dK^T products.
+#include <type_traits>
+
 #include "attn_device.h"
 #include "attn_kernels.h"
 
@@ -75,21 +77,43 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const uint16_t* __restrict
 // kq = w % 4 (32 keys) for query half qh = w / 4 of every 64-query step: waves w and
 // w + 4 accumulate partial dK and dV for the same keys over different queries, and
 // the two partials are added through LDS at the end.
+//
+// K, V (resident) and the Q, dO stages sit in LDS as XOR chunk-inner blocks (see
+// attn_device.h): MFMA-operand reads of 16 rows at one chunk and the transpose reads of
+// dO^T and Q^T are both free of bank conflicts, every lane keeps a few base addresses
+// and the rest are immediate offsets, and each 4 DMA lanes fetch one 64-byte piece of a
+// row.  One step is 32 fenced slots of one product each, in four phases:
+//   S  = Q K^T                       (8 products)
+//   dP = dO V^T   beside P = 2^(S c - LSE log2 e), computed in place of S
+//   dV^T += dO^T P   beside dS = P (dP - D), computed in place of dP
+//   dK^T += Q^T dS
+// so the vector work of each phase runs next to matrix products that do not need it;
+// LDS reads run two slots ahead of their products.
 template <int D, bool CAUSAL, int EXPMODE>
 __global__ __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_per_eu(2, 2)))
 void bwd_main_kernel(BwdArgs a) {
   constexpr int KSTEPS = D / 16;
   constexpr int DBLK = D / 32;
-  constexpr int CPR = D / 8;
+  constexpr int CG = D / 32;                   // 4-chunk groups per row
+  constexpr int ROWB = D * 2;                  // bytes per row in memory
   constexpr int KT = kBwdBN * D;               // elements of the K (or V) tile
   constexpr int QT = kBwdBM * D;               // elements of one Q (or dO) tile
-  constexpr int KDMAS = kBwdBN * CPR / 512;    // 16-byte chunks per thread, K or V tile
-  constexpr int QDMAS = kBwdBM * CPR / 512;    // 16-byte chunks per thread, Q or dO tile
-  __shared__ __attribute__((aligned(1024))) uint16_t k_lds[KT];
-  __shared__ __attribute__((aligned(1024))) uint16_t v_lds[KT];
-  __shared__ __attribute__((aligned(1024))) uint16_t q_lds[2][QT];
-  __shared__ __attribute__((aligned(1024))) uint16_t do_lds[2][QT];
-  __shared__ __attribute__((aligned(1024))) float sd_lds[2][2 * kBwdBM];  // [stage][LSE log2e | D]
+  constexpr int KDMAS = kBwdBN / 16 * CG / 8;  // 1024-byte blocks per wave, K or V tile
+  constexpr int QDMAS = kBwdBM / 16 * CG / 8;  // 1024-byte blocks per wave, Q or dO tile
+  constexpr int PD = 2;                        // slots between an LDS read and its product
+  constexpr int NS = 4 * KSTEPS;               // slots per step (== 4 * 2 * DBLK)
+  static_assert(KSTEPS == 2 * DBLK && KDMAS * 8 * 16 == kBwdBN * CG && QDMAS * 8 * 16 == kBwdBM * CG, "tiling");
+  // One LDS buffer, [K | V | Q stage 0 | Q stage 1 | dO stage 0 | dO stage 1 | LSE, D]: every
+  // operand read reaches its tile from a lane's base register by an immediate offset
+  // below 64 KiB (K and V from the K base; the four stages from the Q base).
+  constexpr int K_OFF = 0, V_OFF = 2 * KT, Q_OFF = 4 * KT, DO_OFF = Q_OFF + 4 * QT, SD_OFF = DO_OFF + 4 * QT;
+  static_assert(V_OFF + 2 * KT - K_OFF <= 65536 && SD_OFF - Q_OFF <= 65536, "immediate LDS offsets");
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[SD_OFF + 2 * 2 * kBwdBM * 4];
+  uint16_t* const k_lds = (uint16_t*)(smem + K_OFF);
+  uint16_t* const v_lds = (uint16_t*)(smem + V_OFF);
+  uint16_t* const q_lds[2] = {(uint16_t*)(smem + Q_OFF), (uint16_t*)(smem + Q_OFF + 2 * QT)};
+  uint16_t* const do_lds[2] = {(uint16_t*)(smem + DO_OFF), (uint16_t*)(smem + DO_OFF + 2 * QT)};
+  float (*const sd_lds)[2 * kBwdBM] = (float (*)[2 * kBwdBM])(smem + SD_OFF);  // [stage][LSE log2e | D]
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -114,32 +138,33 @@ void bwd_main_kernel(BwdArgs a) {
   const int key = kw + col;  // this lane's key (column of S)
   const size_t kvbase = ((size_t)b * a.Hkv + hkv) * (size_t)S * D;
 
+  // DMA: wave w fills blocks i * 8 + w of a tile; block bl holds rows 16 (bl / CG) ..,
+  // chunks 4 (bl % CG) ..; lane l fetches row l / 4 of it, chunk (l % 4) ^ ((l / 16) % 4).
+  const int dl_r = lane >> 2, dl_c = (lane & 3) ^ ((lane >> 4) & 3);
   // K and V tiles -> LDS for the whole run (rows past the end are clamped to a real
   // row; their probabilities are masked to 0).
 #pragma unroll
   for (int i = 0; i < KDMAS; ++i) {
-    const int pch = (i * 8 + wave) * 64 + lane;
-    const int r = pch / CPR;
-    const int src = (min(k0 + r, S - 1)) * D + swz_chunk<D>(r, pch % CPR) * 8;
-    dma16(a.k + kvbase + src, k_lds + (i * 8 + wave_u) * 512);
-    dma16(a.v + kvbase + src, v_lds + (i * 8 + wave_u) * 512);
+    const int bl = i * 8 + wave;
+    const int r = (bl / CG) * 16 + dl_r;
+    const size_t src = kvbase + (size_t)min(k0 + r, S - 1) * D + ((bl % CG) * 4 + dl_c) * 8;
+    dma16(a.k + src, k_lds + (i * 8 + wave_u) * 512);
+    dma16(a.v + src, v_lds + (i * 8 + wave_u) * 512);
   }
 
   const int nqt = (S + kBwdBM - 1) / kBwdBM;
   const int q_first = CAUSAL ? (k0 / kBwdBM) : 0;
   const int per_head = nqt - q_first;
   const int steps = G * per_head;
+  const int S_pad = (S + kBwdBM - 1) / kBwdBM * kBwdBM;
 
-  // Q, dO, LSE (log2 units) and D of a step -> LDS stage, all by DMA (LSE and D come
-  // from the padded workspace rows written by the preprocess kernel).
-  int qdma_row[QDMAS], qdma_off[QDMAS];
+  // Per-lane byte offsets of the Q / dO DMA within a tile.
+  uint32_t qd_off[QDMAS];
 #pragma unroll
   for (int i = 0; i < QDMAS; ++i) {
-    const int pch = (i * 8 + wave) * 64 + lane;
-    qdma_row[i] = pch / CPR;
-    qdma_off[i] = swz_chunk<D>(qdma_row[i], pch % CPR) * 8;
+    const int bl = i * 8 + wave;
+    qd_off[i] = (uint32_t)(((bl / CG) * 16 + dl_r) * ROWB + ((bl % CG) * 4 + dl_c) * 16);
   }
-  const int S_pad = (S + kBwdBM - 1) / kBwdBM * kBwdBM;
   // Step order: query tiles from the last one down, the group's heads innermost, so the
   // workgroups of one (batch, KV head), which share an XCD when B*Hkv is a multiple of
   // 8, read the same Q/dO rows at about the same time.
@@ -149,22 +174,48 @@ void bwd_main_kernel(BwdArgs a) {
     const int hq = hkv * G + g;
     const size_t rbase = ((size_t)b * a.Hq + hq) * (size_t)S;
     const int q0 = qt * kBwdBM;
+    const char* qb = (const char*)(a.q + (rbase + q0) * D);
+    const char* ob = (const char*)(a.dO + (rbase + q0) * D);
+    if (q0 + kBwdBM <= S) {
 #pragma unroll
-    for (int i = 0; i < QDMAS; ++i) {
-      const size_t src = (rbase + min(q0 + qdma_row[i], S - 1)) * D + qdma_off[i];
-      dma16(a.q + src, q_lds[st] + (i * 8 + wave_u) * 512);
-      dma16(a.dO + src, do_lds[st] + (i * 8 + wave_u) * 512);
+      for (int i = 0; i < QDMAS; ++i) {
+        dma16_s(qb, qd_off[i], q_lds[st] + (i * 8 + wave_u) * 512);
+        dma16_s(ob, qd_off[i], do_lds[st] + (i * 8 + wave_u) * 512);
+      }
+    } else {
+      int lr = dl_r;
+      __asm__ volatile("" : "+v"(lr));  // keep this rare path's row arithmetic inside it
+#pragma unroll
+      for (int i = 0; i < QDMAS; ++i) {
+        const int row = ((i * 8 + wave) / CG) * 16 + lr;  // row within the tile
+        const int rc = min(q0 + row, S - 1) - q0;
+        const uint32_t off = qd_off[i] + (uint32_t)((rc - row) * ROWB);
+        dma16_s(qb, off, q_lds[st] + (i * 8 + wave_u) * 512);
+        dma16_s(ob, off, do_lds[st] + (i * 8 + wave_u) * 512);
+      }
     }
-    if (wave == 0 && lane < 32) {
+    // LSE log2e (wave 0) and D (wave 1) of the 64 queries: 16 lanes x 16 bytes each.
+    if (wave_u < 2) {
       const size_t pbase = ((size_t)b * a.Hq + hq) * (size_t)S_pad + q0;
-      const float* src = lane < 16 ? a.lse2 + pbase + 4 * lane : a.delta + pbase + 4 * (lane - 16);
-      dma16(reinterpret_cast<const uint16_t*>(src), reinterpret_cast<uint16_t*>(&sd_lds[st][0]));
+      const void* src = uniform_ptr((wave_u == 0 ? a.lse2 : a.delta) + pbase);
+      if (lane < 16) dma16_s(src, (uint32_t)lane * 16u, &sd_lds[st][wave_u * kBwdBM]);
     }
   };
 
-  // Transpose-read lane offsets (see attn_device.h and attn_fwd.hip).
+  // Per-lane LDS byte offsets.  Operand reads (16 rows at one chunk): chunk ks*2 + half,
+  // one register per parity of ks, the rest by (ks / 2) * 1024.
+  const int ra0 = opaque(Q_OFF + blk_chunk_inner_x<D>(qh * 32 + col, half));
+  const int ra1 = opaque(Q_OFF + blk_chunk_inner_x<D>(qh * 32 + col, 2 + half));
+  const int rb0 = opaque(K_OFF + blk_chunk_inner_x<D>(kq * 32 + col, half));
+  const int rb1 = opaque(K_OFF + blk_chunk_inner_x<D>(kq * 32 + col, 2 + half));
+  // Transpose reads of dO^T and Q^T: source lane s reads 4 d-values of query row
+  // qh*32 + t*16 + (s / 32) * 4 + (s % 16) / 4 (+ 8 for the second read) at column
+  // 16 * ((s / 16) % 2) + 4 * (s % 4) of d block db; the rest by (t * CG + db) * 1024.
   const int trow = (lane >> 5) * 4 + ((lane >> 2) & 3);
-  const int tcol = ((lane >> 4) & 1) * 16 + (lane & 3) * 4;
+  const int tcl = ((lane >> 4) & 1) * 2 + ((lane >> 1) & 1);
+  const int tq = Q_OFF + (2 * qh * CG) * 1024 + (lane & 1) * 8;
+  const int tr0 = opaque(tq + (trow * 4 + (tcl ^ ((trow >> 2) & 3))) * 16);
+  const int tr1 = opaque(tq + ((trow + 8) * 4 + (tcl ^ (((trow + 8) >> 2) & 3))) * 16);
 
   f32x16 dk_acc[DBLK], dv_acc[DBLK];
 #pragma unroll
@@ -174,82 +225,128 @@ void bwd_main_kernel(BwdArgs a) {
   }
   const float c = a.scale * kLog2e;  // signed: no running maximum is needed here
 
-  if (steps > 0) stage_in(0, 0);
-  for (int step = 0; step < steps; ++step) {
-    const int st = step & 1;
+  // One step on stage ST; MASKED adds the causal / end-of-sequence mask to P.
+  auto compute = [&](const int q0, auto stage, auto masked) {
+    constexpr int ST = decltype(stage)::value;
+    constexpr bool MASKED = decltype(masked)::value;
+    // Tile offsets from the lane bases (ra*, tr* hold Q stage 0; rb* hold K).
+    constexpr int QS = ST * 2 * QT, OS = DO_OFF - Q_OFF + ST * 2 * QT, VS = V_OFF - K_OFF;
+    const char* L = (const char*)smem;
+    const float* sd = sd_lds[ST];
+    // Mask (MASKED only): register v holds query qb + e_v, e_v = (v/4)*8 + v%4, with
+    // qb = q0 + qh*32 + half*4; P = 0 where e_v < lim_c (key > query) or e_v >= lim_s
+    // (query past the end), and everywhere if the key is past the end.
+    int lim_c = -1, lim_s = 64;
+    if constexpr (MASKED) {
+      const int qb = q0 + qh * 32 + half * 4;
+      lim_s = S - qb;
+      lim_c = key >= S ? 64 : (CAUSAL ? key - qb : -1);
+    }
+
+    bf16x8 fa[NS], fb[NS];  // operand fragments of phase A/B slots
+    i16x4 tlo[NS], thi[NS];   // transpose-read halves of phase C/D slots
+    f32x4 l4[4], d4[4];       // LSE log2e and D of this lane's 16 query rows
+    auto issue = [&](const int i) {
+      if (i < 2 * KSTEPS) {
+        const int ks = i % KSTEPS;
+        const int o = (ks >> 1) * 1024;
+        const int ao = (i < KSTEPS ? QS : OS) + o, bo = (i < KSTEPS ? 0 : VS) + o;
+        fa[i] = *(const bf16x8*)(L + ((ks & 1) ? ra1 : ra0) + ao);
+        fb[i] = *(const bf16x8*)(L + ((ks & 1) ? rb1 : rb0) + bo);
+      } else if (i < NS) {
+        const int p = (i - 2 * KSTEPS) % (2 * DBLK), t = p / DBLK, db = p % DBLK;
+        const int o = (i < 3 * KSTEPS ? OS : QS) + (t * CG + db) * 1024;
+        tlo[i] = lds_read_tr16((const uint16_t*)(L + tr0 + o));
+        thi[i] = lds_read_tr16((const uint16_t*)(L + tr1 + o));
+      }
+      if (i < 4) l4[i] = *(const f32x4*)(&sd[qh * 32 + i * 8 + half * 4]);
+      // D is first needed two slots into phase C: read it at the end of phase B, when the
+      // LSE values are nearly dead.
+      if (i >= 2 * KSTEPS - 2 && i < 2 * KSTEPS + 2) {
+        const int g4 = i - (2 * KSTEPS - 2);
+        d4[g4] = *(const f32x4*)(&sd[kBwdBM + qh * 32 + g4 * 8 + half * 4]);
+      }
+    };
+
+    f32x16 sacc = f32x16{}, dpacc = f32x16{};
+    uint32_t pw[2][4], sw[2][4];  // P and dS packed to bf16 pairs: [t][pair], registers v = 8t ..
+#pragma unroll
+    for (int i = 0; i < PD; ++i) issue(i);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < NS; ++i) {
+      issue(i + PD);
+      if (i < KSTEPS) {
+        sacc = mfma32(fa[i], fb[i], sacc);
+      } else if (i < 2 * KSTEPS) {
+        dpacc = mfma32(fa[i], fb[i], dpacc);
+        // P for a share of the 16 registers, once S has had two slots to finish.
+        const int j = i - KSTEPS - 2;
+        if (j >= 0) {
+          const int n = KSTEPS - 2, e0 = j * 16 / n, e1 = (j + 1) * 16 / n;
+#pragma unroll
+          for (int v = e0; v < e1; ++v) {
+            float p = exp2_sm<EXPMODE>(fmaf(sacc[v], c, -l4[v >> 2][v & 3]));
+            if constexpr (MASKED) {
+              const int ev = (v >> 2) * 8 + (v & 3);
+              p = (ev < lim_c || ev >= lim_s) ? 0.0f : p;
+            }
+            sacc[v] = p;
+            if (v & 1) pw[v >> 3][(v & 7) >> 1] = pack_bf16x2(sacc[v - 1], p);
+          }
+        }
+      } else if (i < 3 * KSTEPS) {
+        const int p = i - 2 * KSTEPS, t = p / DBLK, db = p % DBLK;
+        const u32x4 w = {pw[t][0], pw[t][1], pw[t][2], pw[t][3]};
+        dv_acc[db] = mfma32(join(tlo[i], thi[i]), __builtin_bit_cast(bf16x8, w), dv_acc[db]);
+        // dS for a share of the 16 registers, once dP has had two slots to finish.
+        const int j = p - 2;
+        if (j >= 0) {
+          const int n = 2 * DBLK - 2, e0 = j * 16 / n, e1 = (j + 1) * 16 / n;
+#pragma unroll
+          for (int v = e0; v < e1; ++v) {
+            const float ds = sacc[v] * (dpacc[v] - d4[v >> 2][v & 3]);
+            dpacc[v] = ds;
+            if (v & 1) sw[v >> 3][(v & 7) >> 1] = pack_bf16x2(dpacc[v - 1], ds);
+          }
+        }
+      } else {
+        const int p = i - 3 * KSTEPS, t = p / DBLK, db = p % DBLK;
+        const u32x4 w = {sw[t][0], sw[t][1], sw[t][2], sw[t][3]};
+        dk_acc[db] = mfma32(join(tlo[i], thi[i]), __builtin_bit_cast(bf16x8, w), dk_acc[db]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  auto do_step = [&](const int step, auto stage) {
+    constexpr int ST = decltype(stage)::value;
     wait_dma();
     __syncthreads();  // this step's Q, dO, LSE, D are in LDS; every wave is done with the previous stage
-    const int g = step % G;
+    if (step + 1 < steps) stage_in(step + 1, ST ^ 1);
     const int qt = nqt - 1 - step / G;
-    const int hq = hkv * G + g;
     const int q0 = qt * kBwdBM;
     const int qs = q0 + qh * 32;  // first query of this wave's half
-    if (step + 1 < steps) stage_in(step + 1, st ^ 1);
-
-    const uint16_t* Qs = q_lds[st];
-    const uint16_t* Os = do_lds[st];
     if (!CAUSAL || kw <= qs + 31) {
-      // S = Q K^T and dP = dO V^T, 32 queries x 32 keys: register v holds query
-      // qs + (v/4)*8 + half*4 + v%4 of this lane's key column.
-      f32x16 sacc = f32x16{}, dpacc = f32x16{};
-#pragma unroll
-      for (int ks = 0; ks < KSTEPS; ++ks) {
-        const int aoff = swz<D>(qh * 32 + col, ks * 16 + half * 8);
-        const int boff = swz<D>(kq * 32 + col, ks * 16 + half * 8);
-        sacc = mfma32(*(const bf16x8*)(Qs + aoff), *(const bf16x8*)(k_lds + boff), sacc);
-        dpacc = mfma32(*(const bf16x8*)(Os + aoff), *(const bf16x8*)(v_lds + boff), dpacc);
-      }
       const bool need_mask = (kw + 32 > S) || (qs + 32 > S) || (CAUSAL && kw + 31 > qs);
-      // P and dS packed to bf16: pb[t] / sb[t] hold registers v = 8t .. 8t+7, the B-operand
-      // layout of the dV^T and dK^T products.
-      bf16x8 pb[2], sb[2];
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        u32x4 wp, wsd;
-#pragma unroll
-        for (int gg = 0; gg < 2; ++gg) {
-          const int g4 = 2 * t + gg;
-          const int qr = qh * 32 + g4 * 8 + half * 4;
-          const f32x4 l4 = *(const f32x4*)(&sd_lds[st][qr]);
-          const f32x4 d4 = *(const f32x4*)(&sd_lds[st][kBwdBM + qr]);
-          float pv[4], dsv[4];
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int v = g4 * 4 + r;
-            float p = exp2_sm<EXPMODE>(fmaf(sacc[v], c, -l4[r]));
-            if (need_mask) {
-              const int q = q0 + qr + r;
-              if (key >= S || q >= S || (CAUSAL && key > q)) p = 0.0f;
-            }
-            pv[r] = p;
-            dsv[r] = p * (dpacc[v] - d4[r]);
-          }
-          wp[2 * gg] = pack_bf16x2(pv[0], pv[1]);
-          wp[2 * gg + 1] = pack_bf16x2(pv[2], pv[3]);
-          wsd[2 * gg] = pack_bf16x2(dsv[0], dsv[1]);
-          wsd[2 * gg + 1] = pack_bf16x2(dsv[2], dsv[3]);
-        }
-        pb[t] = __builtin_bit_cast(bf16x8, wp);
-        sb[t] = __builtin_bit_cast(bf16x8, wsd);
-      }
-      // dV^T += dO^T P and dK^T += Q^T dS over this wave's 32 queries.
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        const int row = qh * 32 + t * 16 + trow;
-#pragma unroll
-        for (int db = 0; db < DBLK; ++db) {
-          const int o0 = swz<D>(row, db * 32 + tcol), o1 = swz<D>(row + 8, db * 32 + tcol);
-          dv_acc[db] = mfma32(join(lds_read_tr16(Os + o0), lds_read_tr16(Os + o1)), pb[t], dv_acc[db]);
-          dk_acc[db] = mfma32(join(lds_read_tr16(Qs + o0), lds_read_tr16(Qs + o1)), sb[t], dk_acc[db]);
-        }
+      if (need_mask) {
+        compute(q0, stage, std::true_type{});
+      } else {
+        compute(q0, stage, std::false_type{});
       }
     }
+  };
+
+  if (steps > 0) stage_in(0, 0);
+  for (int step = 0; step < steps; step += 2) {
+    do_step(step, std::integral_constant<int, 0>{});
+    if (step + 1 < steps) do_step(step + 1, std::integral_constant<int, 1>{});
   }
 
   // Add the two query halves' partial dK, dV through LDS (the Q/dO stages are free now),
   // then dK = scale dK_acc, dV = dV_acc.
-  float* red = reinterpret_cast<float*>(&q_lds[0][0]);  // 4 waves x DBLK x 16 x 64 floats
-  static_assert(sizeof(q_lds) + sizeof(do_lds) >= 4 * DBLK * 16 * 64 * sizeof(float), "reduction space");
+  float* red = reinterpret_cast<float*>(smem + Q_OFF);  // 4 waves x DBLK x 16 x 64 floats
+  static_assert(SD_OFF - Q_OFF >= 4 * DBLK * 16 * 64 * (int)sizeof(float), "reduction space");
   __syncthreads();
 #pragma unroll
   for (int pass = 0; pass < 2; ++pass) {
@@ -273,6 +370,8 @@ void bwd_main_kernel(BwdArgs a) {
   }
   if (qh == 0 && key < S) {
     const float ks = a.scale;
+    // The lane's half, recomputed here rather than kept live across the loop.
+    const int half = __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u)) >> 5;
     uint16_t* dkr = a.dk + kvbase + (size_t)key * D;
     uint16_t* dvr = a.dv + kvbase + (size_t)key * D;
 #pragma unroll

@@ -186,6 +186,17 @@ __device__ __forceinline__ void dma16(const void* g, const void* lds_wave_base) 
 
 // The same with a scalar (wave-uniform) 64-bit base and a 32-bit per-lane byte offset:
 // no per-lane address arithmetic when the offsets stay fixed across a loop.
+// A wave-uniform pointer moved to scalar registers (lane 0's copy).  For code where the
+// compiler cannot prove uniformity (divergent branches) but a scalar base is required.
+// readfirstlane returns a signed int: both halves go through uint32_t so that neither
+// is sign-extended into the other.
+__device__ __forceinline__ const void* uniform_ptr(const void* p) {
+  const uint64_t b64 = (uint64_t)(uintptr_t)p;
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(b64 >> 32));
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)b64);
+  return (const void*)(uintptr_t)(((uint64_t)hi << 32) | (uint64_t)lo);
+}
+
 __device__ __forceinline__ void dma16_s(const void* sbase, uint32_t voff, const void* lds_wave_base) {
   const uint32_t l = lds_addr(lds_wave_base);
   const uint32_t ls = __builtin_amdgcn_readfirstlane(l);
@@ -193,6 +204,14 @@ __device__ __forceinline__ void dma16_s(const void* sbase, uint32_t voff, const 
                    :
                    : "s"(ls), "v"(voff), "s"(sbase)
                    : "memory", "m0");
+}
+
+// A value the optimiser must treat as unknown: keeps a base address in one register
+// instead of letting its constant part merge into per-use offsets past what the LDS
+// instructions' 16-bit immediate can hold.
+__device__ __forceinline__ int opaque(int x) {
+  __asm__ volatile("" : "+v"(x));
+  return x;
 }
 
 // Wait until every DMA (and every other vector memory operation) of the wave is done.
