@@ -285,7 +285,8 @@ void bwd_main_kernel(BwdArgs a) {
         if (j >= 0) {
           const int n = KSTEPS - 2, e0 = j * 16 / n, e1 = (j + 1) * 16 / n;
 #pragma unroll
-          for (int v = e0; v < e1; ++v) {
+          for (int v = 0; v < 16; ++v) {
+            if (v < e0 || v >= e1) continue;
             float p = exp2_sm<EXPMODE>(fmaf(sacc[v], c, -l4[v >> 2][v & 3]));
             if constexpr (MASKED) {
               const int ev = (v >> 2) * 8 + (v & 3);
@@ -304,7 +305,8 @@ void bwd_main_kernel(BwdArgs a) {
         if (j >= 0) {
           const int n = 2 * DBLK - 2, e0 = j * 16 / n, e1 = (j + 1) * 16 / n;
 #pragma unroll
-          for (int v = e0; v < e1; ++v) {
+          for (int v = 0; v < 16; ++v) {
+            if (v < e0 || v >= e1) continue;
             const float ds = sacc[v] * (dpacc[v] - d4[v >> 2][v & 3]);
             dpacc[v] = ds;
             if (v & 1) sw[v >> 3][(v & 7) >> 1] = pack_bf16x2(dpacc[v - 1], ds);
@@ -400,6 +402,13 @@ void bwd_main_kernel(BwdArgs a) {
 //     dQ^T += K^T dS^T                              (K^T by LDS transpose reads)
 // It recomputes S and dP (two of the backward's five products) instead of adding
 // partial dQ blocks from every key tile with fp32 atomics, and it is deterministic.
+//
+// K and V tiles sit in LDS as XOR chunk-inner blocks (attn_device.h), filled by coalesced
+// DMA; both the operand reads of K and V and the transpose reads of K^T are free of bank
+// conflicts.  One tile is 48 fenced slots of one product each: S^T (16), then dP^T
+// beside P^T = 2^(S^T c - LSE log2 e) computed in place of S^T, then dQ^T beside
+// dS^T = P^T (dP^T - D) computed in place of dP^T, one 8-key block ahead of the products
+// that use it.  LDS reads run two slots ahead.
 constexpr int kDqBM = 128;  // queries per workgroup
 constexpr int kDqBN = 64;   // keys per tile
 
@@ -407,11 +416,18 @@ template <int D, bool CAUSAL, int EXPMODE>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(2, 2)))
 void bwd_dq_kernel(BwdArgs a) {
   constexpr int BN = kDqBN;
+  constexpr int KB = BN / 32;           // 32-key blocks per tile
   constexpr int KSTEPS = D / 16;
   constexpr int DBLK = D / 32;
-  constexpr int CPR = D / 8;
-  constexpr int TILE = BN * D;
-  constexpr int DMAS = BN * CPR / 256;
+  constexpr int CG = D / 32;            // 4-chunk groups per row
+  constexpr int ROWB = D * 2;           // bytes per row in memory
+  constexpr int TILE = BN * D;          // elements of one K or V tile
+  constexpr int DMAS = BN / 16 * CG / 4;  // 1024-byte blocks per wave per tile
+  constexpr int NA = KSTEPS * KB;       // S^T slots
+  constexpr int NC = 2 * KB * DBLK;     // dQ^T slots
+  constexpr int NS = 2 * NA + NC;       // slots per tile
+  constexpr int PD = 2;
+  static_assert(DMAS * 4 * 16 == BN * CG && KB == 2, "tiling");
   __shared__ __attribute__((aligned(1024))) uint16_t smem[4 * TILE];  // K ring (2 tiles), V ring (2 tiles)
 
   const int tid = threadIdx.x;
@@ -458,106 +474,171 @@ void bwd_dq_kernel(BwdArgs a) {
   const int kv_end = CAUSAL ? min(S, q0 + kDqBM) : S;
   const int nkv = (kv_end + BN - 1) / BN;
 
+  // DMA of a tile: wave w fills blocks 4 i + w; lane l fetches row l / 4 of the block,
+  // chunk (l % 4) ^ ((l / 16) % 4).  Fixed per-lane offsets from a scalar tile base; the
+  // last tile, if it runs past the end of the sequence, clamps its rows (their scores
+  // are masked).
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  const int dl_r = lane >> 2, dl_c = (lane & 3) ^ ((lane >> 4) & 3);
   uint32_t dma_off[DMAS];
 #pragma unroll
   for (int i = 0; i < DMAS; ++i) {
-    const int pch = (i * 4 + wave) * 64 + lane;
-    const int r = pch / CPR;
-    dma_off[i] = (uint32_t)(r * D + swz_chunk<D>(r, pch % CPR) * 8) * 2u;
+    const int bl = i * 4 + wave;
+    dma_off[i] = (uint32_t)(((bl / CG) * 16 + dl_r) * ROWB + ((bl % CG) * 4 + dl_c) * 16);
   }
-  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
   auto dma_tile = [&](const uint16_t* __restrict__ src, int j, uint16_t* slot) {
-    const uint16_t* base = src + (size_t)j * BN * D;
+    const char* base = (const char*)(src + (size_t)j * BN * D);
     if (j * BN + BN <= S) {
 #pragma unroll
       for (int i = 0; i < DMAS; ++i) dma16_s(base, dma_off[i], slot + (i * 4 + wave_u) * 512);
     } else {
+      int lr = dl_r;
+      __asm__ volatile("" : "+v"(lr));  // keep this rare path's row arithmetic inside it
 #pragma unroll
       for (int i = 0; i < DMAS; ++i) {
-        const int pch = (i * 4 + wave) * 64 + lane;
-        const int r = pch / CPR;
-        const int rc = min(j * BN + r, S - 1) - j * BN;
-        const uint32_t off = (uint32_t)(rc * D + swz_chunk<D>(r, pch % CPR) * 8) * 2u;
-        dma16_s(base, off, slot + (i * 4 + wave_u) * 512);
+        const int row = ((i * 4 + wave) / CG) * 16 + lr;  // row within the tile
+        const int rc = min(j * BN + row, S - 1) - j * BN;
+        dma16_s(base, dma_off[i] + (uint32_t)((rc - row) * ROWB), slot + (i * 4 + wave_u) * 512);
       }
     }
   };
   uint16_t* const Kring = smem;
   uint16_t* const Vring = smem + 2 * TILE;
 
+  // Per-lane LDS byte offsets.  K and V operand reads: key row kb*32 + col, chunk
+  // ks*2 + half (one register per parity of ks).  K^T transpose reads: source lane s
+  // reads 4 d-values of key row kb*32 + t*16 + (s / 32) * 4 + (s % 16) / 4 (+ 8 for the
+  // second read) at column 16 * ((s / 16) % 2) + 4 * (s % 4) of d block db.
+  const int ka0 = opaque(blk_chunk_inner_x<D>(col, half)), ka1 = opaque(blk_chunk_inner_x<D>(col, 2 + half));
   const int trow = (lane >> 5) * 4 + ((lane >> 2) & 3);
-  const int tcol = ((lane >> 4) & 1) * 16 + (lane & 3) * 4;
+  const int tcl = ((lane >> 4) & 1) * 2 + ((lane >> 1) & 1);
+  const int tr0 = opaque((trow * 4 + (tcl ^ ((trow >> 2) & 3))) * 16 + (lane & 1) * 8);
+  const int tr1 = opaque(((trow + 8) * 4 + (tcl ^ (((trow + 8) >> 2) & 3))) * 16 + (lane & 1) * 8);
 
   f32x16 dq[DBLK];
 #pragma unroll
   for (int db = 0; db < DBLK; ++db) dq[db] = f32x16{};
 
-  dma_tile(Kg, 0, Kring);
-  dma_tile(Vg, 0, Vring);
-  wait_dma();
-  __syncthreads();
+  // One key tile on ring slot P; MASKED adds the causal / end-of-sequence mask to P^T.
+  auto compute = [&](const int j, auto parity, auto masked) __attribute__((always_inline)) {
+    constexpr int P = decltype(parity)::value;
+    constexpr bool MASKED = decltype(masked)::value;
+    constexpr int KO = P * TILE * 2, VO = (2 + P) * TILE * 2;  // byte offsets of K_j, V_j
+    const char* L = (const char*)smem;
+    const int k0 = j * BN;
+    int lim = BN;  // keys at tile positions e > lim are masked
+    if constexpr (MASKED) {
+      const int lim_s = S - 1 - k0 - half * 4;
+      lim = CAUSAL ? min(lim_s, qi - k0 - half * 4) : lim_s;
+    }
+    bf16x8 fr[2 * NA];      // K / V fragments of the S^T and dP^T slots
+    i16x4 tlo[NC], thi[NC];  // K^T transpose-read halves of the dQ^T slots
+    auto issue = [&](const int i) __attribute__((always_inline)) {
+      if (i < 2 * NA) {
+        const int k = i % NA, kb = k % KB, ks = k / KB;
+        const int o = (i < NA ? KO : VO) + kb * 32 / 16 * CG * 1024 + (ks >> 1) * 1024;
+        fr[i] = *(const bf16x8*)(L + ((ks & 1) ? ka1 : ka0) + o);
+      } else if (i < NS) {
+        const int p = i - 2 * NA, u = p / DBLK, db = p % DBLK;  // u = kb * 2 + t
+        const int o = KO + (u * CG + db) * 1024;
+        tlo[p] = lds_read_tr16((const uint16_t*)(L + tr0 + o));
+        thi[p] = lds_read_tr16((const uint16_t*)(L + tr1 + o));
+      }
+    };
+    f32x16 s[KB], dp[KB];
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+      s[kb] = f32x16{};
+      dp[kb] = f32x16{};
+    }
+    uint32_t dw[2 * KB][4];  // dS^T packed to bf16 pairs: [kb * 2 + t][pair]
+    // dS for 8-key block u (registers v = 8t .. 8t+7 of key block kb).
+    auto ds_block = [&](const int u, const int v0, const int v1) __attribute__((always_inline)) {
+      const int kb = u >> 1;
+#pragma unroll
+      for (int vv = 0; vv < 8; ++vv) {
+        if (vv < v0 || vv >= v1) continue;
+        const int v = (u & 1) * 8 + vv;
+        const float ds = s[kb][v] * (dp[kb][v] - dd);
+        dp[kb][v] = ds;
+        if (v & 1) dw[u][(v & 7) >> 1] = pack_bf16x2(dp[kb][v - 1], ds);
+      }
+    };
+#pragma unroll
+    for (int i = 0; i < PD; ++i) issue(i);
+    __builtin_amdgcn_sched_barrier(0);
+    // Three loops, one per phase (each small enough to unroll completely).
+#pragma unroll
+    for (int i = 0; i < NA; ++i) {
+      issue(i + PD);
+      const int kb = i % KB, ks = i / KB;
+      s[kb] = mfma32(fr[i], qf[ks], s[kb]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int i = NA; i < 2 * NA; ++i) {
+      issue(i + PD);
+      const int k = i - NA, kb = k % KB, ks = k / KB;
+      dp[kb] = mfma32(fr[i], of[ks], dp[kb]);
+      // P^T for a share of the 32 scores, once S^T has had a slot to finish.
+      if (k >= 1) {
+        const int n = NA - 1, e0 = (k - 1) * 2 * 16 / n, e1 = k * 2 * 16 / n;
+#pragma unroll
+        for (int e = 0; e < 2 * 16; ++e) {
+          if (e < e0 || e >= e1) continue;
+          float p = exp2_sm<EXPMODE>(fmaf(s[e >> 4][e & 15], c, -lse2));
+          if constexpr (MASKED) {
+            const int ek = (e >> 4) * 32 + ((e & 15) >> 2) * 8 + (e & 3);  // key - k0 - half*4
+            p = ek > lim ? 0.0f : p;
+          }
+          s[e >> 4][e & 15] = p;
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int i = 2 * NA; i < NS; ++i) {
+      issue(i + PD);
+      const int p = i - 2 * NA, u = p / DBLK, db = p % DBLK;
+      // dS for block u before its first product, and for block u + 1 beside the
+      // products of block u.
+      if (p == 0) ds_block(0, 0, 8);
+      if (u + 1 < 2 * KB) {
+        const int r = p % DBLK;
+        ds_block(u + 1, r * 8 / DBLK, (r + 1) * 8 / DBLK);
+      }
+      const u32x4 w = {dw[u][0], dw[u][1], dw[u][2], dw[u][3]};
+      dq[db] = mfma32(join(tlo[p], thi[p]), __builtin_bit_cast(bf16x8, w), dq[db]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
 
-  for (int j = 0; j < nkv; ++j) {
-    const int st = j & 1;
+  auto step = [&](const int j, auto parity) {
+    constexpr int P = decltype(parity)::value;
     if (j + 1 < nkv) {
-      dma_tile(Kg, j + 1, Kring + (st ^ 1) * TILE);
-      dma_tile(Vg, j + 1, Vring + (st ^ 1) * TILE);
+      dma_tile(Kg, j + 1, Kring + (1 - P) * TILE);
+      dma_tile(Vg, j + 1, Vring + (1 - P) * TILE);
     }
     const int k0 = j * BN;
     if (!CAUSAL || k0 <= qw + 31) {
-      const uint16_t* Ks = Kring + st * TILE;
-      const uint16_t* Vs = Vring + st * TILE;
-      f32x16 s[2] = {f32x16{}, f32x16{}}, dp[2] = {f32x16{}, f32x16{}};
-#pragma unroll
-      for (int ks = 0; ks < KSTEPS; ++ks) {
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-          const int off = swz<D>(kb * 32 + col, ks * 16 + half * 8);
-          s[kb] = mfma32(*(const bf16x8*)(Ks + off), qf[ks], s[kb]);
-          dp[kb] = mfma32(*(const bf16x8*)(Vs + off), of[ks], dp[kb]);
-        }
-      }
       const bool need_mask = (k0 + BN > S) || (CAUSAL && k0 + BN - 1 > qw);
-      const int lim_s = S - 1 - k0 - half * 4;
-      const int lim = CAUSAL ? min(lim_s, qi - k0 - half * 4) : lim_s;
-      bf16x8 dsf[2][2];
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-          u32x4 w;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            float d2[2];
-#pragma unroll
-            for (int u = 0; u < 2; ++u) {
-              const int v = t * 8 + 2 * e + u;
-              float p = exp2_sm<EXPMODE>(fmaf(s[kb][v], c, -lse2));
-              if (need_mask && kb * 32 + (v >> 2) * 8 + (v & 3) > lim) p = 0.0f;
-              d2[u] = p * (dp[kb][v] - dd);
-            }
-            w[e] = pack_bf16x2(d2[0], d2[1]);
-          }
-          dsf[kb][t] = __builtin_bit_cast(bf16x8, w);
-        }
-      }
-      // dQ^T += K^T dS^T
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-          const int row = kb * 32 + t * 16 + trow;
-#pragma unroll
-          for (int db = 0; db < DBLK; ++db) {
-            const bf16x8 kt = join(lds_read_tr16(Ks + swz<D>(row, db * 32 + tcol)),
-                                   lds_read_tr16(Ks + swz<D>(row + 8, db * 32 + tcol)));
-            dq[db] = mfma32(kt, dsf[kb][t], dq[db]);
-          }
-        }
+      if (need_mask) {
+        compute(j, parity, std::true_type{});
+      } else {
+        compute(j, parity, std::false_type{});
       }
     }
     wait_dma();
     __syncthreads();
+  };
+
+  dma_tile(Kg, 0, Kring);
+  dma_tile(Vg, 0, Vring);
+  wait_dma();
+  __syncthreads();
+  for (int j = 0; j < nkv; j += 2) {
+    step(j, std::integral_constant<int, 0>{});
+    if (j + 1 < nkv) step(j + 1, std::integral_constant<int, 1>{});
   }
 
   if (qi < S) {
