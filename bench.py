@@ -15,6 +15,8 @@ fp64 oracle timed on this host on a bounded sample of the same workload.
 """
 
 import argparse
+import glob
+import hashlib
 import json
 import math
 import os
@@ -45,6 +47,28 @@ def parse():
                     help="instead of the benchmark, run a plain device copy of MIB MiB (3 times): the "
                          "reference kernel that scales rocprofv3 FETCH_SIZE/WRITE_SIZE into bytes")
     return ap.parse_args()
+
+
+def traffic_record(kernel: str, workload: str):
+    """HBM bytes per launch of `kernel` on `workload` from the counter record committed under
+    profiles/ (rocprofv3 FETCH_SIZE and WRITE_SIZE, each scaled by the same counter's reading
+    for a plain device copy), or None when there is no record or the kernel's sources have
+    changed since it was taken (the record holds their SHA-256)."""
+    h = hashlib.sha256()
+    for n in ("attn_bwd.hip", "attn_device.h", "attn_kernels.h") if kernel.startswith("bwd") else \
+             ("attn_fwd.hip", "attn_device.h", "attn_kernels.h"):
+        with open(os.path.join(ROOT, "exact_attention_27_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    for path in sorted(glob.glob(os.path.join(ROOT, "profiles", "*.md"))):
+        with open(path) as f:
+            for line in f:
+                if not line.startswith("record: "):
+                    continue
+                rec = json.loads(line[len("record: "):])
+                if rec.get("kernel") == kernel and rec.get("workload") == workload and \
+                        rec.get("source_sha256") == h.hexdigest():
+                    return int(rec["bytes_per_launch"])
+    return None
 
 
 def copy_calibration(mib: int) -> None:
@@ -174,8 +198,10 @@ def main():
         main_ms = fwd_ms
         achieved = fwd_tf
         dominant = "fwd_kernel"
+    traffic = traffic_record(dominant, w.name)
     roofline = {"kernel": dominant, "bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
+                "traffic_unit": "bytes per launch (HBM, rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
                 "avg_launch_ms": round(main_ms, 4)}
     breakdown = {"fwd_ms": round(fwd_ms, 4), "fwd_tflops": round(fwd_tf, 2),
                  "fwd_frac_of_peak": round(fwd_tf / PEAK_BF16_TFLOPS, 4)}
