@@ -30,7 +30,11 @@ if ROOT not in sys.path:
 METRIC = "attention fwd/bwd bf16 TFLOPS and % of MI355X MFMA peak, S=2k–32k, d=128"
 PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA, published (256 CU x 4096 flop/clk x 2.4 GHz)
 
-NAMES = {"tiny_fwd": 1, "prefill_fwd": 2, "long_context_fwd": 3, "bwd": 4, "gqa_fwd_bwd": 5}
+
+
+def workload_names():
+    import workloads
+    return {w.name: n for n, w in workloads.WORKLOADS.items()}
 
 
 def parse():
@@ -38,7 +42,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="gqa_fwd_bwd", choices=sorted(NAMES))
+    ap.add_argument("--workload", default="gqa_fwd_bwd", choices=sorted(workload_names()))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target oracle sample time")
     ap.add_argument("--exp-mode", type=int, default=None)
@@ -135,7 +139,7 @@ def main():
     import exact_attention_27_amd as ea
     import workloads
 
-    w = workloads.WORKLOADS[NAMES[args.workload]]
+    w = workloads.WORKLOADS[workload_names()[args.workload]]
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     host = workloads.make_inputs(w)

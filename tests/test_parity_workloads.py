@@ -125,3 +125,24 @@ def test_gqa_fwd_bwd():
     host, dev = load(w)
     o, lse = fwd_check(w, host, dev, rows_per_head=60, seed=5000)
     bwd_check(w, host, dev, o, lse, kv_heads=[(1, 5)])
+
+
+def test_long_64k_fwd():
+    w = workloads.WORKLOADS[6]
+    print(f"\n[{w.name}] {w.describe()}", flush=True)
+    host, dev = load(w)
+    fwd_check(w, host, dev, rows_per_head=48, seed=6000)
+
+
+def test_long_128k_fwd():
+    w = workloads.WORKLOADS[7]
+    print(f"\n[{w.name}] {w.describe()} (MQA: 4 query heads on 1 KV head)", flush=True)
+    host, dev = load(w)
+    fwd_check(w, host, dev, rows_per_head=48, seed=7000)
+
+
+def test_long_noncausal_fwd():
+    w = workloads.WORKLOADS[8]
+    print(f"\n[{w.name}] {w.describe()}", flush=True)
+    host, dev = load(w)
+    fwd_check(w, host, dev, rows_per_head=48, seed=8000)

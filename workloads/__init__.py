@@ -6,7 +6,7 @@ without sharing any of the method.
 
 Recipe (the same everywhere):
   * ``torch.Generator('cpu').manual_seed(seed)``; by default ``seed`` is the
-    workload number (1-5).
+    workload number.
   * Draw order: Q, K, V, dO, each ``torch.randn`` fp32 N(0, 1) with its full
     shape ([B,Hq,S,d] for Q and dO, [B,Hkv,S,d] for K and V).
   * Long-context workload only: for each batch entry, ``floor(0.01 * S)`` distinct
@@ -66,6 +66,11 @@ WORKLOADS: Dict[int, Workload] = {
     3: Workload(3, "long_context_fwd", 1, 16, 16, 32768, 128, True, ("fwd",), outlier_frac=0.01),
     4: Workload(4, "bwd", 4, 16, 16, 4096, 128, True, ("fwd", "bwd")),
     5: Workload(5, "gqa_fwd_bwd", 2, 32, 8, 8192, 128, True, ("fwd", "bwd")),
+    # Longer contexts and the non-causal long forward (the pages' long-context motivation:
+    # throughput against S beyond 32k).
+    6: Workload(6, "long_64k_fwd", 1, 8, 8, 65536, 128, True, ("fwd",)),
+    7: Workload(7, "long_128k_fwd", 1, 4, 1, 131072, 128, True, ("fwd",)),
+    8: Workload(8, "long_noncausal_fwd", 1, 16, 16, 32768, 128, False, ("fwd",)),
 }
 
 
