@@ -34,7 +34,15 @@ PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA, published (256 CU x 4096 f
 
 def workload_names():
     import workloads
-    return {w.name: n for n, w in workloads.WORKLOADS.items()}
+    names = {w.name: n for n, w in workloads.WORKLOADS.items()}
+    names.update({w.name: n for n, w in workloads.VARLEN_WORKLOADS.items()})
+    return names
+
+
+def get_workload(name):
+    import workloads
+    n = workload_names()[name]
+    return workloads.WORKLOADS[n] if n in workloads.WORKLOADS else workloads.VARLEN_WORKLOADS[n]
 
 
 def parse():
@@ -125,6 +133,103 @@ def cpu_baseline(w, inputs, target_s):
     }
 
 
+def cpu_baseline_varlen(w, inputs, target_s):
+    """The fp64 oracle forward of one (sequence, query head) pair at a time, sequences in
+    packed order, until about target_s seconds have passed."""
+    import numpy as np
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+    except Exception:  # noqa: BLE001
+        threads = os.cpu_count() or 1
+    cu = inputs["cu_seqlens"].tolist()
+    pairs, toks, flop, t0 = 0, 0, 0.0, time.perf_counter()
+    done = False
+    for s in range(len(cu) - 1):
+        a, n = cu[s], cu[s + 1] - cu[s]
+        for h in range(w.Hq):
+            hk = oracle.kv_head_of(h, w.Hq, w.Hkv)
+            f = lambda x, hh: x[a:a + n, hh].float().numpy().astype(np.float64)
+            oracle.head_forward(f(inputs["q"], h), f(inputs["k"], hk), f(inputs["v"], hk), w.scale, w.causal)
+            flop += 4.0 * n * n * w.d / (2 if w.causal else 1)
+            pairs += 1
+            toks += n
+            if time.perf_counter() - t0 >= target_s:
+                done = True
+                break
+        if done:
+            break
+    dt = time.perf_counter() - t0
+    return {
+        "value": flop / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+        "sample": f"fp64 numpy oracle, fwd of {pairs} of {w.n * w.Hq} (sequence, query head) pairs "
+                  f"({toks} query rows) of the packed batch, d={w.d}, {dt:.1f} s; algorithmic flop",
+    }
+
+
+def main_varlen(args, w):
+    """Time the packed forward (attn_fwd_varlen) on a variable-length workload."""
+    import torch
+    import exact_attention_27_amd as ea
+    import workloads
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    host = workloads.make_varlen_inputs(w)
+    t = {n: x.to(dev) for n, x in host.items()}
+    lens = w.lengths()
+    total = sum(lens)
+    opt = ea.attn_default_options()
+    if args.exp_mode is not None:
+        opt.exp_mode = args.exp_mode
+    if args.tau is not None:
+        opt.tau = args.tau
+    o = torch.empty_like(t["q"])
+    lse = torch.empty((w.Hq, total), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        ea.attn_fwd_varlen(t["q"], t["k"], t["v"], t["cu_seqlens"], max(lens), w.scale, w.causal, o=o, lse=lse,
+                           opt=opt, stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev[0].record(stream)
+    for _ in range(args.steps):
+        step()
+    ev[1].record(stream)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms_step = elapsed * 1e3 / args.steps
+    fwd_ms = ev[0].elapsed_time(ev[1]) / args.steps
+    flop = w.fwd_flop()
+    value = flop / (ms_step * 1e-3) / 1e12
+    fwd_tf = flop / (fwd_ms * 1e-3) / 1e12
+    roofline = {"kernel": "fwd_kernel", "bound": "mfma", "achieved": round(fwd_tf, 2), "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(fwd_tf / PEAK_BF16_TFLOPS, 4),
+                "traffic": traffic_record("fwd_kernel", w.name),
+                "traffic_unit": "bytes per launch (HBM, rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
+                "avg_launch_ms": round(fwd_ms, 4)}
+    cpu = None if args.no_cpu_baseline else cpu_baseline_varlen(w, host, args.cpu_seconds)
+    line = {
+        "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": w.name, "sequences": w.n, "lengths": f"{min(lens)}..{max(lens)} log-uniform",
+                   "total_tokens": total, "Hq": w.Hq, "Hkv": w.Hkv, "d": w.d, "causal": w.causal,
+                   "passes": "fwd", "exp_mode": int(opt.exp_mode), "tau": float(opt.tau), "step_flop": flop},
+        "frac_of_peak": round(value / PEAK_BF16_TFLOPS, 4),
+        "roofline": roofline, "breakdown": {"fwd_ms": round(fwd_ms, 4), "fwd_tflops": round(fwd_tf, 2)},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
 def main():
     args = parse()
     if args.copy_calibration:
@@ -139,7 +244,10 @@ def main():
     import exact_attention_27_amd as ea
     import workloads
 
-    w = workloads.WORKLOADS[workload_names()[args.workload]]
+    w = get_workload(args.workload)
+    if isinstance(w, workloads.VarlenWorkload):
+        main_varlen(args, w)
+        return
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     host = workloads.make_inputs(w)

@@ -5,7 +5,7 @@ kernels.  torch supplies device memory and the current stream.  There is no fall
 if libattn.so is missing or fails to load, every call raises.
 
 The functions carry the C names:
-    attn_fwd, attn_fwd_ex, attn_bwd, attn_bwd_ex, attn_bwd_phase, attn_bwd_workspace_bytes,
+    attn_fwd, attn_fwd_ex, attn_fwd_varlen, attn_bwd, attn_bwd_ex, attn_bwd_phase, attn_bwd_workspace_bytes,
     attn_default_options, attn_status_string, attn_exp2_eval, attn_exp2_poly_host
 """
 
@@ -20,7 +20,7 @@ import torch
 
 __all__ = [
     "AttnError", "attn_options", "library_path", "lib",
-    "attn_fwd", "attn_fwd_ex", "attn_bwd", "attn_bwd_ex", "attn_bwd_phase", "attn_bwd_workspace_bytes",
+    "attn_fwd", "attn_fwd_ex", "attn_fwd_varlen", "attn_bwd", "attn_bwd_ex", "attn_bwd_phase", "attn_bwd_workspace_bytes",
     "attn_default_options", "attn_status_string", "attn_exp2_eval", "attn_exp2_poly_host",
     "ATTN_EXP_HW", "ATTN_EXP_POLY3",
 ]
@@ -67,6 +67,9 @@ def lib() -> ctypes.CDLL:
         L.attn_status_string.argtypes = [_I]
         L.attn_fwd.restype = _I
         L.attn_fwd.argtypes = [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _P]
+        L.attn_fwd_varlen.restype = _I
+        L.attn_fwd_varlen.argtypes = [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _I,
+                                      ctypes.POINTER(attn_options), _P]
         L.attn_fwd_ex.restype = _I
         L.attn_fwd_ex.argtypes = [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I,
                                   ctypes.POINTER(attn_options), _P]
@@ -167,6 +170,44 @@ def attn_fwd_ex(q, k, v, scale: Optional[float] = None, causal: bool = False,
         st = lib().attn_fwd_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, Hq, Hkv, S, d,
                                scale, int(bool(causal)), None if op is None else ctypes.byref(op),
                                _stream(stream))
+    _check(st)
+    return o, lse
+
+
+def attn_fwd_varlen(q, k, v, cu_seqlens, max_seqlen: int, scale: Optional[float] = None, causal: bool = False,
+                    o: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                    opt: Optional[attn_options] = None, exp_mode: Optional[int] = None,
+                    tau: Optional[float] = None, stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Forward pass over a packed batch of sequences of different lengths.
+
+    q: [total, Hq, d], k and v: [total, Hkv, d] bf16; cu_seqlens: [nseq + 1] int32 device
+    tensor of token offsets; max_seqlen should be >= every length (query rows past it
+    are not written).  Returns (o [total, Hq, d] bf16, lse [Hq, total] fp32).  scale
+    defaults to 1/sqrt(d)."""
+    if q.dim() != 3 or k.dim() != 3:
+        raise ValueError("q and k must be [total, H, d]")
+    total, Hq, d = (int(x) for x in q.shape)
+    Hkv = int(k.shape[1])
+    _need(q, "q", torch.bfloat16, (total, Hq, d))
+    _need(k, "k", torch.bfloat16, (total, Hkv, d))
+    _need(v, "v", torch.bfloat16, (total, Hkv, d))
+    if cu_seqlens.dtype != torch.int32 or cu_seqlens.dim() != 1 or not cu_seqlens.is_contiguous():
+        raise ValueError("cu_seqlens must be a contiguous 1-D int32 tensor")
+    if cu_seqlens.device != q.device:
+        raise ValueError("cu_seqlens must be on the same device as q")
+    nseq = int(cu_seqlens.numel()) - 1
+    if o is None:
+        o = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((Hq, total), dtype=torch.float32, device=q.device)
+    _need(o, "o", torch.bfloat16, (total, Hq, d))
+    _need(lse, "lse", torch.float32, (Hq, total))
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    op = _options(opt, exp_mode, tau)
+    with torch.cuda.device(q.device):
+        st = lib().attn_fwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(cu_seqlens),
+                                   max(nseq, 0), total, int(max_seqlen), Hq, Hkv, d, scale, int(bool(causal)),
+                                   None if op is None else ctypes.byref(op), _stream(stream))
     _check(st)
     return o, lse
 

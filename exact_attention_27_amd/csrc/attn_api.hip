@@ -103,6 +103,8 @@ int attn_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse
   a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.S = S;
   scale_setup(scale, &a.c, &a.q_and, &a.q_xor);
   a.tau = o_.tau;
+  a.cu_seqlens = nullptr;
+  a.total = 0;
   (void)hipGetLastError();  // a stale error from earlier work is not this call's failure
   return hip_status(attn::launch_fwd(a, d, causal != 0, o_.exp_mode, static_cast<hipStream_t>(stream)));
 }
@@ -110,6 +112,42 @@ int attn_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse
 int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
              int B, int Hq, int Hkv, int S, int d, float scale, int causal, void* stream) {
   return attn_fwd_ex(q, k, v, o, lse, B, Hq, Hkv, S, d, scale, causal, nullptr, stream);
+}
+
+int attn_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
+                    const int* cu_seqlens, int nseq, int total, int max_seqlen,
+                    int Hq, int Hkv, int d, float scale, int causal,
+                    const attn_options* opt, void* stream) {
+  if (nseq < 0 || total < 0 || max_seqlen < 0 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0) return ATTN_ERR_SHAPE;
+  if (d != 64 && d != 128) return ATTN_ERR_UNSUPPORTED;
+  // Workgroups (sequences x heads x query tiles) must fit in 31 bits; row offsets are
+  // computed in 64 bits, per-tile offsets in 32.
+  const int64_t tiles = ((int64_t)max_seqlen + 127) / 128;
+  if ((int64_t)nseq * Hq * tiles >= (int64_t)1 << 31) return ATTN_ERR_SHAPE;
+  if ((int64_t)Hq * d * 64 * 2 >= (int64_t)1 << 31) return ATTN_ERR_SHAPE;
+  const attn_options o_ = opt ? *opt : attn_default_options();
+  int st = check_options(o_);
+  if (st != ATTN_OK) return st;
+  if (!std::isfinite(scale)) return ATTN_ERR_VALUE;
+  if (nseq == 0 || total == 0 || max_seqlen == 0) return ATTN_OK;
+  if (!q || !k || !v || !o || !lse || !cu_seqlens) return ATTN_ERR_NULL;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse) ||
+      (reinterpret_cast<uintptr_t>(cu_seqlens) & 3u) != 0)
+    return ATTN_ERR_ALIGN;
+
+  attn::FwdArgs a;
+  a.q = static_cast<const uint16_t*>(q);
+  a.k = static_cast<const uint16_t*>(k);
+  a.v = static_cast<const uint16_t*>(v);
+  a.o = static_cast<uint16_t*>(o);
+  a.lse = lse;
+  a.B = nseq; a.Hq = Hq; a.Hkv = Hkv; a.S = max_seqlen;
+  scale_setup(scale, &a.c, &a.q_and, &a.q_xor);
+  a.tau = o_.tau;
+  a.cu_seqlens = cu_seqlens;
+  a.total = total;
+  (void)hipGetLastError();
+  return hip_status(attn::launch_fwd_varlen(a, d, causal != 0, o_.exp_mode, static_cast<hipStream_t>(stream)));
 }
 
 size_t attn_bwd_workspace_bytes(int B, int Hq, int Hkv, int S, int d) {

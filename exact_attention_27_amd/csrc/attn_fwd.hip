@@ -54,7 +54,9 @@ constexpr int kFwdBM = 32 * kFwdWaves;    // queries per workgroup
 #define FWD_PD 2                          // slots between an LDS read and its product
 #endif
 
-template <int D, bool CAUSAL, int EXPMODE>
+// VARLEN: a packed batch of sequences of different lengths (FwdArgs::cu_seqlens), with
+// token-major rows (row stride H*d instead of d); otherwise the dense [B, H, S, d] layout.
+template <int D, bool CAUSAL, int EXPMODE, bool VARLEN>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(2, 2)))
 void fwd_kernel(FwdArgs a) {
   constexpr int BN = kFwdBN;
@@ -90,12 +92,32 @@ void fwd_kernel(FwdArgs a) {
   const int b = bh / a.Hq;
   const int hq = bh - b * a.Hq;
   const int hkv = hq / (a.Hq / a.Hkv);
-  const int S = a.S;
   const int q0 = qt * BM;
+  // Rows of this (batch or sequence, head): S of them, D elements each, rs_q / rs_kv
+  // elements apart; LSE of query i at lse[lse0 + i].
+  int S, Sq;  // keys (the sequence's length) and the queries this launch writes
+  size_t qbase, kvbase, lse0;
+  constexpr int RS_DENSE = D;
+  int rs_q = RS_DENSE, rs_kv = RS_DENSE;
+  if constexpr (VARLEN) {
+    const int start = min(max(a.cu_seqlens[b], 0), a.total);
+    const int end = min(max(a.cu_seqlens[b + 1], start), a.total);
+    S = end - start;
+    Sq = min(S, a.S);     // queries past max_seqlen (a.S) are not written
+    if (q0 >= Sq) return;  // the whole workgroup: this tile lies past its sequence
+    rs_q = a.Hq * D;
+    rs_kv = a.Hkv * D;
+    qbase = (size_t)start * rs_q + (size_t)hq * D;
+    kvbase = (size_t)start * rs_kv + (size_t)hkv * D;
+    lse0 = (size_t)hq * a.total + start;
+  } else {
+    S = Sq = a.S;
+    qbase = ((size_t)b * a.Hq + hq) * (size_t)S * D;
+    kvbase = ((size_t)b * a.Hkv + hkv) * (size_t)S * D;
+    lse0 = ((size_t)b * a.Hq + hq) * S;
+  }
   const int qw = q0 + wave * 32;  // first query of this wave
   const int qi = qw + col;        // this lane's query
-  const size_t qbase = ((size_t)b * a.Hq + hq) * (size_t)S * D;
-  const size_t kvbase = ((size_t)b * a.Hkv + hkv) * (size_t)S * D;
   const uint16_t* __restrict__ Kg = a.k + kvbase;
   const uint16_t* __restrict__ Vg = a.v + kvbase;
 
@@ -104,7 +126,7 @@ void fwd_kernel(FwdArgs a) {
   // branch, so all the loads are in flight together.
   bf16x8 qf[KSTEPS];
   {
-    const u32x4* qrow = (const u32x4*)(a.q + qbase + (size_t)min(qi, S - 1) * D + half * 8);
+    const u32x4* qrow = (const u32x4*)(a.q + qbase + (size_t)min(qi, S - 1) * rs_q + half * 8);
 #pragma unroll
     for (int ks = 0; ks < KSTEPS; ++ks) qf[ks] = __builtin_bit_cast(bf16x8, (qrow[ks * 2] & a.q_and) ^ a.q_xor);
   }
@@ -121,7 +143,7 @@ void fwd_kernel(FwdArgs a) {
   // the sequence, clamps its rows to a real row (their scores are masked, so any finite
   // data will do).
   constexpr int CG = D / 32;    // 4-chunk groups per row
-  constexpr int ROWB = D * 2;   // bytes per K/V row in memory
+  const int ROWB = rs_kv * 2;   // bytes between K/V rows in memory (2 D when dense)
   static_assert(4 % CG == 0 && BN * CG == 64 * DMAS, "DMA block assignment");
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
   const int w_rg = wave_u / CG, w_cg = wave_u % CG;  // block (w_rg, w_cg) for i = 0
@@ -130,7 +152,7 @@ void fwd_kernel(FwdArgs a) {
   const uint32_t k_goff = (uint32_t)((w_rg * 16 + k_lr) * ROWB + (w_cg * 4 + k_lc) * 16);
   const uint32_t v_goff = (uint32_t)((w_rg * 16 + v_lr) * ROWB + (w_cg * 4 + v_lc) * 16);
   auto dma_tile = [&](const uint16_t* __restrict__ src, int j, uint16_t* slot, int lr, int lc, uint32_t goff) {
-    const char* base = (const char*)(src + (size_t)j * BN * D);
+    const char* base = (const char*)(src + (size_t)j * BN * rs_kv);
     if (j * BN + BN <= S) {
 #pragma unroll
       for (int i = 0; i < DMAS; ++i)
@@ -308,8 +330,8 @@ void fwd_kernel(FwdArgs a) {
   // Epilogue: O = O_acc / l (bf16, round to nearest even) and LSE in natural log.
   const float l = sum_halves(l_run);
   const float inv = 1.0f / l;
-  if (qi < S) {
-    uint16_t* orow = a.o + qbase + (size_t)qi * D;
+  if (qi < Sq) {
+    uint16_t* orow = a.o + qbase + (size_t)qi * rs_q;
 #pragma unroll
     for (int db = 0; db < DBLK; ++db) {
 #pragma unroll
@@ -320,24 +342,24 @@ void fwd_kernel(FwdArgs a) {
         *(u32x2*)(orow + db * 32 + g * 8 + half * 4) = w;
       }
     }
-    if (half == 0) a.lse[((size_t)b * a.Hq + hq) * S + qi] = (m_ref + log2f(l)) * kLn2;
+    if (half == 0) a.lse[lse0 + qi] = (m_ref + log2f(l)) * kLn2;
   }
 }
 
-template <int D, bool CAUSAL, int EXPMODE>
+template <int D, bool CAUSAL, int EXPMODE, bool VARLEN>
 hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t stream) {
   const int nqt = (a.S + kFwdBM - 1) / kFwdBM;
   const dim3 grid((unsigned)(nqt * a.B * a.Hq));
-  hipLaunchKernelGGL((fwd_kernel<D, CAUSAL, EXPMODE>), grid, dim3(256), 0, stream, a);
+  hipLaunchKernelGGL((fwd_kernel<D, CAUSAL, EXPMODE, VARLEN>), grid, dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 
-template <int D>
+template <int D, bool VARLEN>
 hipError_t launch_fwd_d(const FwdArgs& a, bool causal, int exp_mode, hipStream_t stream) {
   if (causal) {
-    return exp_mode == 0 ? launch_fwd_t<D, true, 0>(a, stream) : launch_fwd_t<D, true, 1>(a, stream);
+    return exp_mode == 0 ? launch_fwd_t<D, true, 0, VARLEN>(a, stream) : launch_fwd_t<D, true, 1, VARLEN>(a, stream);
   }
-  return exp_mode == 0 ? launch_fwd_t<D, false, 0>(a, stream) : launch_fwd_t<D, false, 1>(a, stream);
+  return exp_mode == 0 ? launch_fwd_t<D, false, 0, VARLEN>(a, stream) : launch_fwd_t<D, false, 1, VARLEN>(a, stream);
 }
 
 __global__ void exp2_eval_kernel(const float* x, float* y, long n, int mode) {
@@ -348,7 +370,13 @@ __global__ void exp2_eval_kernel(const float* x, float* y, long n, int mode) {
 }  // namespace
 
 hipError_t launch_fwd(const FwdArgs& a, int d, bool causal, int exp_mode, hipStream_t stream) {
-  return d == 64 ? launch_fwd_d<64>(a, causal, exp_mode, stream) : launch_fwd_d<128>(a, causal, exp_mode, stream);
+  return d == 64 ? launch_fwd_d<64, false>(a, causal, exp_mode, stream)
+                 : launch_fwd_d<128, false>(a, causal, exp_mode, stream);
+}
+
+hipError_t launch_fwd_varlen(const FwdArgs& a, int d, bool causal, int exp_mode, hipStream_t stream) {
+  return d == 64 ? launch_fwd_d<64, true>(a, causal, exp_mode, stream)
+                 : launch_fwd_d<128, true>(a, causal, exp_mode, stream);
 }
 
 hipError_t launch_exp2_eval(const float* x, float* y, long n, int exp_mode, hipStream_t stream) {

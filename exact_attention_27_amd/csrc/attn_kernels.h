@@ -21,6 +21,12 @@ struct FwdArgs {
   float c;
   uint32_t q_and, q_xor;
   float tau;
+  // Variable-length (packed) batches; nullptr for the dense [B, H, S, d] layout.  With
+  // cu_seqlens set, B is the number of sequences, S the longest sequence (grid size),
+  // q/o are [total, Hq, d], k/v [total, Hkv, d] and lse [Hq, total]; sequence b is the
+  // rows cu_seqlens[b] .. cu_seqlens[b + 1] - 1 (clamped to [0, total]).
+  const int* cu_seqlens;
+  int total;
 };
 
 struct BwdArgs {
@@ -42,6 +48,8 @@ struct BwdArgs {
 };
 
 hipError_t launch_fwd(const FwdArgs& a, int d, bool causal, int exp_mode, hipStream_t stream);
+// The same forward over a variable-length packed batch (a.cu_seqlens != nullptr).
+hipError_t launch_fwd_varlen(const FwdArgs& a, int d, bool causal, int exp_mode, hipStream_t stream);
 // phases: bit 0 = preprocess (D, LSE log2 e), bit 1 = dK/dV kernel, bit 2 = dQ kernel.
 // 7 runs the whole backward.
 hipError_t launch_bwd(const BwdArgs& a, int d, bool causal, int exp_mode, int phases, hipStream_t stream);

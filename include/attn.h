@@ -107,6 +107,32 @@ int attn_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse
                 const attn_options* opt, void* stream);
 
 /*
+ * Forward pass over a variable-length (packed) batch: nseq sequences of different
+ * lengths laid end to end, as a prefill server batches prompts (the pages' integration
+ * target: prefill in SGLang and vLLM, hyper.ai FlashAttention-4 story).  Attention is
+ * taken within each sequence only (causal: key j visible to query i of the same sequence
+ * iff j <= i).  Layout, token-major:
+ *     q, o : [total, Hq,  d] bf16     k, v : [total, Hkv, d] bf16
+ *     lse  : [Hq, total]     fp32 (natural log, as in attn_fwd)
+ *     cu_seqlens : [nseq + 1] int32 DEVICE array, 0 <= cu_seqlens[0] <= ... <=
+ *                  cu_seqlens[nseq] <= total; sequence b is rows cu_seqlens[b] ..
+ *                  cu_seqlens[b + 1] - 1.
+ * max_seqlen should be >= every sequence's length: it sizes the launch.  Query rows at
+ * positions >= max_seqlen within their sequence are not written; the rows that are
+ * written still attend over their whole sequence's keys (all of them when non-causal).
+ * The library does not read cu_seqlens on the host (it is device memory and the call is
+ * asynchronous); offsets outside [0, total] are clamped (and a decreasing offset gives
+ * an empty sequence), so no access leaves the tensors.  Rows not covered by any sequence
+ * are left unwritten.  nseq == 0, total == 0 or max_seqlen == 0 is an empty problem
+ * (ATTN_OK, nothing launched).  Other conventions as above; opt == NULL means the
+ * defaults.
+ */
+int attn_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
+                    const int* cu_seqlens, int nseq, int total, int max_seqlen,
+                    int Hq, int Hkv, int d, float scale, int causal,
+                    const attn_options* opt, void* stream);
+
+/*
  * Bytes of device workspace attn_bwd needs for these sizes: two fp32 row arrays
  * [B*Hq][S_pad] (the row terms D_i = <dO_i, O_i> and LSE_i log2(e), S_pad = S rounded
  * up to a multiple of 64), each rounded up to 256 bytes.  Returns 0 for invalid or

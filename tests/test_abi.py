@@ -140,3 +140,39 @@ def test_bwd_phase_rejects_unknown_phase():
     p = list(args)
     p[0] = None
     assert lib.attn_bwd_phase(2, *p, None, None) == NULL
+
+
+def fwd_varlen(q=A, k=A, v=A, o=A, lse=A, cu=ctypes.c_void_p(0x30000), nseq=2, total=16, max_seqlen=8, Hq=2, Hkv=1,
+               d=64, scale=0.125, causal=0, opt=None):
+    lib = ea.lib()
+    return lib.attn_fwd_varlen(q, k, v, o, lse, cu, nseq, total, max_seqlen, Hq, Hkv, d, scale, causal,
+                               None if opt is None else ctypes.byref(opt), None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), NULL), (dict(k=None), NULL), (dict(v=None), NULL), (dict(o=None), NULL), (dict(lse=None), NULL),
+    (dict(cu=None), NULL),
+    (dict(nseq=-1), SHAPE), (dict(total=-1), SHAPE), (dict(max_seqlen=-1), SHAPE), (dict(Hq=3, Hkv=2), SHAPE),
+    (dict(Hkv=0), SHAPE), (dict(nseq=1 << 30, max_seqlen=1 << 30, Hq=64, Hkv=64), SHAPE),
+    (dict(d=96), UNSUP), (dict(opt=ea.attn_options(4, 8.0, 0)), UNSUP),
+    (dict(v=ctypes.c_void_p(0x10008)), ALIGN), (dict(cu=ctypes.c_void_p(0x30002)), ALIGN),
+    (dict(scale=float("nan")), VALUE), (dict(opt=ea.attn_options(0, -2.0, 0)), VALUE),
+])
+def test_fwd_varlen_rejects(kw, status):
+    assert fwd_varlen(**kw) == status
+
+
+@pytest.mark.parametrize("kw", [dict(nseq=0), dict(total=0), dict(max_seqlen=0),
+                                dict(nseq=0, q=None, k=None, v=None, o=None, lse=None, cu=None)])
+def test_fwd_varlen_empty_is_ok_without_launch(kw):
+    assert fwd_varlen(**kw) == OK
+
+
+def test_fwd_varlen_binding_checks_arguments():
+    import torch
+    q = torch.zeros(10, 2, 64, dtype=torch.bfloat16)
+    k = torch.zeros(10, 1, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        ea.attn_fwd_varlen(q, k, k, torch.tensor([0, 10], dtype=torch.int64), 10)
+    with pytest.raises(ValueError):
+        ea.attn_fwd_varlen(q, k, k[:9], torch.tensor([0, 10], dtype=torch.int32), 10)

@@ -74,6 +74,73 @@ WORKLOADS: Dict[int, Workload] = {
 }
 
 
+@dataclasses.dataclass(frozen=True)
+class VarlenWorkload:
+    """A packed (variable-length) forward batch: ``n`` sequences whose lengths are drawn
+    log-uniformly in [min_len, max_len] from the workload's seed, laid end to end."""
+    number: int
+    name: str
+    n: int
+    min_len: int
+    max_len: int
+    Hq: int
+    Hkv: int
+    d: int
+    causal: bool
+    passes: Tuple[str, ...] = ("fwd",)
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / math.sqrt(self.d)
+
+    @property
+    def group(self) -> int:
+        return self.Hq // self.Hkv
+
+    def lengths(self):
+        g = torch.Generator("cpu").manual_seed(self.number)
+        u = torch.empty(self.n, dtype=torch.float64).uniform_(math.log(self.min_len), math.log(self.max_len + 1), generator=g)
+        return [min(self.max_len, max(self.min_len, int(x))) for x in torch.exp(u).floor().tolist()]
+
+    def fwd_flop(self) -> float:
+        """Algorithmic forward flop: sum over sequences of 4*Hq*len^2*d, halved when causal."""
+        f = sum(4.0 * self.Hq * n * n * self.d for n in self.lengths())
+        return f / 2 if self.causal else f
+
+    def describe(self) -> str:
+        ls = self.lengths()
+        return (f"{self.n} sequences, lengths {min(ls)}..{max(ls)} (total {sum(ls)} tokens), Hq={self.Hq} "
+                f"Hkv={self.Hkv} d={self.d} {'causal' if self.causal else 'non-causal'}")
+
+
+VARLEN_WORKLOADS: Dict[int, VarlenWorkload] = {
+    # A prefill batch of prompts of mixed lengths (the pages' integration target: prefill
+    # in SGLang/vLLM).
+    9: VarlenWorkload(9, "varlen_prefill_fwd", 32, 256, 8192, 32, 8, 128, True),
+}
+
+
+def make_varlen_tensors(lengths, Hq: int, Hkv: int, d: int, seed: int) -> Dict[str, torch.Tensor]:
+    """Seeded packed bf16 CPU tensors: q [T,Hq,d], k, v [T,Hkv,d] (T = sum of lengths), drawn
+    in that order as fp32 N(0,1) after ``seed`` and rounded to bf16, and the int32 offsets
+    cu_seqlens [n+1]."""
+    g = torch.Generator("cpu").manual_seed(seed)
+    T = int(sum(lengths))
+    q = torch.randn((T, Hq, d), generator=g, dtype=torch.float32)
+    k = torch.randn((T, Hkv, d), generator=g, dtype=torch.float32)
+    v = torch.randn((T, Hkv, d), generator=g, dtype=torch.float32)
+    cu = torch.zeros(len(lengths) + 1, dtype=torch.int32)
+    if lengths:
+        cu[1:] = torch.cumsum(torch.tensor(lengths, dtype=torch.int64), 0).to(torch.int32)
+    return {"q": q.to(torch.bfloat16), "k": k.to(torch.bfloat16), "v": v.to(torch.bfloat16), "cu_seqlens": cu}
+
+
+def make_varlen_inputs(w: VarlenWorkload, seed: int | None = None) -> Dict[str, torch.Tensor]:
+    """Inputs of the packed workload ``w`` (seed defaults to its number + 100, so that the
+    tensor draws do not repeat the draws of its lengths)."""
+    return make_varlen_tensors(w.lengths(), w.Hq, w.Hkv, w.d, w.number + 100 if seed is None else seed)
+
+
 def make_tensors(B: int, Hq: int, Hkv: int, S: int, d: int, seed: int,
                  outlier_frac: float = 0.0, with_do: bool = True) -> Dict[str, torch.Tensor]:
     """Seeded bf16 CPU tensors q, k, v (and do) following the recipe above."""
