@@ -55,6 +55,7 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target oracle sample time")
     ap.add_argument("--exp-mode", type=int, default=None)
     ap.add_argument("--tau", type=float, default=None)
+    ap.add_argument("--variant", type=int, default=None, help="forward schedule: 0 default, 1 ping-pong")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="instead of the benchmark, run a plain device copy of MIB MiB (3 times): the "
                          "reference kernel that scales rocprofv3 FETCH_SIZE/WRITE_SIZE into bytes")
@@ -185,6 +186,8 @@ def main_varlen(args, w):
         opt.exp_mode = args.exp_mode
     if args.tau is not None:
         opt.tau = args.tau
+    if args.variant is not None:
+        opt.variant = args.variant
     o = torch.empty_like(t["q"])
     lse = torch.empty((w.Hq, total), dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream()
@@ -222,7 +225,8 @@ def main_varlen(args, w):
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": w.name, "sequences": w.n, "lengths": f"{min(lens)}..{max(lens)} log-uniform",
                    "total_tokens": total, "Hq": w.Hq, "Hkv": w.Hkv, "d": w.d, "causal": w.causal,
-                   "passes": "fwd", "exp_mode": int(opt.exp_mode), "tau": float(opt.tau), "step_flop": flop},
+                   "passes": "fwd", "exp_mode": int(opt.exp_mode), "tau": float(opt.tau),
+                   "variant": int(opt.variant), "step_flop": flop},
         "frac_of_peak": round(value / PEAK_BF16_TFLOPS, 4),
         "roofline": roofline, "breakdown": {"fwd_ms": round(fwd_ms, 4), "fwd_tflops": round(fwd_tf, 2)},
         "cpu_baseline": cpu,
@@ -258,6 +262,8 @@ def main():
         opt.exp_mode = args.exp_mode
     if args.tau is not None:
         opt.tau = args.tau
+    if args.variant is not None:
+        opt.variant = args.variant
     o = torch.empty_like(q)
     lse = torch.empty((w.B, w.Hq, w.S), dtype=torch.float32, device=dev)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
@@ -334,7 +340,7 @@ def main():
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "S": w.S, "d": w.d,
                    "causal": w.causal, "passes": "+".join(w.passes), "exp_mode": int(opt.exp_mode),
-                   "tau": float(opt.tau), "step_flop": flop},
+                   "tau": float(opt.tau), "variant": int(opt.variant), "step_flop": flop},
         "frac_of_peak": round(value / PEAK_BF16_TFLOPS, 4),
         "roofline": roofline, "breakdown": breakdown, "cpu_baseline": cpu,
     }

@@ -22,11 +22,13 @@ __all__ = [
     "AttnError", "attn_options", "library_path", "lib",
     "attn_fwd", "attn_fwd_ex", "attn_fwd_varlen", "attn_bwd", "attn_bwd_ex", "attn_bwd_phase", "attn_bwd_workspace_bytes",
     "attn_default_options", "attn_status_string", "attn_exp2_eval", "attn_exp2_poly_host",
-    "ATTN_EXP_HW", "ATTN_EXP_POLY3",
+    "ATTN_EXP_HW", "ATTN_EXP_POLY3", "ATTN_VARIANT_DEFAULT", "ATTN_VARIANT_PINGPONG",
 ]
 
 ATTN_EXP_HW = 0
 ATTN_EXP_POLY3 = 1
+ATTN_VARIANT_DEFAULT = 0
+ATTN_VARIANT_PINGPONG = 1
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 
@@ -130,14 +132,16 @@ def _need(t: torch.Tensor, name: str, dtype: torch.dtype, shape) -> None:
         raise ValueError(f"{name} must be contiguous")
 
 
-def _options(opt, exp_mode, tau):
-    if opt is None and exp_mode is None and tau is None:
+def _options(opt, exp_mode, tau, variant=None):
+    if opt is None and exp_mode is None and tau is None and variant is None:
         return None
     o = attn_default_options() if opt is None else attn_options(opt.exp_mode, opt.tau, opt.variant)
     if exp_mode is not None:
         o.exp_mode = int(exp_mode)
     if tau is not None:
         o.tau = float(tau)
+    if variant is not None:
+        o.variant = int(variant)
     return o
 
 
@@ -152,8 +156,10 @@ def _dims(q: torch.Tensor, k: torch.Tensor):
 def attn_fwd_ex(q, k, v, scale: Optional[float] = None, causal: bool = False,
                 o: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
                 opt: Optional[attn_options] = None, exp_mode: Optional[int] = None,
-                tau: Optional[float] = None, stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
-    """Forward pass; returns (o [B,Hq,S,d] bf16, lse [B,Hq,S] fp32).  scale defaults to 1/sqrt(d)."""
+                tau: Optional[float] = None, stream=None, variant: Optional[int] = None
+                ) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Forward pass; returns (o [B,Hq,S,d] bf16, lse [B,Hq,S] fp32).  scale defaults to 1/sqrt(d).
+    variant: ATTN_VARIANT_DEFAULT or ATTN_VARIANT_PINGPONG (the forward schedule)."""
     B, Hq, Hkv, S, d = _dims(q, k)
     _need(q, "q", torch.bfloat16, (B, Hq, S, d))
     _need(k, "k", torch.bfloat16, (B, Hkv, S, d))
@@ -165,7 +171,7 @@ def attn_fwd_ex(q, k, v, scale: Optional[float] = None, causal: bool = False,
     _need(o, "o", torch.bfloat16, (B, Hq, S, d))
     _need(lse, "lse", torch.float32, (B, Hq, S))
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
-    op = _options(opt, exp_mode, tau)
+    op = _options(opt, exp_mode, tau, variant)
     with torch.cuda.device(q.device):
         st = lib().attn_fwd_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, Hq, Hkv, S, d,
                                scale, int(bool(causal)), None if op is None else ctypes.byref(op),
@@ -177,7 +183,8 @@ def attn_fwd_ex(q, k, v, scale: Optional[float] = None, causal: bool = False,
 def attn_fwd_varlen(q, k, v, cu_seqlens, max_seqlen: int, scale: Optional[float] = None, causal: bool = False,
                     o: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
                     opt: Optional[attn_options] = None, exp_mode: Optional[int] = None,
-                    tau: Optional[float] = None, stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
+                    tau: Optional[float] = None, stream=None, variant: Optional[int] = None
+                    ) -> Tuple[torch.Tensor, torch.Tensor]:
     """Forward pass over a packed batch of sequences of different lengths.
 
     q: [total, Hq, d], k and v: [total, Hkv, d] bf16; cu_seqlens: [nseq + 1] int32 device
@@ -203,7 +210,7 @@ def attn_fwd_varlen(q, k, v, cu_seqlens, max_seqlen: int, scale: Optional[float]
     _need(o, "o", torch.bfloat16, (total, Hq, d))
     _need(lse, "lse", torch.float32, (Hq, total))
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
-    op = _options(opt, exp_mode, tau)
+    op = _options(opt, exp_mode, tau, variant)
     with torch.cuda.device(q.device):
         st = lib().attn_fwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(cu_seqlens),
                                    max(nseq, 0), total, int(max_seqlen), Hq, Hkv, d, scale, int(bool(causal)),

@@ -34,7 +34,7 @@ int check_sizes(int B, int Hq, int Hkv, int S, int d, bool* empty) {
 
 int check_options(const attn_options& o) {
   if (o.exp_mode != ATTN_EXP_HW && o.exp_mode != ATTN_EXP_POLY3) return ATTN_ERR_UNSUPPORTED;
-  if (o.variant != 0) return ATTN_ERR_UNSUPPORTED;
+  if (o.variant != 0 && o.variant != 1) return ATTN_ERR_UNSUPPORTED;
   if (!std::isfinite(o.tau) || o.tau < 0.0f || o.tau > 30.0f) return ATTN_ERR_VALUE;
   return ATTN_OK;
 }
@@ -106,7 +106,7 @@ int attn_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse
   a.cu_seqlens = nullptr;
   a.total = 0;
   (void)hipGetLastError();  // a stale error from earlier work is not this call's failure
-  return hip_status(attn::launch_fwd(a, d, causal != 0, o_.exp_mode, static_cast<hipStream_t>(stream)));
+  return hip_status(attn::launch_fwd(a, d, causal != 0, o_.exp_mode, o_.variant, static_cast<hipStream_t>(stream)));
 }
 
 int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
@@ -147,7 +147,7 @@ int attn_fwd_varlen(const void* q, const void* k, const void* v, void* o, float*
   a.cu_seqlens = cu_seqlens;
   a.total = total;
   (void)hipGetLastError();
-  return hip_status(attn::launch_fwd_varlen(a, d, causal != 0, o_.exp_mode, static_cast<hipStream_t>(stream)));
+  return hip_status(attn::launch_fwd_varlen(a, d, causal != 0, o_.exp_mode, o_.variant, static_cast<hipStream_t>(stream)));
 }
 
 size_t attn_bwd_workspace_bytes(int B, int Hq, int Hkv, int S, int d) {

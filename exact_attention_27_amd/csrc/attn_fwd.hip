@@ -47,26 +47,28 @@
 namespace attn {
 namespace {
 
-constexpr int kFwdWaves = 4;
 constexpr int kFwdBN = 64;                // keys per LDS tile
-constexpr int kFwdBM = 32 * kFwdWaves;    // queries per workgroup
 #ifndef FWD_PD
 #define FWD_PD 2                          // slots between an LDS read and its product
 #endif
 
 // VARLEN: a packed batch of sequences of different lengths (FwdArgs::cu_seqlens), with
 // token-major rows (row stride H*d instead of d); otherwise the dense [B, H, S, d] layout.
-template <int D, bool CAUSAL, int EXPMODE, bool VARLEN>
-__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(2, 2)))
+// W: waves per workgroup.  W = 4: every wave meets the barrier after phase 2, and two
+// workgroups share a CU.  W = 8: the staggered two-group schedule described below, one
+// workgroup per CU.
+template <int D, bool CAUSAL, int EXPMODE, bool VARLEN, int W>
+__global__ __attribute__((amdgpu_flat_work_group_size(64 * W, 64 * W), amdgpu_waves_per_eu(2, 2)))
 void fwd_kernel(FwdArgs a) {
+  static_assert(W == 4 || W == 8, "4 or 8 waves per workgroup");
   constexpr int BN = kFwdBN;
-  constexpr int BM = kFwdBM;
+  constexpr int BM = 32 * W;            // queries per workgroup
   constexpr int KB = BN / 32;           // 32-key blocks per tile
   constexpr int KSTEPS = D / 16;        // MFMA k-steps of S^T = K Q^T
   constexpr int DBLK = D / 32;          // 32-row blocks of O^T
   constexpr int CPR = D / 8;            // 16-byte chunks per row
   constexpr int TILE = BN * D;          // bf16 elements of one K or V tile
-  constexpr int DMAS = BN * CPR / 256;  // 16-byte chunks per thread per tile
+  constexpr int DMAS = BN * CPR / (64 * W);  // 16-byte chunks per thread per tile
   constexpr int NQK = KSTEPS * KB;      // phase-1 slots (products of S_{j+1})
   constexpr int NPV = 2 * KB * DBLK;    // phase-2 slots (products of O^T)
   constexpr int NE = KB * 16;           // scores per lane per tile
@@ -74,9 +76,10 @@ void fwd_kernel(FwdArgs a) {
   constexpr int MAX0 = NPV / 4;         // first phase-2 slot that takes part of the maximum
   constexpr int PD = FWD_PD;
   static_assert(NE % NQK == 0 && EPS % 2 == 0, "exponentials must pair up per slot");
-  static_assert(BN % 32 == 0 && DMAS * 256 == BN * CPR, "tile must split evenly over 256 threads");
-  // K ring (2 tiles) then V ring (2 tiles), each tile [BN][D] in 1024-byte blocks.
-  __shared__ __attribute__((aligned(1024))) uint16_t smem[4 * TILE];
+  static_assert(BN % 32 == 0 && DMAS * 64 * W == BN * CPR, "tile must split evenly over the threads");
+  constexpr int VR = W == 8 ? 3 : 2;    // V ring slots (the K ring has 2)
+  // K ring then V ring, each tile [BN][D] in 1024-byte blocks.
+  __shared__ __attribute__((aligned(1024))) uint16_t smem[(2 + VR) * TILE];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -136,7 +139,7 @@ void fwd_kernel(FwdArgs a) {
 
   // LDS tiles use the blocked layouts of attn_device.h: K chunk-inner with XOR (read as
   // MFMA A operands, 16 rows at one chunk), V chunk-inner (read by transpose reads).  A
-  // tile is (BN / 16) x (D / 32) blocks of 1024 bytes; wave w DMAs blocks 4 i + w,
+  // tile is (BN / 16) x (D / 32) blocks of 1024 bytes; wave w of W DMAs blocks W i + w,
   // i < DMAS.  Lane l fetches row l / 4 of the block, chunk l % 4 (K: XOR (l / 16) % 4),
   // so every 4 lanes read one aligned 64-byte piece of a row.  The per-lane global byte offsets are
   // fixed and the tile base is a scalar; only the last tile, if it runs past the end of
@@ -144,7 +147,7 @@ void fwd_kernel(FwdArgs a) {
   // data will do).
   constexpr int CG = D / 32;    // 4-chunk groups per row
   const int ROWB = rs_kv * 2;   // bytes between K/V rows in memory (2 D when dense)
-  static_assert(4 % CG == 0 && BN * CG == 64 * DMAS, "DMA block assignment");
+  static_assert(W % CG == 0 && (BN / 16) * CG == W * DMAS, "DMA block assignment");
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
   const int w_rg = wave_u / CG, w_cg = wave_u % CG;  // block (w_rg, w_cg) for i = 0
   const int k_lr = lane >> 2, k_lc = (lane & 3) ^ ((lane >> 4) & 3);
@@ -156,14 +159,14 @@ void fwd_kernel(FwdArgs a) {
     if (j * BN + BN <= S) {
 #pragma unroll
       for (int i = 0; i < DMAS; ++i)
-        dma16_s(base + i * (4 / CG) * 16 * ROWB, goff, slot + (i * 4 + wave_u) * 512);
+        dma16_s(base + i * (W / CG) * 16 * ROWB, goff, slot + (i * W + wave_u) * 512);
     } else {
       __asm__ volatile("" : "+v"(lr));  // keep this rare path's row arithmetic inside it
 #pragma unroll
       for (int i = 0; i < DMAS; ++i) {
-        const int r = (i * (4 / CG) + w_rg) * 16 + lr;  // row within the tile
+        const int r = (i * (W / CG) + w_rg) * 16 + lr;  // row within the tile
         const int rc = min(j * BN + r, S - 1) - j * BN;
-        dma16_s(base, (uint32_t)(rc * ROWB + (w_cg * 4 + lc) * 16), slot + (i * 4 + wave_u) * 512);
+        dma16_s(base, (uint32_t)(rc * ROWB + (w_cg * 4 + lc) * 16), slot + (i * W + wave_u) * 512);
       }
     }
   };
@@ -216,10 +219,23 @@ void fwd_kernel(FwdArgs a) {
     return max_halves(mx) * c;
   };
 
-  // Prologue: K_0, V_0, K_1 in flight; S_0 computed.
+  // Ring discipline.  Every wave issues its share of the next tiles right after a
+  // barrier and waits for that share before its next barrier, so a tile issued after
+  // barrier m is complete for everyone after barrier m+1.  After barrier m the tiles
+  // K_{m+2} (into K_m's slot) and V_{m+1} (into slot (m+1) % VR) are issued.
+  //
+  // W = 8 (two-wave-group ping-pong): the halves of the workgroup run the same steps
+  // half a step apart, so the two waves sharing a SIMD (waves w and w+4) are in
+  // complementary phases.  Group 0 meets each barrier after phase 2 of a step, group 1
+  // after phase 1.  Between two barriers group 0 runs phases 1 and 2 of step s while
+  // group 1 runs phase 2 of step s-1 and phase 1 of step s: the tiles read are K_{s+1},
+  // V_s and V_{s-1} while K_{s+2} and V_{s+1} land, hence 3 V slots.
+  const int grp = W == 8 ? (wave_u >= W / 2) : 0;
+  // Prologue: K_0, K_1, V_0 resident; S_0 computed; a second barrier frees K_0's slot;
+  // then K_2 and V_1 in flight.
   dma_k(0, Kring);
-  dma_v(0, Vring);
   if (nkv > 1) dma_k(1, Kring + TILE);
+  dma_v(0, Vring);
   wait_dma();
   __syncthreads();
   f32x16 sc[KB];
@@ -232,17 +248,31 @@ void fwd_kernel(FwdArgs a) {
       sc[kb] = mfma32(*(const bf16x8*)((const char*)Kring + k_off(kb, ks)), qf[ks], sc[kb]);
   if (needs_mask(0)) mask(sc, 0);
   float mt = tile_max(sc);  // scaled maximum of the score tile the next step exponentiates
+  __syncthreads();  // every wave has read K_0
+  if (nkv > 2) dma_k(2, Kring);
+  if (nkv > 1) dma_v(1, Vring + TILE);
+  int r_cur = 0;  // V ring slot of V_s, s % VR
 
   // One key tile: S_j (in cur) -> O; S_{j+1} (into nxt).  P is the ring parity of j;
   // the loop below is unrolled by two so that every LDS slot offset is a constant and
   // the score registers swap roles instead of being copied.
   auto step = [&](const int j, f32x16 (&cur)[KB], f32x16 (&nxt)[KB], auto parity) {
-    constexpr int P = decltype(parity)::value;
+    constexpr int P = decltype(parity)::value;  // j % 2
+    const int r1 = r_cur == VR - 1 ? 0 : r_cur + 1;                 // V slot of V_{j+1}
+    const int r2 = r1 == VR - 1 ? 0 : r1 + 1;                       // V slot of V_{j+2}
     const char* Ks = (const char*)(Kring + (1 - P) * TILE);          // K_{j+1}
-    const char* Vs = (const char*)(Vring + P * TILE) + v_lds;        // V_j
-    // Free slots: K_j's (read by the previous step's QK) and V_{j-1}'s (read by its PV).
-    if (j + 2 < nkv) dma_k(j + 2, Kring + P * TILE);
-    if (j + 1 < nkv) dma_v(j + 1, Vring + (1 - P) * TILE);
+    const char* Vs = (const char*)(Vring + r_cur * TILE) + v_lds;    // V_j
+    // This step's barrier (j+1): wait for this wave's share of K_{j+2} and V_{j+1}, meet
+    // the other waves, then start K_{j+3} (into K_{j+1}'s slot, read by both groups in
+    // phase 1, before their barrier) and V_{j+2} (into the slot of V_{j-1} for W = 8,
+    // whose last reader, group 1, finished it before the previous barrier; of V_j for
+    // W = 4, read by every wave in phase 2, before this barrier).
+    auto barrier = [&]() {
+      wait_dma();
+      __syncthreads();
+      if (j + 3 < nkv) dma_k(j + 3, Kring + (1 - P) * TILE);
+      if (j + 2 < nkv) dma_v(j + 2, Vring + r2 * TILE);
+    };
 
     // LDS reads of slot i: the K fragment of product i of phase 1, or the two V^T
     // halves of product i - NQK of phase 2.
@@ -279,6 +309,10 @@ void fwd_kernel(FwdArgs a) {
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int i = 0; i < NQK + NPV; ++i) {
+      if (i == NQK) {
+        if (grp != 0) barrier();
+        __builtin_amdgcn_sched_barrier(0);
+      }
       issue(i + PD);
       if (i < NQK) {
         // Phase 1: one product of S_{j+1}; EPS exponentials of S_j.
@@ -311,8 +345,8 @@ void fwd_kernel(FwdArgs a) {
     }
     l_run += lt0 + lt1;
     mt = max_halves(mx) * c;
-    wait_dma();
-    __syncthreads();
+    if (grp == 0) barrier();
+    r_cur = r1;
     // S_{j+1} as computed is exact except on tiles that need a mask (at most the last
     // two of a wave): mask those and take their maximum again.
     if (j + 1 < nkv && needs_mask((j + 1) * BN)) {
@@ -346,20 +380,28 @@ void fwd_kernel(FwdArgs a) {
   }
 }
 
-template <int D, bool CAUSAL, int EXPMODE, bool VARLEN>
+template <int D, bool CAUSAL, int EXPMODE, bool VARLEN, int W>
 hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t stream) {
-  const int nqt = (a.S + kFwdBM - 1) / kFwdBM;
+  const int nqt = (a.S + 32 * W - 1) / (32 * W);
   const dim3 grid((unsigned)(nqt * a.B * a.Hq));
-  hipLaunchKernelGGL((fwd_kernel<D, CAUSAL, EXPMODE, VARLEN>), grid, dim3(256), 0, stream, a);
+  hipLaunchKernelGGL((fwd_kernel<D, CAUSAL, EXPMODE, VARLEN, W>), grid, dim3(64 * W), 0, stream, a);
   return hipGetLastError();
 }
 
-template <int D, bool VARLEN>
-hipError_t launch_fwd_d(const FwdArgs& a, bool causal, int exp_mode, hipStream_t stream) {
+template <int D, bool VARLEN, int W>
+hipError_t launch_fwd_w(const FwdArgs& a, bool causal, int exp_mode, hipStream_t stream) {
   if (causal) {
-    return exp_mode == 0 ? launch_fwd_t<D, true, 0, VARLEN>(a, stream) : launch_fwd_t<D, true, 1, VARLEN>(a, stream);
+    return exp_mode == 0 ? launch_fwd_t<D, true, 0, VARLEN, W>(a, stream)
+                         : launch_fwd_t<D, true, 1, VARLEN, W>(a, stream);
   }
-  return exp_mode == 0 ? launch_fwd_t<D, false, 0, VARLEN>(a, stream) : launch_fwd_t<D, false, 1, VARLEN>(a, stream);
+  return exp_mode == 0 ? launch_fwd_t<D, false, 0, VARLEN, W>(a, stream)
+                       : launch_fwd_t<D, false, 1, VARLEN, W>(a, stream);
+}
+
+template <int D, bool VARLEN>
+hipError_t launch_fwd_d(const FwdArgs& a, bool causal, int exp_mode, int variant, hipStream_t stream) {
+  return variant == 1 ? launch_fwd_w<D, VARLEN, 8>(a, causal, exp_mode, stream)
+                      : launch_fwd_w<D, VARLEN, 4>(a, causal, exp_mode, stream);
 }
 
 __global__ void exp2_eval_kernel(const float* x, float* y, long n, int mode) {
@@ -369,14 +411,14 @@ __global__ void exp2_eval_kernel(const float* x, float* y, long n, int mode) {
 
 }  // namespace
 
-hipError_t launch_fwd(const FwdArgs& a, int d, bool causal, int exp_mode, hipStream_t stream) {
-  return d == 64 ? launch_fwd_d<64, false>(a, causal, exp_mode, stream)
-                 : launch_fwd_d<128, false>(a, causal, exp_mode, stream);
+hipError_t launch_fwd(const FwdArgs& a, int d, bool causal, int exp_mode, int variant, hipStream_t stream) {
+  return d == 64 ? launch_fwd_d<64, false>(a, causal, exp_mode, variant, stream)
+                 : launch_fwd_d<128, false>(a, causal, exp_mode, variant, stream);
 }
 
-hipError_t launch_fwd_varlen(const FwdArgs& a, int d, bool causal, int exp_mode, hipStream_t stream) {
-  return d == 64 ? launch_fwd_d<64, true>(a, causal, exp_mode, stream)
-                 : launch_fwd_d<128, true>(a, causal, exp_mode, stream);
+hipError_t launch_fwd_varlen(const FwdArgs& a, int d, bool causal, int exp_mode, int variant, hipStream_t stream) {
+  return d == 64 ? launch_fwd_d<64, true>(a, causal, exp_mode, variant, stream)
+                 : launch_fwd_d<128, true>(a, causal, exp_mode, variant, stream);
 }
 
 hipError_t launch_exp2_eval(const float* x, float* y, long n, int exp_mode, hipStream_t stream) {

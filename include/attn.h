@@ -72,6 +72,12 @@ enum {
                           summary (section 2.B)                                    */
 };
 
+/* Forward schedules (attn_options.variant). */
+enum {
+    ATTN_VARIANT_DEFAULT = 0, /* 4-wave workgroups, two per CU                      */
+    ATTN_VARIANT_PINGPONG = 1 /* 8-wave workgroups in two half-step-staggered groups */
+};
+
 /*
  * Tuning knobs of the forward and backward kernels.  The plain entry points use
  * the defaults (attn_default_options): the choices that measured fastest.
@@ -82,7 +88,16 @@ enum {
  *              softmax rescaling" of "NVIDIA's FlashAttention-4", section "The
  *              Technical Edge").  The result is the same for every tau; tau only
  *              bounds the unnormalised probabilities by 2^tau.  tau <= 30.
- *   variant  : 0 = default kernel shape; other values are reserved.
+ *   variant  : forward schedule (the backward has one schedule and ignores it).
+ *              ATTN_VARIANT_DEFAULT (0): 4-wave workgroups of 128 queries, two per
+ *              CU, every wave in the same phase order.  ATTN_VARIANT_PINGPONG (1):
+ *              8-wave workgroups of 256 queries, one per CU, whose two 4-wave
+ *              halves run half a step apart, so that of the two waves sharing a
+ *              SIMD one exponentiates while the other runs matrix products (the
+ *              two-team pipelining of the gist.science summary, section 2.A, and
+ *              the overlap of "NVIDIA's FlashAttention-4", section "The Technical
+ *              Edge").  Both give bit-identical results.  Other values:
+ *              ATTN_ERR_UNSUPPORTED.
  */
 typedef struct attn_options {
     int exp_mode;

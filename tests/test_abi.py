@@ -84,7 +84,7 @@ def test_fwd_empty_is_ok_without_launch(kw):
 
 
 @pytest.mark.parametrize("opt,status", [
-    (ea.attn_options(5, 8.0, 0), UNSUP), (ea.attn_options(0, 8.0, 3), UNSUP),
+    (ea.attn_options(5, 8.0, 0), UNSUP), (ea.attn_options(0, 8.0, 3), UNSUP), (ea.attn_options(0, 8.0, 2), UNSUP), (ea.attn_options(0, 8.0, -1), UNSUP),
     (ea.attn_options(0, -1.0, 0), VALUE), (ea.attn_options(0, float("nan"), 0), VALUE), (ea.attn_options(1, 31.0, 0), VALUE),
 ])
 def test_fwd_rejects_options(opt, status):
