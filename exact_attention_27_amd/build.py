@@ -28,12 +28,28 @@ def command(out: str = LIB):
         hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-shared", "-fPIC",
         # Packed-fp32 VALU forms are kept out of every kernel.
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-        # Hardware fp32 atomic add for the dQ accumulator (no compare-and-swap loops).
-        "-munsafe-fp-atomics",
         "-Wno-unused-command-line-argument",
         "-I", os.path.join(ROOT, "include"), "-I", CSRC,
         "-o", out,
     ] + [os.path.join(CSRC, s) for s in SOURCES]
+
+
+PROBE_SRC = os.path.join(CSRC, "probes", "mfma_ceiling.hip")
+PROBE_BIN = os.path.join(PKG, "probes", "mfma_ceiling")
+
+
+def build_probe(verbose: bool = True) -> str:
+    """Compile the stand-alone MFMA ceiling probe (not part of the library) next to the
+    package, as a check that it builds; run it on a GPU to measure the ceiling."""
+    os.makedirs(os.path.dirname(PROBE_BIN), exist_ok=True)
+    cmd = [hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17",
+           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-o", PROBE_BIN, PROBE_SRC]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed ({r.returncode}):\n{r.stderr}")
+    return PROBE_BIN
 
 
 def build(verbose: bool = True) -> str:
@@ -53,3 +69,4 @@ def build(verbose: bool = True) -> str:
 
 if __name__ == "__main__":
     build()
+    build_probe()
