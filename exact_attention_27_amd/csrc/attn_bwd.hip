@@ -442,10 +442,23 @@ void bwd_dq_kernel(BwdArgs a) {
   const int nqt = (S + kDqBM - 1) / kDqBM;
   const int bid = blockIdx.x;
   const int qt = CAUSAL ? (nqt - 1 - bid / nbh) : (bid / nbh);
-  const int bh = bid % nbh;
-  const int b = bh / a.Hq;
-  const int hq = bh - b * a.Hq;
-  const int hkv = hq / (a.Hq / a.Hkv);
+  // Head of this workgroup, as in the forward: with B * Hkv a multiple of 8, every query
+  // head and query tile of one KV group lands on one XCD (XCD = bid % 8) and reads K and
+  // V through one L2.
+  const int G = a.Hq / a.Hkv;
+  const int u = bid % nbh;
+  int kvg, g;
+  if (((a.B * a.Hkv) & 7) == 0) {
+    const int jj = u >> 3;
+    kvg = (jj / G) * 8 + (u & 7);
+    g = jj - (jj / G) * G;
+  } else {
+    kvg = u / G;
+    g = u - kvg * G;
+  }
+  const int b = kvg / a.Hkv;
+  const int hkv = kvg - b * a.Hkv;
+  const int hq = hkv * G + g;
   const int q0 = qt * kDqBM;
   const int qw = q0 + wave * 32;
   const int qi = qw + col;  // this lane's query

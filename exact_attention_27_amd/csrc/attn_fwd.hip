@@ -36,9 +36,9 @@
 //
 // Causal masking: key tiles above the diagonal of the workgroup are never loaded;
 // only tiles that straddle the diagonal or the end of the sequence are masked.
-// Workgroups are dispatched longest-first (largest query tile index first), and all
-// query tiles of one head are spaced B*Hq workgroups apart so that, when B*Hq is a
-// multiple of 8, they run on one XCD and share its L2 for K and V.
+// Workgroups are dispatched longest-first (largest query tile index first), and when the
+// number of KV groups is a multiple of 8 all query heads and query tiles of one KV group
+// run on one XCD and share its L2 for K and V.
 #include <type_traits>
 
 #include "attn_device.h"
@@ -91,10 +91,26 @@ void fwd_kernel(FwdArgs a) {
   const int nqt = (a.S + BM - 1) / BM;
   const int bid = blockIdx.x;
   const int qt = CAUSAL ? (nqt - 1 - bid / nbh) : (bid / nbh);
-  const int bh = bid % nbh;
-  const int b = bh / a.Hq;
-  const int hq = bh - b * a.Hq;
-  const int hkv = hq / (a.Hq / a.Hkv);
+  // Head of this workgroup.  Workgroups go to the 8 XCDs round-robin (XCD = bid % 8), and
+  // nbh is a multiple of 8 whenever the number of KV groups (B * Hkv) is; then position u
+  // in a query-tile level maps to KV group ((u / 8) / G) * 8 + u % 8 and query head g =
+  // (u / 8) % G of it, so every query head and query tile of one KV group runs on one XCD
+  // and reads its K and V through one L2.
+  const int G = a.Hq / a.Hkv;
+  const int ngrp = a.B * a.Hkv;
+  const int u = bid % nbh;
+  int kvg, g;
+  if ((ngrp & 7) == 0) {
+    const int jj = u >> 3;
+    kvg = (jj / G) * 8 + (u & 7);
+    g = jj - (jj / G) * G;
+  } else {
+    kvg = u / G;
+    g = u - kvg * G;
+  }
+  const int b = kvg / a.Hkv;
+  const int hkv = kvg - b * a.Hkv;
+  const int hq = hkv * G + g;
   const int q0 = qt * BM;
   // Rows of this (batch or sequence, head): S of them, D elements each, rs_q / rs_kv
   // elements apart; LSE of query i at lse[lse0 + i].
