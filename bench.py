@@ -95,6 +95,26 @@ def copy_calibration(mib: int) -> None:
     print(json.dumps({"copy_calibration_bytes_read": n, "copy_calibration_bytes_written": n, "calls": 3}), flush=True)
 
 
+def mfma_ceiling():
+    """The chip's sustained dense bf16 MFMA rate with N(0,1) bf16 operands, from the
+    stand-alone probe (exact_attention_27_amd/csrc/probes/mfma_ceiling.hip, built by
+    build()), run as a child process; None if the probe is not built or fails."""
+    exe = os.path.join(ROOT, "exact_attention_27_amd", "probes", "mfma_ceiling")
+    if not os.path.exists(exe):
+        return None
+    import subprocess
+    try:
+        r = subprocess.run([exe, "--json"], capture_output=True, text=True, timeout=120)
+        rec = json.loads(r.stdout.strip().splitlines()[-1]) if r.returncode == 0 else None
+    except (subprocess.SubprocessError, ValueError, IndexError):
+        rec = None
+    if rec is None:
+        return None
+    return {"value": rec["tflops"], "unit": "TFLOP/s", "operands": "random N(0,1) bf16",
+            "probe": "csrc/probes/mfma_ceiling.hip, 8 launches of back-to-back v_mfma_f32_32x32x16_bf16, "
+                     "2 waves per SIMD, after the timed region"}
+
+
 def cpu_baseline(w, inputs, target_s):
     """The fp64 oracle (fwd + bwd of one (batch, query head) pair at a time, at the
     workload's full S) on this host, until about target_s seconds have passed."""
@@ -218,6 +238,9 @@ def main_varlen(args, w):
                 "traffic": traffic_record("fwd_kernel", w.name),
                 "traffic_unit": "bytes per launch (HBM, rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
                 "avg_launch_ms": round(fwd_ms, 4)}
+    ceiling = mfma_ceiling()
+    if ceiling:
+        roofline["frac_of_measured_ceiling"] = round(fwd_tf / ceiling["value"], 4)
     cpu = None if args.no_cpu_baseline else cpu_baseline_varlen(w, host, args.cpu_seconds)
     line = {
         "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
@@ -228,7 +251,7 @@ def main_varlen(args, w):
                    "passes": "fwd", "exp_mode": int(opt.exp_mode), "tau": float(opt.tau),
                    "variant": int(opt.variant), "step_flop": flop},
         "frac_of_peak": round(value / PEAK_BF16_TFLOPS, 4),
-        "roofline": roofline, "breakdown": {"fwd_ms": round(fwd_ms, 4), "fwd_tflops": round(fwd_tf, 2)},
+        "roofline": roofline, "mfma_ceiling": ceiling, "breakdown": {"fwd_ms": round(fwd_ms, 4), "fwd_tflops": round(fwd_tf, 2)},
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
@@ -330,6 +353,9 @@ def main():
         breakdown.update({"bwd_ms": round(bwd_ms, 4), "bwd_tflops": round(bwd_tf, 2),
                           "bwd_frac_of_peak": round(bwd_tf / PEAK_BF16_TFLOPS, 4)})
 
+    ceiling = mfma_ceiling()
+    if ceiling:
+        roofline["frac_of_measured_ceiling"] = round(achieved / ceiling["value"], 4)
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(w, host, args.cpu_seconds)
@@ -342,7 +368,7 @@ def main():
                    "causal": w.causal, "passes": "+".join(w.passes), "exp_mode": int(opt.exp_mode),
                    "tau": float(opt.tau), "variant": int(opt.variant), "step_flop": flop},
         "frac_of_peak": round(value / PEAK_BF16_TFLOPS, 4),
-        "roofline": roofline, "breakdown": breakdown, "cpu_baseline": cpu,
+        "roofline": roofline, "mfma_ceiling": ceiling, "breakdown": breakdown, "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
 

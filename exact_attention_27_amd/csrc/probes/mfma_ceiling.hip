@@ -14,7 +14,8 @@
 //
 // Build and run (any directory):
 //   hipcc --offload-arch=gfx950 -O3 -o /tmp/mfma_ceiling <repo>/exact_attention_27_amd/csrc/probes/mfma_ceiling.hip
-//   /tmp/mfma_ceiling
+//   /tmp/mfma_ceiling           both operand sets, twice, as text
+//   /tmp/mfma_ceiling --json    the random set once, as one JSON line (what bench.py reads)
 #include <hip/hip_runtime.h>
 
 #include <cstdio>
@@ -60,7 +61,7 @@ void mfma_loop(const u32x4* src, float* out, int iters) {
 }
 
 template <bool RANDOM>
-bool run(const char* name, const u32x4* src, float* out, int iters) {
+bool run(const char* name, const u32x4* src, float* out, int iters, bool json = false) {
   hipEvent_t e0, e1;
   if (hipEventCreate(&e0) != hipSuccess || hipEventCreate(&e1) != hipSuccess) return false;
   hipLaunchKernelGGL((mfma_loop<RANDOM>), dim3(kBlocks), dim3(256), 0, 0, src, out, iters / 8);
@@ -70,15 +71,20 @@ bool run(const char* name, const u32x4* src, float* out, int iters) {
   float ms = 0.f;
   if (hipEventElapsedTime(&ms, e0, e1) != hipSuccess) return false;
   const double products = 8.0 * kBlocks * 4 * (double)iters * 8;
-  std::printf("%-9s operands: %8.2f ms for 8 launches, %7.1f TFLOP/s bf16 dense\n", name, ms,
-              products * 32768.0 / (ms * 1e-3) / 1e12);
+  const double tflops = products * 32768.0 / (ms * 1e-3) / 1e12;
+  if (json) {
+    std::printf("{\"operands\": \"%s\", \"tflops\": %.1f, \"ms\": %.2f, \"launches\": 8}\n", name, tflops, ms);
+  } else {
+    std::printf("%-9s operands: %8.2f ms for 8 launches, %7.1f TFLOP/s bf16 dense\n", name, ms, tflops);
+  }
   std::fflush(stdout);
   return true;
 }
 
 }  // namespace
 
-int main() {
+int main(int argc, char** argv) {
+  const bool json = argc > 1 && std::strcmp(argv[1], "--json") == 0;
   static unsigned short h[kFragWords * 8];
   unsigned st = 12345u;
   for (int i = 0; i < kFragWords * 8; ++i) {
@@ -96,8 +102,9 @@ int main() {
   if (hipMalloc(&src, sizeof(h)) != hipSuccess || hipMalloc(&out, (size_t)kBlocks * 256 * 4) != hipSuccess) return 1;
   if (hipMemcpy(src, h, sizeof(h), hipMemcpyHostToDevice) != hipSuccess) return 1;
   const int iters = 4096 * 8;
-  bool ok = run<false>("constant", src, out, iters) && run<true>("random", src, out, iters) &&
-            run<false>("constant", src, out, iters) && run<true>("random", src, out, iters);
+  bool ok = json ? run<true>("random", src, out, iters, true)
+                 : (run<false>("constant", src, out, iters) && run<true>("random", src, out, iters) &&
+                    run<false>("constant", src, out, iters) && run<true>("random", src, out, iters));
   ok = ok && hipDeviceSynchronize() == hipSuccess;
   return ok ? 0 : 1;
 }

@@ -48,3 +48,12 @@ def test_traffic_goes_null_when_the_kernel_changes(tmp_path, monkeypatch, kernel
     path.write_bytes(path.read_bytes() + b"\n// changed\n")
     assert bench.traffic_record(kernel, workload) is None
     assert bench.traffic_record(kernel, "no_such_workload") is None
+
+
+def test_mfma_ceiling_probe_is_optional_without_a_gpu():
+    """bench.py runs the stand-alone MFMA ceiling probe as a child process; without a GPU
+    (or without the built probe) it reports null instead of failing."""
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present: the probe would run")
+    assert bench.mfma_ceiling() is None
