@@ -136,8 +136,10 @@ int attn_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse
  * positions >= max_seqlen within their sequence are not written; the rows that are
  * written still attend over their whole sequence's keys (all of them when non-causal).
  * The library does not read cu_seqlens on the host (it is device memory and the call is
- * asynchronous); offsets outside [0, total] are clamped (and a decreasing offset gives
- * an empty sequence), so no access leaves the tensors.  Rows not covered by any sequence
+ * asynchronous); offsets outside [0, total] are clamped and a sequence whose end lies
+ * before its start is empty, so no access leaves the tensors.  Offsets that are not
+ * non-decreasing can make two sequences overlap; rows written by both then hold either
+ * result (unspecified).  Rows not covered by any sequence
  * are left unwritten.  nseq == 0, total == 0 or max_seqlen == 0 is an empty problem
  * (ATTN_OK, nothing launched).  Other conventions as above; opt == NULL means the
  * defaults.

@@ -1,4 +1,5 @@
-"""GPU parity on the five workload configurations, at full size, in the launch
+"""GPU parity on the dense workload configurations (the five headline ones and the long-context
+rows: 64k, 128k GQA, non-causal 32k), at full size, in the launch
 configuration bench.py times (default options, one stream).
 
 Bar (plain, no floor allowance): bf16 outputs max-abs <= 2e-2 and mean-abs <= 2e-3
