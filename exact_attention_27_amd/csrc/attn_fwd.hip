@@ -1,11 +1,11 @@
 // attn_fwd.hip - forward pass of exact attention on gfx950 (CDNA4).
 //
-// One workgroup of 4 waves owns 128 consecutive queries of one (batch, query head);
-// each wave owns 32 of them.  The workgroup walks the key/value sequence in tiles of
-// 64 keys that are staged through LDS and shared by its 4 waves; the S x S score
-// matrix never leaves registers (the memory-traffic argument of "NVIDIA Blackwell:
-// FlashAttention-4 Overcomes Memory Bottlenecks", body paragraph, and of the
-// hyper.ai FlashAttention-4 story).
+// One workgroup of W waves (4 by default, 8 for the ping-pong schedule) owns 32 W
+// consecutive queries of one (batch, query head); each wave owns 32 of them.  The
+// workgroup walks the key/value sequence in tiles of 64 keys that are staged through LDS
+// and shared by its waves; the S x S score matrix never leaves registers (the
+// memory-traffic argument of "NVIDIA Blackwell: FlashAttention-4 Overcomes Memory
+// Bottlenecks", body paragraph, and of the hyper.ai FlashAttention-4 story).
 //
 // Per key tile, each wave computes the transposed scores S^T = K Q^T with
 // v_mfma_f32_32x32x16_bf16 (K from LDS as the A operand, Q^T held in registers as the
@@ -32,7 +32,8 @@
 // Both phases are written out as slots of one matrix product each, fenced so the
 // compiler keeps them: a slot issues the LDS reads of the slot two ahead, its product,
 // and its share of the vector work.  The matrix cores of a SIMD are shared by two
-// waves (of different workgroups), which fill each other's gaps.
+// waves, which fill each other's gaps: of two different workgroups for W = 4, or of the
+// two halves of one workgroup, kept half a step apart, for W = 8.
 //
 // Causal masking: key tiles above the diagonal of the workgroup are never loaded;
 // only tiles that straddle the diagonal or the end of the sequence are masked.
@@ -269,9 +270,10 @@ void fwd_kernel(FwdArgs a) {
   if (nkv > 1) dma_v(1, Vring + TILE);
   int r_cur = 0;  // V ring slot of V_s, s % VR
 
-  // One key tile: S_j (in cur) -> O; S_{j+1} (into nxt).  P is the ring parity of j;
-  // the loop below is unrolled by two so that every LDS slot offset is a constant and
-  // the score registers swap roles instead of being copied.
+  // One key tile: S_j (in cur) -> O; S_{j+1} (into nxt).  P is the K ring parity of j;
+  // the loop below is unrolled by two so that the K slot offsets are constants and the
+  // score registers swap roles instead of being copied (the V slot, r_cur, is one
+  // wave-uniform value per step).
   auto step = [&](const int j, f32x16 (&cur)[KB], f32x16 (&nxt)[KB], auto parity) {
     constexpr int P = decltype(parity)::value;  // j % 2
     const int r1 = r_cur == VR - 1 ? 0 : r_cur + 1;                 // V slot of V_{j+1}
@@ -280,9 +282,9 @@ void fwd_kernel(FwdArgs a) {
     const char* Vs = (const char*)(Vring + r_cur * TILE) + v_lds;    // V_j
     // This step's barrier (j+1): wait for this wave's share of K_{j+2} and V_{j+1}, meet
     // the other waves, then start K_{j+3} (into K_{j+1}'s slot, read by both groups in
-    // phase 1, before their barrier) and V_{j+2} (into the slot of V_{j-1} for W = 8,
-    // whose last reader, group 1, finished it before the previous barrier; of V_j for
-    // W = 4, read by every wave in phase 2, before this barrier).
+    // phase 1, before their barrier) and V_{j+2}: for W = 8 into the slot of V_{j-1},
+    // whose last reader (group 1, phase 2 of step j-1) finished before reaching this
+    // barrier; for W = 4 into the slot of V_j, read by every wave in phase 2, before it.
     auto barrier = [&]() {
       wait_dma();
       __syncthreads();
