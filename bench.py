@@ -309,11 +309,19 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    # A forward-only step is one launch: one event pair around the whole timed loop gives
+    # its average duration back to back.  The backward's phases need events between them.
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps if do_bwd else 1)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(evs[i])
+    if do_bwd:
+        for i in range(args.steps):
+            step(evs[i])
+    else:
+        evs[0][0].record(stream)
+        for i in range(args.steps):
+            step()
+        evs[0][1].record(stream)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
 

@@ -111,6 +111,25 @@ def _ptr(t: Optional[torch.Tensor]):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
+class _Nothing:
+    def __enter__(self):
+        return None
+
+    def __exit__(self, *exc):
+        return False
+
+
+_NOTHING = _Nothing()
+
+
+def _on(device: torch.device):
+    """torch.cuda.device(device), or nothing when it is already the current device (the
+    context manager costs microseconds per call, which short launches feel)."""
+    if device.type == "cuda" and device.index is not None and device.index == torch.cuda.current_device():
+        return _NOTHING
+    return torch.cuda.device(device)
+
+
 def _stream(stream) -> ctypes.c_void_p:
     if stream is None:
         stream = torch.cuda.current_stream()
@@ -172,7 +191,7 @@ def attn_fwd_ex(q, k, v, scale: Optional[float] = None, causal: bool = False,
     _need(lse, "lse", torch.float32, (B, Hq, S))
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
     op = _options(opt, exp_mode, tau, variant)
-    with torch.cuda.device(q.device):
+    with _on(q.device):
         st = lib().attn_fwd_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, Hq, Hkv, S, d,
                                scale, int(bool(causal)), None if op is None else ctypes.byref(op),
                                _stream(stream))
@@ -211,7 +230,7 @@ def attn_fwd_varlen(q, k, v, cu_seqlens, max_seqlen: int, scale: Optional[float]
     _need(lse, "lse", torch.float32, (Hq, total))
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
     op = _options(opt, exp_mode, tau, variant)
-    with torch.cuda.device(q.device):
+    with _on(q.device):
         st = lib().attn_fwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(cu_seqlens),
                                    max(nseq, 0), total, int(max_seqlen), Hq, Hkv, d, scale, int(bool(causal)),
                                    None if op is None else ctypes.byref(op), _stream(stream))
@@ -267,7 +286,7 @@ def attn_bwd_phase(phase: int, q, k, v, o, lse, do, scale: Optional[float] = Non
         raise ValueError("workspace must be a contiguous GPU tensor")
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
     op = _options(opt, exp_mode, tau)
-    with torch.cuda.device(q.device):
+    with _on(q.device):
         st = lib().attn_bwd_phase(int(phase), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(do),
                                _ptr(dq), _ptr(dk), _ptr(dv), B, Hq, Hkv, S, d, scale,
                                int(bool(causal)), _ptr(workspace),
