@@ -169,6 +169,9 @@ __host__ __device__ constexpr int blk_chunk_inner_x(int r, int c) {
 // not make every later LDS read wait for it.  The block has no register outputs; the
 // LDS it writes is read only after wait_dma()/vmcnt waits and a barrier, which the
 // kernels place explicitly.  lds_wave_base must be the same for all lanes of the wave.
+// The DMA takes its LDS address from m0, which the block sets; the compiler treats m0 as
+// reserved and warns about the clobber, but it uses m0 nowhere in these kernels (every
+// m0 write in their assembly is one of these blocks; tests/test_isa.py checks that).
 // ---------------------------------------------------------------------------------
 // LDS byte address of a generic pointer into LDS: a generic LDS address is the LDS
 // aperture in the upper 32 bits and the LDS byte address in the lower 32, so truncation
@@ -184,8 +187,6 @@ __device__ __forceinline__ void dma16(const void* g, const void* lds_wave_base) 
                    : "memory", "m0");
 }
 
-// The same with a scalar (wave-uniform) 64-bit base and a 32-bit per-lane byte offset:
-// no per-lane address arithmetic when the offsets stay fixed across a loop.
 // A wave-uniform pointer moved to scalar registers (lane 0's copy).  For code where the
 // compiler cannot prove uniformity (divergent branches) but a scalar base is required.
 // readfirstlane returns a signed int: both halves go through uint32_t so that neither
@@ -197,6 +198,8 @@ __device__ __forceinline__ const void* uniform_ptr(const void* p) {
   return (const void*)(uintptr_t)(((uint64_t)hi << 32) | (uint64_t)lo);
 }
 
+// dma16 with a scalar (wave-uniform) 64-bit base and a 32-bit per-lane byte offset:
+// no per-lane address arithmetic when the offsets stay fixed across a loop.
 __device__ __forceinline__ void dma16_s(const void* sbase, uint32_t voff, const void* lds_wave_base) {
   const uint32_t l = lds_addr(lds_wave_base);
   const uint32_t ls = __builtin_amdgcn_readfirstlane(l);
