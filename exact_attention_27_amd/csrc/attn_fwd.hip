@@ -270,12 +270,15 @@ void fwd_kernel(FwdArgs a) {
   if (nkv > 1) dma_v(1, Vring + TILE);
   int r_cur = 0;  // V ring slot of V_s, s % VR
 
-  // One key tile: S_j (in cur) -> O; S_{j+1} (into nxt).  P is the K ring parity of j;
-  // the loop below is unrolled by two so that the K slot offsets are constants and the
-  // score registers swap roles instead of being copied (the V slot, r_cur, is one
-  // wave-uniform value per step).
-  auto step = [&](const int j, f32x16 (&cur)[KB], f32x16 (&nxt)[KB], auto parity) {
-    constexpr int P = decltype(parity)::value;  // j % 2
+  // One key tile: S_j (in cur) -> O; S_{j+1} (into nxt).  P is the K ring parity of j,
+  // a constant in computing steps: their loop is unrolled by two so that the K slot
+  // offsets are constants and the score registers swap roles instead of being copied
+  // (the V slot, r_cur, is one wave-uniform value per step).  A dead step (DEAD true:
+  // a tile wholly above the wave's queries) only meets the barrier and issues the wave's
+  // share of the DMA, in which every wave of the workgroup takes part.
+  auto step = [&](const int j, f32x16 (&cur)[KB], f32x16 (&nxt)[KB], auto parity, auto dead) {
+    const int P = parity;  // j % 2
+    constexpr bool DEAD = decltype(dead)::value;
     const int r1 = r_cur == VR - 1 ? 0 : r_cur + 1;                 // V slot of V_{j+1}
     const int r2 = r1 == VR - 1 ? 0 : r1 + 1;                       // V slot of V_{j+2}
     const char* Ks = (const char*)(Kring + (1 - P) * TILE);          // K_{j+1}
@@ -291,6 +294,11 @@ void fwd_kernel(FwdArgs a) {
       if (j + 3 < nkv) dma_k(j + 3, Kring + (1 - P) * TILE);
       if (j + 2 < nkv) dma_v(j + 2, Vring + r2 * TILE);
     };
+    if constexpr (DEAD) {
+      barrier();
+      r_cur = r1;
+      return;
+    }
 
     // LDS reads of slot i: the K fragment of product i of phase 1, or the two V^T
     // halves of product i - NQK of phase 2.
@@ -373,11 +381,19 @@ void fwd_kernel(FwdArgs a) {
     }
   };
 
+  // This wave's live tiles: all nkv, or under the causal mask those holding a key at or
+  // below its last query (wave-uniform, at least 1).  The steps past them are dead.  (The
+  // last live step still forms S_{nlive} and discards it: peeling that step off costs
+  // more registers than the 16 products it would save.)
+  const int nlive = CAUSAL ? min(nkv, (min(S, q0 + wave_u * 32 + 32) + BN - 1) / BN) : nkv;
+  using Even = std::integral_constant<int, 0>;
+  using Odd = std::integral_constant<int, 1>;
   f32x16 sn[KB];
-  for (int j = 0; j < nkv; j += 2) {
-    step(j, sc, sn, std::integral_constant<int, 0>{});
-    if (j + 1 < nkv) step(j + 1, sn, sc, std::integral_constant<int, 1>{});
+  for (int j = 0; j < nlive; j += 2) {
+    step(j, sc, sn, Even{}, std::false_type{});
+    if (j + 1 < nlive) step(j + 1, sn, sc, Odd{}, std::false_type{});
   }
+  for (int j = nlive; j < nkv; ++j) step(j, sc, sn, j & 1, std::true_type{});
 
   // Epilogue: O = O_acc / l (bf16, round to nearest even) and LSE in natural log.
   const float l = sum_halves(l_run);
