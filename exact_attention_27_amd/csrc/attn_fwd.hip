@@ -74,7 +74,6 @@ void fwd_kernel(FwdArgs a) {
   constexpr int NPV = 2 * KB * DBLK;    // phase-2 slots (products of O^T)
   constexpr int NE = KB * 16;           // scores per lane per tile
   constexpr int EPS = NE / NQK;         // exponentials per phase-1 slot
-  constexpr int MAX0 = NPV / 4;         // first phase-2 slot that takes part of the maximum
   constexpr int PD = FWD_PD;
   static_assert(NE % NQK == 0 && EPS % 2 == 0, "exponentials must pair up per slot");
   static_assert(BN % 32 == 0 && DMAS * 64 * W == BN * CPR, "tile must split evenly over the threads");
@@ -210,6 +209,7 @@ void fwd_kernel(FwdArgs a) {
   float l_run = 0.0f;       // this lane's part of the running row sum
   const float c = a.c;
   const float tau = a.tau;
+  const float thr = exp2f(tau - 1.0f);  // partial row sum that calls for the rescale test
 
   // Tiles that reach past the end of the sequence or (causal) past the wave's first
   // query: the only ones with masked scores.
@@ -264,7 +264,9 @@ void fwd_kernel(FwdArgs a) {
     for (int kb = 0; kb < KB; ++kb)
       sc[kb] = mfma32(*(const bf16x8*)((const char*)Kring + k_off(kb, ks)), qf[ks], sc[kb]);
   if (needs_mask(0)) mask(sc, 0);
-  float mt = tile_max(sc);  // scaled maximum of the score tile the next step exponentiates
+  // The first reference maximum is S_0's (O and the row sum are still zero, so nothing
+  // needs rescaling).
+  m_ref = tile_max(sc);
   __syncthreads();  // every wave has read K_0
   if (nkv > 2) dma_k(2, Kring);
   if (nkv > 1) dma_v(1, Vring + TILE);
@@ -316,69 +318,74 @@ void fwd_kernel(FwdArgs a) {
 #pragma unroll
     for (int i = 0; i < PD; ++i) issue(i);
 
-    // The (rare) rescale.  mt is the scaled maximum of S_j, found while the previous
-    // step's PV products ran; one wave-uniform branch.
-    if (wave_any(mt > m_ref + tau)) {
-      const float m_new = fmaxf(m_ref, mt);
-      const float alpha = (m_new == -INFINITY) ? 1.0f : exp2_sm<0>(m_ref - m_new);
-#pragma unroll
-      for (int db = 0; db < DBLK; ++db) oacc[db] *= alpha;
-      l_run *= alpha;
-      m_ref = m_new;
-    }
-    const float mu = m_ref == -INFINITY ? 0.0f : m_ref;
+    float mu = m_ref == -INFINITY ? 0.0f : m_ref;
 
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) nxt[kb] = f32x16{};
     uint32_t pw[KB][2][4];  // P_j packed to bf16 pairs: [key block][16-key half][pair]
-    float lt0 = 0.0f, lt1 = 0.0f, mx = -INFINITY;
+    float lt0 = 0.0f, lt1 = 0.0f;
+    // Exponentials of S_j registers e, e+1 with the reference maximum m_ref, into pw and
+    // (lt0, lt1).  Called with compile-time e only (unrolled loops), so pw stays in
+    // registers.
+    auto exp_pair = [&](const int e) {
+      const float p0 = exp2_sm<EXPMODE>(fmaf(cur[e >> 4][e & 15], c, -mu));
+      const float p1 = exp2_sm<EXPMODE>(fmaf(cur[e >> 4][(e & 15) + 1], c, -mu));
+      lt0 += p0;
+      lt1 += p1;
+      pw[e >> 4][(e >> 3) & 1][(e & 7) >> 1] = pack_bf16x2(p0, p1);
+    };
     __builtin_amdgcn_sched_barrier(0);
+    // Phase 1: the NQK products of S_{j+1}, EPS exponentials of S_j beside each.
 #pragma unroll
-    for (int i = 0; i < NQK + NPV; ++i) {
-      if (i == NQK) {
-        if (grp != 0) barrier();
-        __builtin_amdgcn_sched_barrier(0);
-      }
+    for (int i = 0; i < NQK; ++i) {
       issue(i + PD);
-      if (i < NQK) {
-        // Phase 1: one product of S_{j+1}; EPS exponentials of S_j.
-        const int kb = i % KB, ks = i / KB;
-        nxt[kb] = mfma32(kfrag[i], qf[ks], nxt[kb]);
+      const int kb = i % KB, ks = i / KB;
+      nxt[kb] = mfma32(kfrag[i], qf[ks], nxt[kb]);
 #pragma unroll
-        for (int e = i * EPS; e < (i + 1) * EPS; e += 2) {
-          const float p0 = exp2_sm<EXPMODE>(fmaf(cur[e >> 4][e & 15], c, -mu));
-          const float p1 = exp2_sm<EXPMODE>(fmaf(cur[e >> 4][(e & 15) + 1], c, -mu));
-          lt0 += p0;
-          lt1 += p1;
-          pw[e >> 4][(e >> 3) & 1][(e & 7) >> 1] = pack_bf16x2(p0, p1);
-        }
-        // Keep the row-sum additions in this slot (they would otherwise sink below the
-        // barrier, where no matrix product runs beside them).
-        __asm__ volatile("" : "+v"(lt0), "+v"(lt1));
-      } else {
-        // Phase 2: one product of O^T; part of the maximum of S_{j+1} once its last
-        // products have had time to finish.
-        const int p = i - NQK, db = p % DBLK, kb = p / (2 * DBLK), t = (p / DBLK) & 1;
-        const u32x4 w = {pw[kb][t][0], pw[kb][t][1], pw[kb][t][2], pw[kb][t][3]};
-        oacc[db] = mfma32(join(vlo[p], vhi[p]), __builtin_bit_cast(bf16x8, w), oacc[db]);
-        if (p >= MAX0) {
-          const int e0 = (p - MAX0) * NE / (NPV - MAX0), e1 = (p - MAX0 + 1) * NE / (NPV - MAX0);
+      for (int e = i * EPS; e < (i + 1) * EPS; e += 2) exp_pair(e);
+      // Keep the row-sum additions in this slot (they would otherwise sink below the
+      // barrier, where no matrix product runs beside them).
+      __asm__ volatile("" : "+v"(lt0), "+v"(lt1));
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // The (rare) rescale, decided after the exponentials.  A score more than tau above
+    // m_ref gives p > 2^tau, so while every lane's partial sum stays below 2^(tau-1) no
+    // rescale is due.  Otherwise take S_j's maximum and apply the rule exactly: if it
+    // exceeds m_ref + tau anywhere in the wave, rescale O^T and the running sum by
+    // 2^(m_ref - m_new), move m_ref and redo the exponentials.  One wave-uniform branch
+    // per step.
+    if (wave_any(!(lt0 + lt1 < thr) || m_ref == -INFINITY)) {
+      const float mt = tile_max(cur);
+      if (wave_any(mt > m_ref + tau)) {
+        const float m_new = fmaxf(m_ref, mt);
+        const float alpha = (m_new == -INFINITY) ? 1.0f : exp2_sm<0>(m_ref - m_new);
 #pragma unroll
-          for (int e = e0; e < e1; ++e) mx = fmaxf(mx, nxt[e >> 4][e & 15]);
-        }
+        for (int db = 0; db < DBLK; ++db) oacc[db] *= alpha;
+        l_run *= alpha;
+        m_ref = m_new;
+        mu = m_ref == -INFINITY ? 0.0f : m_ref;
+        lt0 = lt1 = 0.0f;
+#pragma unroll
+        for (int e = 0; e < NE; e += 2) exp_pair(e);
       }
+    }
+    if (grp != 0) barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    // Phase 2: the NPV products of O^T.
+#pragma unroll
+    for (int i = NQK; i < NQK + NPV; ++i) {
+      issue(i + PD);
+      const int p = i - NQK, db = p % DBLK, kb = p / (2 * DBLK), t = (p / DBLK) & 1;
+      const u32x4 w = {pw[kb][t][0], pw[kb][t][1], pw[kb][t][2], pw[kb][t][3]};
+      oacc[db] = mfma32(join(vlo[p], vhi[p]), __builtin_bit_cast(bf16x8, w), oacc[db]);
       __builtin_amdgcn_sched_barrier(0);
     }
     l_run += lt0 + lt1;
-    mt = max_halves(mx) * c;
     if (grp == 0) barrier();
     r_cur = r1;
     // S_{j+1} as computed is exact except on tiles that need a mask (at most the last
-    // two of a wave): mask those and take their maximum again.
-    if (j + 1 < nkv && needs_mask((j + 1) * BN)) {
-      mask(nxt, (j + 1) * BN);
-      mt = tile_max(nxt);
-    }
+    // two of a wave).
+    if (j + 1 < nkv && needs_mask((j + 1) * BN)) mask(nxt, (j + 1) * BN);
   };
 
   // This wave's live tiles: all nkv, or under the causal mask those holding a key at or
