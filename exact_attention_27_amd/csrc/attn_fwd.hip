@@ -25,18 +25,22 @@
 // rescales O^T and the running sum by 2^(m_ref - m_new) and moves m_ref; otherwise
 // the probabilities 2^(x - m_ref) are used as they are (they stay <= 2^tau).  Since
 // O and the sum always share m_ref, the final O = O_acc / l is exact for every tau.
+// The tile maximum itself is only taken when the test can fire: the exponentials are
+// computed with m_ref first, and unless some lane's partial row sum reaches 2^(tau-1)
+// (which any score above m_ref + tau forces) no rescale is due.
 //
 // Software pipeline of one key tile j (a "step"), per wave: the products of tile j+1's
 // scores S_{j+1} = K_{j+1} Q^T are issued while the vector units exponentiate S_j
-// (phase 1), then O^T += V_j^T P_j^T while they take the maximum of S_{j+1} (phase 2).
+// (phase 1), then, after the rescale test, O^T += V_j^T P_j^T (phase 2).
 // Both phases are written out as slots of one matrix product each, fenced so the
 // compiler keeps them: a slot issues the LDS reads of the slot two ahead, its product,
 // and its share of the vector work.  The matrix cores of a SIMD are shared by two
 // waves, which fill each other's gaps: of two different workgroups for W = 4, or of the
 // two halves of one workgroup, kept half a step apart, for W = 8.
 //
-// Causal masking: key tiles above the diagonal of the workgroup are never loaded;
-// only tiles that straddle the diagonal or the end of the sequence are masked.
+// Causal masking: key tiles above the diagonal of the workgroup are never loaded, and a
+// wave skips the loaded tiles that lie wholly above its own queries; only tiles that
+// straddle the diagonal or the end of the sequence are masked.
 // Workgroups are dispatched longest-first (largest query tile index first), and when the
 // number of KV groups is a multiple of 8 all query heads and query tiles of one KV group
 // run on one XCD and share its L2 for K and V.
