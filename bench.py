@@ -263,8 +263,9 @@ def main():
         copy_calibration(args.copy_calibration)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this library has no multi-GPU path "
-              "(see DESIGN.md for how attention would shard); run with --gpus 1", file=sys.stderr)
+        print("bench.py measures one GPU only: this library has no multi-GPU path (attention "
+              "would shard over batch and heads with no exchange, each GPU running these kernels "
+              "on its share); run with --gpus 1", file=sys.stderr)
         sys.exit(2)
 
     import torch

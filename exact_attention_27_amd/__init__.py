@@ -139,16 +139,27 @@ def _stream(stream) -> ctypes.c_void_p:
 
 
 def _need(t: torch.Tensor, name: str, dtype: torch.dtype, shape) -> None:
+    """Type, dtype, shape and layout of one operand (the device is checked by _same_gpu)."""
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a torch.Tensor")
-    if t.device.type != "cuda":
-        raise ValueError(f"{name} must be on a GPU device (got {t.device})")
     if t.dtype != dtype:
         raise TypeError(f"{name} must be {dtype} (got {t.dtype})")
     if tuple(t.shape) != tuple(shape):
         raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
+
+
+def _same_gpu(**tensors) -> None:
+    """Every operand on one GPU device (the first one's)."""
+    device = None
+    for name, t in tensors.items():
+        if t.device.type != "cuda":
+            raise ValueError(f"{name} must be on a GPU device (got {t.device})")
+        if device is None:
+            device = t.device
+        elif t.device != device:
+            raise ValueError(f"{name} is on {t.device}, the other operands on {device}")
 
 
 def _options(opt, exp_mode, tau, variant=None):
@@ -189,6 +200,7 @@ def attn_fwd_ex(q, k, v, scale: Optional[float] = None, causal: bool = False,
         lse = torch.empty((B, Hq, S), dtype=torch.float32, device=q.device)
     _need(o, "o", torch.bfloat16, (B, Hq, S, d))
     _need(lse, "lse", torch.float32, (B, Hq, S))
+    _same_gpu(q=q, k=k, v=v, o=o, lse=lse)
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
     op = _options(opt, exp_mode, tau, variant)
     with _on(q.device):
@@ -219,8 +231,6 @@ def attn_fwd_varlen(q, k, v, cu_seqlens, max_seqlen: int, scale: Optional[float]
     _need(v, "v", torch.bfloat16, (total, Hkv, d))
     if cu_seqlens.dtype != torch.int32 or cu_seqlens.dim() != 1 or not cu_seqlens.is_contiguous():
         raise ValueError("cu_seqlens must be a contiguous 1-D int32 tensor")
-    if cu_seqlens.device != q.device:
-        raise ValueError("cu_seqlens must be on the same device as q")
     nseq = int(cu_seqlens.numel()) - 1
     if o is None:
         o = torch.empty_like(q)
@@ -228,6 +238,7 @@ def attn_fwd_varlen(q, k, v, cu_seqlens, max_seqlen: int, scale: Optional[float]
         lse = torch.empty((Hq, total), dtype=torch.float32, device=q.device)
     _need(o, "o", torch.bfloat16, (total, Hq, d))
     _need(lse, "lse", torch.float32, (Hq, total))
+    _same_gpu(q=q, k=k, v=v, cu_seqlens=cu_seqlens, o=o, lse=lse)
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
     op = _options(opt, exp_mode, tau, variant)
     with _on(q.device):
@@ -279,11 +290,13 @@ def attn_bwd_phase(phase: int, q, k, v, o, lse, do, scale: Optional[float] = Non
     _need(dq, "dq", torch.bfloat16, (B, Hq, S, d))
     _need(dk, "dk", torch.bfloat16, (B, Hkv, S, d))
     _need(dv, "dv", torch.bfloat16, (B, Hkv, S, d))
+    if workspace is not None and (not isinstance(workspace, torch.Tensor) or not workspace.is_contiguous()):
+        raise ValueError("workspace must be a contiguous tensor")
+    _same_gpu(q=q, k=k, v=v, o=o, lse=lse, do=do, dq=dq, dk=dk, dv=dv,
+              **({} if workspace is None else {"workspace": workspace}))
     nbytes = attn_bwd_workspace_bytes(B, Hq, Hkv, S, d)
     if workspace is None:
         workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
-    elif workspace.device.type != "cuda" or not workspace.is_contiguous():
-        raise ValueError("workspace must be a contiguous GPU tensor")
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
     op = _options(opt, exp_mode, tau)
     with _on(q.device):

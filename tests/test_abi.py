@@ -169,10 +169,49 @@ def test_fwd_varlen_empty_is_ok_without_launch(kw):
 
 
 def test_fwd_varlen_binding_checks_arguments():
+    """Operand checks run before the device check, so CPU tensors reach each of them."""
     import torch
     q = torch.zeros(10, 2, 64, dtype=torch.bfloat16)
     k = torch.zeros(10, 1, 64, dtype=torch.bfloat16)
-    with pytest.raises(ValueError):
+    cu = torch.tensor([0, 10], dtype=torch.int32)
+    with pytest.raises(ValueError, match="cu_seqlens must be"):
         ea.attn_fwd_varlen(q, k, k, torch.tensor([0, 10], dtype=torch.int64), 10)
-    with pytest.raises(ValueError):
-        ea.attn_fwd_varlen(q, k, k[:9], torch.tensor([0, 10], dtype=torch.int32), 10)
+    with pytest.raises(ValueError, match="has shape"):
+        ea.attn_fwd_varlen(q, k, k[:9], cu, 10)
+    with pytest.raises(TypeError, match="must be torch.bfloat16"):
+        ea.attn_fwd_varlen(q, k, k.float(), cu, 10)
+    with pytest.raises(ValueError, match="must be on a GPU device"):
+        ea.attn_fwd_varlen(q, k, k, cu, 10)
+
+
+def test_fwd_binding_checks_arguments():
+    import torch
+    q = torch.zeros(1, 4, 32, 64, dtype=torch.bfloat16)
+    k = torch.zeros(1, 2, 32, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="q must be"):
+        ea.attn_fwd(q[0], k, k)
+    with pytest.raises(ValueError, match="has shape"):
+        ea.attn_fwd(q, k, k[:, :, :16])
+    with pytest.raises(TypeError, match="must be torch.bfloat16"):
+        ea.attn_fwd(q, k.half(), k)
+    with pytest.raises(ValueError, match="contiguous"):
+        ea.attn_fwd(q, k.transpose(2, 3).contiguous().transpose(2, 3), k)
+    with pytest.raises(ValueError, match="has shape"):
+        ea.attn_fwd(q, k, k, o=torch.zeros(1, 4, 32, 32, dtype=torch.bfloat16))
+    with pytest.raises(ValueError, match="must be on a GPU device"):
+        ea.attn_fwd(q, k, k)
+
+
+def test_bwd_binding_checks_arguments():
+    import torch
+    q = torch.zeros(1, 4, 32, 64, dtype=torch.bfloat16)
+    k = torch.zeros(1, 2, 32, 64, dtype=torch.bfloat16)
+    lse = torch.zeros(1, 4, 32)
+    with pytest.raises(ValueError, match="has shape"):
+        ea.attn_bwd(q, k, k, q, lse[:, :, :16], q)
+    with pytest.raises(TypeError, match="must be torch.float32"):
+        ea.attn_bwd(q, k, k, q, lse.double(), q)
+    with pytest.raises(ValueError, match="workspace must be"):
+        ea.attn_bwd(q, k, k, q, lse, q, workspace=torch.zeros(64, dtype=torch.uint8)[::2])
+    with pytest.raises(ValueError, match="must be on a GPU device"):
+        ea.attn_bwd(q, k, k, q, lse, q)
