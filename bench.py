@@ -29,6 +29,7 @@ if ROOT not in sys.path:
 
 METRIC = "attention fwd/bwd bf16 TFLOPS and % of MI355X MFMA peak, S=2k–32k, d=128"
 PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA, published (256 CU x 4096 flop/clk x 2.4 GHz)
+VARIANT_NAMES = {0: "auto", 1: "pingpong", 2: "fourwave"}
 
 
 
@@ -55,7 +56,8 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target oracle sample time")
     ap.add_argument("--exp-mode", type=int, default=None)
     ap.add_argument("--tau", type=float, default=None)
-    ap.add_argument("--variant", type=int, default=None, help="forward schedule: 0 default, 1 ping-pong")
+    ap.add_argument("--variant", type=int, default=None,
+                    help="forward schedule: 0 auto (default), 1 ping-pong, 2 four-wave")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="instead of the benchmark, run a plain device copy of MIB MiB (3 times): the "
                          "reference kernel that scales rocprofv3 FETCH_SIZE/WRITE_SIZE into bytes")
@@ -249,7 +251,7 @@ def main_varlen(args, w):
         "config": {"workload": w.name, "sequences": w.n, "lengths": f"{min(lens)}..{max(lens)} log-uniform",
                    "total_tokens": total, "Hq": w.Hq, "Hkv": w.Hkv, "d": w.d, "causal": w.causal,
                    "passes": "fwd", "exp_mode": int(opt.exp_mode), "tau": float(opt.tau),
-                   "variant": int(opt.variant), "step_flop": flop},
+                   "variant": VARIANT_NAMES.get(int(opt.variant), int(opt.variant)), "step_flop": flop},
         "frac_of_peak": round(value / PEAK_BF16_TFLOPS, 4),
         "roofline": roofline, "mfma_ceiling": ceiling, "breakdown": {"fwd_ms": round(fwd_ms, 4), "fwd_tflops": round(fwd_tf, 2)},
         "cpu_baseline": cpu,
@@ -375,7 +377,7 @@ def main():
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "S": w.S, "d": w.d,
                    "causal": w.causal, "passes": "+".join(w.passes), "exp_mode": int(opt.exp_mode),
-                   "tau": float(opt.tau), "variant": int(opt.variant), "step_flop": flop},
+                   "tau": float(opt.tau), "variant": VARIANT_NAMES.get(int(opt.variant), int(opt.variant)), "step_flop": flop},
         "frac_of_peak": round(value / PEAK_BF16_TFLOPS, 4),
         "roofline": roofline, "mfma_ceiling": ceiling, "breakdown": breakdown, "cpu_baseline": cpu,
     }

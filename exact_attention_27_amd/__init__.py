@@ -22,13 +22,14 @@ __all__ = [
     "AttnError", "attn_options", "library_path", "lib",
     "attn_fwd", "attn_fwd_ex", "attn_fwd_varlen", "attn_bwd", "attn_bwd_ex", "attn_bwd_phase", "attn_bwd_workspace_bytes",
     "attn_default_options", "attn_status_string", "attn_exp2_eval", "attn_exp2_poly_host",
-    "ATTN_EXP_HW", "ATTN_EXP_POLY3", "ATTN_VARIANT_DEFAULT", "ATTN_VARIANT_PINGPONG",
+    "ATTN_EXP_HW", "ATTN_EXP_POLY3", "ATTN_VARIANT_AUTO", "ATTN_VARIANT_PINGPONG", "ATTN_VARIANT_FOURWAVE",
 ]
 
 ATTN_EXP_HW = 0
 ATTN_EXP_POLY3 = 1
-ATTN_VARIANT_DEFAULT = 0
+ATTN_VARIANT_AUTO = 0
 ATTN_VARIANT_PINGPONG = 1
+ATTN_VARIANT_FOURWAVE = 2
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 
@@ -189,7 +190,8 @@ def attn_fwd_ex(q, k, v, scale: Optional[float] = None, causal: bool = False,
                 tau: Optional[float] = None, stream=None, variant: Optional[int] = None
                 ) -> Tuple[torch.Tensor, torch.Tensor]:
     """Forward pass; returns (o [B,Hq,S,d] bf16, lse [B,Hq,S] fp32).  scale defaults to 1/sqrt(d).
-    variant: ATTN_VARIANT_DEFAULT or ATTN_VARIANT_PINGPONG (the forward schedule)."""
+    variant: ATTN_VARIANT_AUTO (default), ATTN_VARIANT_PINGPONG or ATTN_VARIANT_FOURWAVE (the
+    forward schedule; all give bit-identical results)."""
     B, Hq, Hkv, S, d = _dims(q, k)
     _need(q, "q", torch.bfloat16, (B, Hq, S, d))
     _need(k, "k", torch.bfloat16, (B, Hkv, S, d))

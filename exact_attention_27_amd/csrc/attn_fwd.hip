@@ -444,8 +444,8 @@ hipError_t launch_fwd_w(const FwdArgs& a, bool causal, int exp_mode, hipStream_t
 }
 
 template <int D, bool VARLEN>
-hipError_t launch_fwd_d(const FwdArgs& a, bool causal, int exp_mode, int variant, hipStream_t stream) {
-  return variant == 1 ? launch_fwd_w<D, VARLEN, 8>(a, causal, exp_mode, stream)
+hipError_t launch_fwd_d(const FwdArgs& a, bool causal, int exp_mode, bool pingpong, hipStream_t stream) {
+  return pingpong ? launch_fwd_w<D, VARLEN, 8>(a, causal, exp_mode, stream)
                       : launch_fwd_w<D, VARLEN, 4>(a, causal, exp_mode, stream);
 }
 
@@ -456,14 +456,14 @@ __global__ void exp2_eval_kernel(const float* x, float* y, long n, int mode) {
 
 }  // namespace
 
-hipError_t launch_fwd(const FwdArgs& a, int d, bool causal, int exp_mode, int variant, hipStream_t stream) {
-  return d == 64 ? launch_fwd_d<64, false>(a, causal, exp_mode, variant, stream)
-                 : launch_fwd_d<128, false>(a, causal, exp_mode, variant, stream);
+hipError_t launch_fwd(const FwdArgs& a, int d, bool causal, int exp_mode, bool pingpong, hipStream_t stream) {
+  return d == 64 ? launch_fwd_d<64, false>(a, causal, exp_mode, pingpong, stream)
+                 : launch_fwd_d<128, false>(a, causal, exp_mode, pingpong, stream);
 }
 
-hipError_t launch_fwd_varlen(const FwdArgs& a, int d, bool causal, int exp_mode, int variant, hipStream_t stream) {
-  return d == 64 ? launch_fwd_d<64, true>(a, causal, exp_mode, variant, stream)
-                 : launch_fwd_d<128, true>(a, causal, exp_mode, variant, stream);
+hipError_t launch_fwd_varlen(const FwdArgs& a, int d, bool causal, int exp_mode, bool pingpong, hipStream_t stream) {
+  return d == 64 ? launch_fwd_d<64, true>(a, causal, exp_mode, pingpong, stream)
+                 : launch_fwd_d<128, true>(a, causal, exp_mode, pingpong, stream);
 }
 
 hipError_t launch_exp2_eval(const float* x, float* y, long n, int exp_mode, hipStream_t stream) {

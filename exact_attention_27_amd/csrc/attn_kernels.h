@@ -47,9 +47,9 @@ struct BwdArgs {
   uint32_t q_and, q_xor;
 };
 
-hipError_t launch_fwd(const FwdArgs& a, int d, bool causal, int exp_mode, int variant, hipStream_t stream);
+hipError_t launch_fwd(const FwdArgs& a, int d, bool causal, int exp_mode, bool pingpong, hipStream_t stream);
 // The same forward over a variable-length packed batch (a.cu_seqlens != nullptr).
-hipError_t launch_fwd_varlen(const FwdArgs& a, int d, bool causal, int exp_mode, int variant, hipStream_t stream);
+hipError_t launch_fwd_varlen(const FwdArgs& a, int d, bool causal, int exp_mode, bool pingpong, hipStream_t stream);
 // phases: bit 0 = preprocess (D, LSE log2 e), bit 1 = dK/dV kernel, bit 2 = dQ kernel.
 // 7 runs the whole backward.
 hipError_t launch_bwd(const BwdArgs& a, int d, bool causal, int exp_mode, int phases, hipStream_t stream);

@@ -74,8 +74,9 @@ enum {
 
 /* Forward schedules (attn_options.variant). */
 enum {
-    ATTN_VARIANT_DEFAULT = 0, /* 4-wave workgroups, two per CU                      */
-    ATTN_VARIANT_PINGPONG = 1 /* 8-wave workgroups in two half-step-staggered groups */
+    ATTN_VARIANT_AUTO = 0,     /* the library picks per launch (the default)          */
+    ATTN_VARIANT_PINGPONG = 1, /* 8-wave workgroups in two half-step-staggered groups */
+    ATTN_VARIANT_FOURWAVE = 2  /* 4-wave workgroups, two per CU                      */
 };
 
 /*
@@ -89,15 +90,19 @@ enum {
  *              Technical Edge").  The result is the same for every tau; tau only
  *              bounds the unnormalised probabilities by 2^tau.  tau <= 30.
  *   variant  : forward schedule (the backward has one schedule and ignores it).
- *              ATTN_VARIANT_DEFAULT (0): 4-wave workgroups of 128 queries, two per
+ *              ATTN_VARIANT_FOURWAVE (2): 4-wave workgroups of 128 queries, two per
  *              CU, every wave in the same phase order.  ATTN_VARIANT_PINGPONG (1):
  *              8-wave workgroups of 256 queries, one per CU, whose two 4-wave
  *              halves run half a step apart, so that of the two waves sharing a
  *              SIMD one exponentiates while the other runs matrix products (the
  *              two-team pipelining of the gist.science summary, section 2.A, and
  *              the overlap of "NVIDIA's FlashAttention-4", section "The Technical
- *              Edge").  Both give bit-identical results.  Other values:
- *              ATTN_ERR_UNSUPPORTED.
+ *              Edge").  ATTN_VARIANT_AUTO (0, the default): the ping-pong schedule
+ *              for dense launches with S >= 8192 that give every CU at least one
+ *              256-query workgroup (B * Hq * ceil(S / 256) >= 256), the 4-wave
+ *              schedule otherwise and for packed batches (which measured faster
+ *              each way).  All schedules give bit-identical results, so the choice
+ *              affects speed only.  Other values: ATTN_ERR_UNSUPPORTED.
  */
 typedef struct attn_options {
     int exp_mode;

@@ -39,7 +39,7 @@ def test_python_binding_has_the_c_names():
 def test_default_options():
     o = ea.attn_default_options()
     assert o.exp_mode in (ea.ATTN_EXP_HW, ea.ATTN_EXP_POLY3)
-    assert 0.0 <= o.tau <= 30.0 and o.variant == 0
+    assert 0.0 <= o.tau <= 30.0 and o.variant == ea.ATTN_VARIANT_AUTO
 
 
 def test_status_strings():
@@ -84,7 +84,7 @@ def test_fwd_empty_is_ok_without_launch(kw):
 
 
 @pytest.mark.parametrize("opt,status", [
-    (ea.attn_options(5, 8.0, 0), UNSUP), (ea.attn_options(0, 8.0, 3), UNSUP), (ea.attn_options(0, 8.0, 2), UNSUP), (ea.attn_options(0, 8.0, -1), UNSUP),
+    (ea.attn_options(5, 8.0, 0), UNSUP), (ea.attn_options(0, 8.0, 3), UNSUP), (ea.attn_options(0, 8.0, 4), UNSUP), (ea.attn_options(0, 8.0, -1), UNSUP),
     (ea.attn_options(0, -1.0, 0), VALUE), (ea.attn_options(0, float("nan"), 0), VALUE), (ea.attn_options(1, 31.0, 0), VALUE),
 ])
 def test_fwd_rejects_options(opt, status):

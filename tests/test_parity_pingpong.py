@@ -1,8 +1,9 @@
 """GPU parity of the ping-pong forward schedule (attn_options.variant = 1: 8-wave
 workgroups whose two halves run half a step apart) against the fp64 oracle on edge
-shapes, and bit for bit against the default schedule on every forward workload at full
-size and on packed (variable-length) batches.  The two schedules perform the same
-arithmetic in the same order for every output, so equality is exact.
+shapes, and bit for bit against the four-wave schedule (variant 2) on every forward
+workload at full size and on packed (variable-length) batches; the automatic choice
+(variant 0, the default) equals both.  The schedules perform the same arithmetic in the
+same order for every output, so equality is exact.
 """
 
 import numpy as np
@@ -17,6 +18,7 @@ from helpers import EDGE_REL, assert_bf16_close, assert_lse_close, f64
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
 PP = ea.ATTN_VARIANT_PINGPONG
+FW = ea.ATTN_VARIANT_FOURWAVE
 
 EDGE = [
     # (B, Hq, Hkv, S, d): one tile, ragged tails on both sides of the 256-query workgroup
@@ -37,7 +39,7 @@ def test_pingpong_edge_shapes(case, causal):
     ro, rl = oracle.attention_forward(f64(t["q"]), f64(t["k"]), f64(t["v"]), scale, causal)
     assert_bf16_close("o", o, ro, rel=EDGE_REL)
     assert_lse_close(lse, rl)
-    o0, l0 = ea.attn_fwd_ex(t["q"], t["k"], t["v"], scale, causal)
+    o0, l0 = ea.attn_fwd_ex(t["q"], t["k"], t["v"], scale, causal, variant=FW)
     torch.cuda.synchronize()
     assert torch.equal(o, o0) and torch.equal(lse, l0)
 
@@ -49,20 +51,22 @@ def test_pingpong_options(exp_mode, tau):
     print(f"\n[pingpong options] exp_mode={exp_mode} tau={tau}", flush=True)
     t = {n: x.to(DEV) for n, x in workloads.make_tensors(B, Hq, Hkv, S, d, seed=77).items()}
     o, lse = ea.attn_fwd_ex(t["q"], t["k"], t["v"], d ** -0.5, True, exp_mode=exp_mode, tau=tau, variant=PP)
-    o0, l0 = ea.attn_fwd_ex(t["q"], t["k"], t["v"], d ** -0.5, True, exp_mode=exp_mode, tau=tau)
+    o0, l0 = ea.attn_fwd_ex(t["q"], t["k"], t["v"], d ** -0.5, True, exp_mode=exp_mode, tau=tau, variant=FW)
     torch.cuda.synchronize()
     assert torch.equal(o, o0) and torch.equal(lse, l0)
 
 
 @pytest.mark.parametrize("wn", [1, 2, 3, 5, 6, 7, 8])
-def test_pingpong_equals_default_on_workloads(wn):
+def test_pingpong_equals_fourwave_on_workloads(wn):
     w = workloads.WORKLOADS[wn]
-    print(f"\n[pingpong == default] {w.name}: {w.describe()}", flush=True)
+    print(f"\n[pingpong == fourwave == auto] {w.name}: {w.describe()}", flush=True)
     t = {n: x.to(DEV) for n, x in workloads.make_inputs(w).items() if n in ("q", "k", "v")}
     o, lse = ea.attn_fwd_ex(t["q"], t["k"], t["v"], w.scale, w.causal, variant=PP)
-    o0, l0 = ea.attn_fwd_ex(t["q"], t["k"], t["v"], w.scale, w.causal)
+    o0, l0 = ea.attn_fwd_ex(t["q"], t["k"], t["v"], w.scale, w.causal, variant=FW)
+    oa, la = ea.attn_fwd(t["q"], t["k"], t["v"], w.scale, w.causal)
     torch.cuda.synchronize()
     assert torch.equal(o, o0) and torch.equal(lse, l0)
+    assert torch.equal(oa, o0) and torch.equal(la, l0)
 
 
 @pytest.mark.parametrize("causal", [False, True])
@@ -76,14 +80,15 @@ def test_pingpong_varlen(causal):
     dev = {n: x.to(DEV) for n, x in t.items()}
     total = int(t["q"].shape[0])
     outs = []
-    for variant in (PP, ea.ATTN_VARIANT_DEFAULT):
+    for variant in (PP, FW, ea.ATTN_VARIANT_AUTO):
         o = torch.full((total, Hq, d), 12288.0, dtype=torch.bfloat16, device=DEV)
         lse = torch.full((Hq, total), 12288.0, dtype=torch.float32, device=DEV)
         ea.attn_fwd_varlen(dev["q"], dev["k"], dev["v"], dev["cu_seqlens"], 1000, d ** -0.5, causal, o=o, lse=lse,
                            variant=variant)
         outs.append((o, lse))
     torch.cuda.synchronize()
-    assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1])
+    for other in outs[1:]:
+        assert torch.equal(outs[0][0], other[0]) and torch.equal(outs[0][1], other[1])
     o, lse = outs[0][0].cpu(), outs[0][1].cpu()
     cu = t["cu_seqlens"].tolist()
     a = cu[6]
