@@ -1,0 +1,62 @@
+"""GPU parity on a seeded random sweep of shapes and options against the fp64 oracle.
+
+Each case draws batch, query heads, GQA group size, a ragged sequence length, head size,
+causal or not, the forward schedule (automatic, ping-pong or four-wave) and the rescale
+threshold from a fixed generator, so the sweep is the same on every run.  The forward is
+checked on every element; the backward on the cases small enough for the oracle to finish
+in about a second.  Lengths cross the 64-key tile, the 128- and 256-query workgroups and
+the diagonal at many offsets, which the fixed edge shapes cannot all reach.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import exact_attention_27_amd as ea
+import oracle
+import workloads
+from helpers import EDGE_REL, assert_bf16_close, assert_lse_close, f64
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+VARIANTS = (ea.ATTN_VARIANT_AUTO, ea.ATTN_VARIANT_PINGPONG, ea.ATTN_VARIANT_FOURWAVE)
+
+
+def _cases(n=40, seed=2027):
+    g = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        G = int(g.choice([1, 2, 4, 8]))
+        Hkv = int(g.integers(1, 3))
+        B = int(g.integers(1, 3))
+        S = int(g.integers(1, 2600))
+        d = int(g.choice([64, 128]))
+        causal = bool(g.integers(0, 2))
+        variant = int(VARIANTS[int(g.integers(0, 3))])
+        tau = float(g.choice([0.0, 8.0]))
+        out.append((i, B, Hkv * G, Hkv, S, d, causal, variant, tau))
+    return out
+
+
+CASES = _cases()
+
+
+@pytest.mark.parametrize("case", CASES, ids=lambda c: "%d-B%dHq%dHkv%dS%dd%d-c%d-v%d-t%g" % c)
+def test_sweep(case):
+    i, B, Hq, Hkv, S, d, causal, variant, tau = case
+    print(f"\n[sweep] {case}", flush=True)
+    t = {n: x.to(DEV) for n, x in workloads.make_tensors(B, Hq, Hkv, S, d, seed=500 + i).items()}
+    scale = d ** -0.5
+    o, lse = ea.attn_fwd_ex(t["q"], t["k"], t["v"], scale, causal, tau=tau, variant=variant)
+    torch.cuda.synchronize()
+    ro, rl = oracle.attention_forward(f64(t["q"]), f64(t["k"]), f64(t["v"]), scale, causal)
+    assert_bf16_close("o", o, ro, rel=EDGE_REL)
+    assert_lse_close(lse, rl)
+    if B * Hq * S * S > 6_000_000:
+        return
+    dq, dk, dv = ea.attn_bwd_ex(t["q"], t["k"], t["v"], o, lse, t["do"], scale, causal, tau=tau)
+    torch.cuda.synchronize()
+    rq, rk, rv = oracle.attention_backward(f64(t["q"]), f64(t["k"]), f64(t["v"]), f64(t["do"]), scale, causal)
+    assert_bf16_close("dq", dq, rq, rel=EDGE_REL)
+    assert_bf16_close("dk", dk, rk, rel=EDGE_REL)
+    assert_bf16_close("dv", dv, rv, rel=EDGE_REL)
