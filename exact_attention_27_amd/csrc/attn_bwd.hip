@@ -482,6 +482,11 @@ void bwd_dq_kernel(BwdArgs a) {
   const size_t prow = ((size_t)b * a.Hq + hq) * (size_t)S_pad + qc;
   const float lse2 = a.lse2[prow];
   const float dd = a.delta[prow];
+  // dP^T chains start from -D (every register of a lane belongs to its query), so the
+  // products give dP^T - D directly and dS^T = P^T (dP^T - D) is one multiply.
+  f32x16 negd;
+#pragma unroll
+  for (int v = 0; v < 16; ++v) negd[v] = -dd;
   const float c = a.scale * kLog2e;  // signed: no running maximum is needed here
 
   const int kv_end = CAUSAL ? min(S, q0 + kDqBM) : S;
@@ -562,7 +567,6 @@ void bwd_dq_kernel(BwdArgs a) {
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
       s[kb] = f32x16{};
-      dp[kb] = f32x16{};
     }
     uint32_t dw[2 * KB][4];  // dS^T packed to bf16 pairs: [kb * 2 + t][pair]
     // dS for 8-key block u (registers v = 8t .. 8t+7 of key block kb).
@@ -572,7 +576,7 @@ void bwd_dq_kernel(BwdArgs a) {
       for (int vv = 0; vv < 8; ++vv) {
         if (vv < v0 || vv >= v1) continue;
         const int v = (u & 1) * 8 + vv;
-        const float ds = s[kb][v] * (dp[kb][v] - dd);
+        const float ds = s[kb][v] * dp[kb][v];
         dp[kb][v] = ds;
         if (v & 1) dw[u][(v & 7) >> 1] = pack_bf16x2(dp[kb][v - 1], ds);
       }
@@ -592,7 +596,7 @@ void bwd_dq_kernel(BwdArgs a) {
     for (int i = NA; i < 2 * NA; ++i) {
       issue(i + PD);
       const int k = i - NA, kb = k % KB, ks = k / KB;
-      dp[kb] = mfma32(fr[i], of[ks], dp[kb]);
+      dp[kb] = mfma32(fr[i], of[ks], ks == 0 ? negd : dp[kb]);
       // P^T for a share of the 32 scores, once S^T has had a slot to finish.
       if (k >= 1) {
         const int n = NA - 1, e0 = (k - 1) * 2 * 16 / n, e1 = k * 2 * 16 / n;
