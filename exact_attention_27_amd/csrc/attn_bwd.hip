@@ -5,7 +5,7 @@
 // FlashAttention-4 story; "NVIDIA Blackwell: FlashAttention-4 Overcomes Memory
 // Bottlenecks", body paragraph).  Three launches on the caller's stream:
 //
-//  1. bwd_pre:  D_i = <dO_i, O_i> in fp32 from the stored bf16 O and dO, and LSE_i log2(e),
+//  1. bwd_pre:  -D_i = -<dO_i, O_i> in fp32 from the stored bf16 O and dO, and LSE_i log2(e),
 //               into the workspace.  Bound by HBM bandwidth.
 //  2. bwd_main: dK and dV.  One workgroup per (batch, KV head, tile of 128 keys) keeps dK
 //               and dV for its keys in registers for the whole run and walks the query
@@ -36,9 +36,10 @@ constexpr int kBwdBM = 64;   // queries per step
 
 // ------------------------------------------------------------------ preprocess
 // Rows are taken in the padded layout [B*Hq][S_pad] (S_pad = S rounded up to a multiple
-// of the 64-query step): D_i = <dO_i, O_i> and LSE_i log2(e) go to the workspace there and
-// padding rows get 0.  The main kernel then moves whole 64-row blocks of D and LSE into
-// LDS with no bounds checks; the dQ kernel reads one of each per lane.
+// of the 64-query step): -D_i = -<dO_i, O_i> and LSE_i log2(e) go to the workspace there and
+// padding rows get 0.  The main kernel then moves whole 64-row blocks of -D and LSE into
+// LDS with no bounds checks; the dQ kernel reads one of each per lane.  Both start their
+// dP products from -D, so dS = P (dP - D) is one multiply.
 template <int D>
 __global__ __launch_bounds__(256) void bwd_pre_kernel(const uint16_t* __restrict__ o, const uint16_t* __restrict__ dO,
                                                       const float* __restrict__ lse, float* __restrict__ delta,
@@ -66,7 +67,7 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const uint16_t* __restrict
 #pragma unroll
   for (int off = LPR / 2; off >= 1; off >>= 1) acc += __shfl_xor(acc, off);
   if (prow < prows && part == 0) {
-    delta[prow] = acc;
+    delta[prow] = -acc;  // -D: the dP products start from it
     lse2[prow] = real ? lse[row] * kLog2e : 0.0f;
   }
 }
@@ -260,15 +261,15 @@ void bwd_main_kernel(BwdArgs a) {
         thi[i] = lds_read_tr16((const uint16_t*)(L + tr1 + o));
       }
       if (i < 4) l4[i] = *(const f32x4*)(&sd[qh * 32 + i * 8 + half * 4]);
-      // D is first needed two slots into phase C: read it at the end of phase B, when the
-      // LSE values are nearly dead.
-      if (i >= 2 * KSTEPS - 2 && i < 2 * KSTEPS + 2) {
-        const int g4 = i - (2 * KSTEPS - 2);
+      // -D of the lane's 16 query rows, in the accumulator's register order: the first dP
+      // product takes it as its accumulator input, so the chain ends at dP - D.
+      if (i >= KSTEPS - 4 && i < KSTEPS) {
+        const int g4 = i - (KSTEPS - 4);
         d4[g4] = *(const f32x4*)(&sd[kBwdBM + qh * 32 + g4 * 8 + half * 4]);
       }
     };
 
-    f32x16 sacc = f32x16{}, dpacc = f32x16{};
+    f32x16 sacc = f32x16{}, dpacc;
     uint32_t pw[2][4], sw[2][4];  // P and dS packed to bf16 pairs: [t][pair], registers v = 8t ..
 #pragma unroll
     for (int i = 0; i < PD; ++i) issue(i);
@@ -279,7 +280,13 @@ void bwd_main_kernel(BwdArgs a) {
       if (i < KSTEPS) {
         sacc = mfma32(fa[i], fb[i], sacc);
       } else if (i < 2 * KSTEPS) {
-        dpacc = mfma32(fa[i], fb[i], dpacc);
+        if (i == KSTEPS) {
+          const f32x16 nd = {d4[0][0], d4[0][1], d4[0][2], d4[0][3], d4[1][0], d4[1][1], d4[1][2], d4[1][3],
+                             d4[2][0], d4[2][1], d4[2][2], d4[2][3], d4[3][0], d4[3][1], d4[3][2], d4[3][3]};
+          dpacc = mfma32(fa[i], fb[i], nd);
+        } else {
+          dpacc = mfma32(fa[i], fb[i], dpacc);
+        }
         // P for a share of the 16 registers, once S has had two slots to finish.
         const int j = i - KSTEPS - 2;
         if (j >= 0) {
@@ -307,7 +314,7 @@ void bwd_main_kernel(BwdArgs a) {
 #pragma unroll
           for (int v = 0; v < 16; ++v) {
             if (v < e0 || v >= e1) continue;
-            const float ds = sacc[v] * (dpacc[v] - d4[v >> 2][v & 3]);
+            const float ds = sacc[v] * dpacc[v];
             dpacc[v] = ds;
             if (v & 1) sw[v >> 3][(v & 7) >> 1] = pack_bf16x2(dpacc[v - 1], ds);
           }
@@ -481,12 +488,12 @@ void bwd_dq_kernel(BwdArgs a) {
   }
   const size_t prow = ((size_t)b * a.Hq + hq) * (size_t)S_pad + qc;
   const float lse2 = a.lse2[prow];
-  const float dd = a.delta[prow];
+  const float nd = a.delta[prow];  // -D
   // dP^T chains start from -D (every register of a lane belongs to its query), so the
   // products give dP^T - D directly and dS^T = P^T (dP^T - D) is one multiply.
   f32x16 negd;
 #pragma unroll
-  for (int v = 0; v < 16; ++v) negd[v] = -dd;
+  for (int v = 0; v < 16; ++v) negd[v] = nd;
   const float c = a.scale * kLog2e;  // signed: no running maximum is needed here
 
   const int kv_end = CAUSAL ? min(S, q0 + kDqBM) : S;

@@ -39,7 +39,7 @@ struct BwdArgs {
   uint16_t* dq;
   uint16_t* dk;
   uint16_t* dv;
-  float* delta;   // [B*Hq][S_pad] fp32 workspace: D_i = <dO_i, O_i> (S_pad = S rounded up to 64)
+  float* delta;   // [B*Hq][S_pad] fp32 workspace: -D_i = -<dO_i, O_i> (S_pad = S rounded up to 64)
   float* lse2;    // [B*Hq][S_pad] fp32 workspace: LSE_i * log2(e)
   int B, Hq, Hkv, S;
   float c;        // |scale| * log2(e) (1 for a zero scale)

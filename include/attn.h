@@ -156,8 +156,8 @@ int attn_fwd_varlen(const void* q, const void* k, const void* v, void* o, float*
 
 /*
  * Bytes of device workspace attn_bwd needs for these sizes: two fp32 row arrays
- * [B*Hq][S_pad] (the row terms D_i = <dO_i, O_i> and LSE_i log2(e), S_pad = S rounded
- * up to a multiple of 64), each rounded up to 256 bytes.  Returns 0 for invalid or
+ * [B*Hq][S_pad] (the row terms -D_i = -<dO_i, O_i> and LSE_i log2(e), S_pad = S
+ * rounded up to a multiple of 64), each rounded up to 256 bytes.  Returns 0 for invalid or
  * empty sizes.
  */
 size_t attn_bwd_workspace_bytes(int B, int Hq, int Hkv, int S, int d);
@@ -187,7 +187,7 @@ int attn_bwd_ex(const void* q, const void* k, const void* v, const void* o, cons
  * order on one stream, with the same arguments and workspace, is exactly attn_bwd_ex
  * (ATTN_BWD_ALL); MAIN and DQ are independent of each other.  The phases communicate
  * through the workspace:
- *   PREPROCESS  reads o, dO, lse; writes D = rowsum(dO * O) and LSE log2(e);
+ *   PREPROCESS  reads o, dO, lse; writes -D = -rowsum(dO * O) and LSE log2(e);
  *   MAIN        reads q, k, v, dO, D and LSE log2(e); writes dk, dv;
  *   DQ          reads q, k, v, dO, D and LSE log2(e); writes dq.
  * Arguments are validated as for attn_bwd_ex; an unknown phase is ATTN_ERR_UNSUPPORTED.
