@@ -271,6 +271,9 @@ void fwd_kernel(FwdArgs a) {
   // The first reference maximum is S_0's (O and the row sum are still zero, so nothing
   // needs rescaling).
   m_ref = tile_max(sc);
+  // -m_ref as the exponent offset (0 while m_ref is -inf), kept in its own register: it
+  // changes only when the reference moves.
+  float nmu = m_ref == -INFINITY ? 0.0f : -m_ref;
   __syncthreads();  // every wave has read K_0
   if (nkv > 2) dma_k(2, Kring);
   if (nkv > 1) dma_v(1, Vring + TILE);
@@ -322,18 +325,19 @@ void fwd_kernel(FwdArgs a) {
 #pragma unroll
     for (int i = 0; i < PD; ++i) issue(i);
 
-    float mu = m_ref == -INFINITY ? 0.0f : m_ref;
 
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) nxt[kb] = f32x16{};
     uint32_t pw[KB][2][4];  // P_j packed to bf16 pairs: [key block][16-key half][pair]
-    float lt0 = 0.0f, lt1 = 0.0f;
+    // The row sums start at -0: -0 + p is exactly p for every p, so the first additions
+    // fold away (+0 + p is not an identity in floating point: it maps -0 to +0).
+    float lt0 = -0.0f, lt1 = -0.0f;
     // Exponentials of S_j registers e, e+1 with the reference maximum m_ref, into pw and
     // (lt0, lt1).  Called with compile-time e only (unrolled loops), so pw stays in
     // registers.
     auto exp_pair = [&](const int e) {
-      const float p0 = exp2_sm<EXPMODE>(fmaf(cur[e >> 4][e & 15], c, -mu));
-      const float p1 = exp2_sm<EXPMODE>(fmaf(cur[e >> 4][(e & 15) + 1], c, -mu));
+      const float p0 = exp2_sm<EXPMODE>(fmaf(cur[e >> 4][e & 15], c, nmu));
+      const float p1 = exp2_sm<EXPMODE>(fmaf(cur[e >> 4][(e & 15) + 1], c, nmu));
       lt0 += p0;
       lt1 += p1;
       pw[e >> 4][(e >> 3) & 1][(e & 7) >> 1] = pack_bf16x2(p0, p1);
@@ -367,8 +371,8 @@ void fwd_kernel(FwdArgs a) {
         for (int db = 0; db < DBLK; ++db) oacc[db] *= alpha;
         l_run *= alpha;
         m_ref = m_new;
-        mu = m_ref == -INFINITY ? 0.0f : m_ref;
-        lt0 = lt1 = 0.0f;
+        nmu = m_ref == -INFINITY ? 0.0f : -m_ref;
+        lt0 = lt1 = -0.0f;
 #pragma unroll
         for (int e = 0; e < NE; e += 2) exp_pair(e);
       }
