@@ -117,16 +117,25 @@ def mfma_ceiling():
                      "2 waves per SIMD, after the timed region"}
 
 
+def blas_threads():
+    """(threads, library) of the BLAS numpy uses on this host, as threadpoolctl reports them."""
+    try:
+        from threadpoolctl import threadpool_info
+        info = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+        if info:
+            return max(i.get("num_threads", 1) for i in info), \
+                "/".join(sorted({f"{i.get('internal_api')} {i.get('version')}" for i in info}))
+    except Exception:  # noqa: BLE001
+        pass
+    return os.cpu_count() or 1, "unknown"
+
+
 def cpu_baseline(w, inputs, target_s):
     """The fp64 oracle (fwd + bwd of one (batch, query head) pair at a time, at the
     workload's full S) on this host, until about target_s seconds have passed."""
     import numpy as np
     import oracle
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
-    except Exception:  # noqa: BLE001
-        threads = os.cpu_count() or 1
+    threads, blas = blas_threads()
     x = {n: inputs[n] for n in ("q", "k", "v", "do")}
     heads, flop, t0 = 0, 0.0, time.perf_counter()
     per_head_fwd = w.fwd_flop() / (w.B * w.Hq)
@@ -150,7 +159,7 @@ def cpu_baseline(w, inputs, target_s):
             break
     dt = time.perf_counter() - t0
     return {
-        "value": flop / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+        "value": flop / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "blas": blas, "kind": "oracle",
         "sample": f"fp64 numpy oracle, {'fwd+bwd' if do_bwd else 'fwd'} of {heads} of {w.B * w.Hq} "
                   f"(batch, query head) pairs at full S={w.S}, d={w.d}, {dt:.1f} s; algorithmic flop",
     }
@@ -161,11 +170,7 @@ def cpu_baseline_varlen(w, inputs, target_s):
     packed order, until about target_s seconds have passed."""
     import numpy as np
     import oracle
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
-    except Exception:  # noqa: BLE001
-        threads = os.cpu_count() or 1
+    threads, blas = blas_threads()
     cu = inputs["cu_seqlens"].tolist()
     pairs, toks, flop, t0 = 0, 0, 0.0, time.perf_counter()
     done = False
@@ -185,7 +190,7 @@ def cpu_baseline_varlen(w, inputs, target_s):
             break
     dt = time.perf_counter() - t0
     return {
-        "value": flop / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+        "value": flop / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "blas": blas, "kind": "oracle",
         "sample": f"fp64 numpy oracle, fwd of {pairs} of {w.n * w.Hq} (sequence, query head) pairs "
                   f"({toks} query rows) of the packed batch, d={w.d}, {dt:.1f} s; algorithmic flop",
     }
