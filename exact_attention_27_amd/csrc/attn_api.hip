@@ -28,6 +28,9 @@ int check_sizes(int B, int Hq, int Hkv, int S, int d, bool* empty) {
   const int64_t tiles = ((int64_t)S + 127) / 128;
   if ((int64_t)B * Hq * tiles >= (int64_t)1 << 31) return ATTN_ERR_SHAPE;
   if ((int64_t)S * d >= (int64_t)1 << 31) return ATTN_ERR_SHAPE;
+  // The backward preprocess runs one thread per 8 elements of each padded row.
+  const int64_t pre_blocks = ((int64_t)B * Hq * ((S + 63) / 64 * 64) * (d / 8) + 255) / 256;
+  if (pre_blocks >= (int64_t)1 << 31) return ATTN_ERR_SHAPE;
   *empty = (B == 0 || S == 0);
   return ATTN_OK;
 }

@@ -91,6 +91,15 @@ def test_fwd_rejects_options(opt, status):
     assert fwd(opt=opt) == status
 
 
+def test_grid_limits():
+    """Sizes whose launch grids would not fit in 31 bits are rejected before any launch
+    (one passes every other limit but the backward preprocess grid)."""
+    assert ea.attn_bwd_workspace_bytes(1, 1 << 14, 1, 1 << 21, 128) == 0
+    assert fwd(B=1, Hq=1 << 14, Hkv=1, S=1 << 21, d=128) == SHAPE
+    assert fwd(B=1 << 20, Hq=1 << 10, Hkv=1, S=1 << 8, d=64) == SHAPE
+    assert ea.attn_bwd_workspace_bytes(1, 1 << 13, 1, 1 << 21, 128) > 0
+
+
 def test_workspace_bytes():
     B, Hq, Hkv, S, d = 2, 4, 2, 100, 128
     rup = lambda x: (x + 255) // 256 * 256
