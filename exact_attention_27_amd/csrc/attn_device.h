@@ -37,20 +37,22 @@ constexpr float kLn2 = 0.6931471805599453f;
 //    describe ("NVIDIA's FlashAttention-4", section "The Technical Edge": cubic
 //    polynomials on ordinary cores instead of the special-function units; gist.science
 //    summary, section 2.B).  The pages give no coefficients or range, so this one is
-//    derived here: x is clamped to >= -127, split as x = n + f with n = round(x)
+//    derived here: x is clamped to [-127, 64], split as x = n + f with n = round(x)
 //    (the 1.5 * 2^23 addition trick) and f in [-1/2, 1/2]; 2^f is a degree-3
 //    polynomial with p(0) = 1 whose coefficients minimise the maximum relative error
 //    on [-1/2, 1/2] (a linear-programming minimax fit, fit_exp2_poly.py beside this
 //    file); 2^n is applied by adding n to the exponent field.  Max relative error
 //    1.02e-4 over the whole range, far below bf16's half-ulp (2^-9), and exactly
-//    2^0 = 1 and 2^-inf = 0.  Valid for x <= 64 (the kernels feed x <= tau <= 30).
+//    2^0 = 1 and 2^-inf = 0.  Arguments above 64 (and +inf) give 2^64: the forward
+//    exponentiates a tile before its rescale test, which only needs such values to be
+//    large (without the clamp the exponent add would overflow into the sign bit).
 // ---------------------------------------------------------------------------------
 constexpr float kExp2C1 = 0x1.62f5fap-1f;
 constexpr float kExp2C2 = 0x1.f00c4cp-3f;
 constexpr float kExp2C3 = 0x1.c2a216p-5f;
 
 __host__ __device__ inline float exp2_poly3(float x) {
-  x = fmaxf(x, -127.0f);
+  x = fminf(fmaxf(x, -127.0f), 64.0f);
   const float t = x + 12582912.0f;  // 1.5 * 2^23: rounds x to an integer in the low mantissa bits
   const float n = t - 12582912.0f;
   const float f = x - n;

@@ -52,10 +52,10 @@
 namespace attn {
 namespace {
 
-constexpr int kFwdBN = 64;                // keys per LDS tile
-#ifndef FWD_PD
-#define FWD_PD 2                          // slots between an LDS read and its product
-#endif
+constexpr int kFwdBN = 64;  // keys per LDS tile
+// Slots between an LDS read and the product that uses it: two hide the read latency
+// behind the two products in between; three or four measured slower on both schedules.
+constexpr int kFwdPD = 2;
 
 // VARLEN: a packed batch of sequences of different lengths (FwdArgs::cu_seqlens), with
 // token-major rows (row stride H*d instead of d); otherwise the dense [B, H, S, d] layout.
@@ -78,7 +78,7 @@ void fwd_kernel(FwdArgs a) {
   constexpr int NPV = 2 * KB * DBLK;    // phase-2 slots (products of O^T)
   constexpr int NE = KB * 16;           // scores per lane per tile
   constexpr int EPS = NE / NQK;         // exponentials per phase-1 slot
-  constexpr int PD = FWD_PD;
+  constexpr int PD = kFwdPD;
   static_assert(NE % NQK == 0 && EPS % 2 == 0, "exponentials must pair up per slot");
   static_assert(BN % 32 == 0 && DMAS * 64 * W == BN * CPR, "tile must split evenly over the threads");
   constexpr int VR = W == 8 ? 3 : 2;    // V ring slots (the K ring has 2)

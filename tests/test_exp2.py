@@ -30,6 +30,14 @@ def test_poly_special_values():
     assert y[4] == 2.0 and y[5] == 256.0 and y[6] == 0.5  # integers are exact: p(0) = 1
 
 
+def test_poly_large_arguments_saturate():
+    """Arguments above 64 (up to +inf) give 2^64: large enough for the forward's rescale
+    test, which sees a tile's exponentials before deciding to rescale."""
+    x = np.array([64.0, 64.5, 100.0, 127.0, 128.0, 200.0, 1000.0, 1e30, np.inf], dtype=np.float32)
+    y = ea.attn_exp2_poly_host(x)
+    assert (y == 2.0 ** 64).all(), y
+
+
 def test_poly_tiny_results_are_tiny():
     x = np.linspace(-127.0, -125.0, 2001).astype(np.float32)
     y = ea.attn_exp2_poly_host(x)

@@ -67,6 +67,29 @@ def test_fwd_options(exp_mode, tau, causal):
     assert_lse_close(lse, rlse)
 
 
+@pytest.mark.parametrize("variant", [ea.ATTN_VARIANT_FOURWAVE, ea.ATTN_VARIANT_PINGPONG])
+@pytest.mark.parametrize("exp_mode", [ea.ATTN_EXP_HW, ea.ATTN_EXP_POLY3])
+@pytest.mark.parametrize("causal", [False, True])
+def test_fwd_huge_score_jump(causal, exp_mode, variant):
+    """Keys 0..63 score 0 and every later key scores 200 (about 288 in log2 units): the
+    second tile is exponentiated against a reference 288 below its maximum before the
+    rescale test sees it, so both exponentials must make that test fire (the cubic
+    saturates at 2^64 rather than wrapping)."""
+    B, Hq, Hkv, S, d = 1, 2, 1, 300, 64
+    print(f"\n[fwd jump] causal={causal} exp_mode={exp_mode} variant={variant}", flush=True)
+    t = inputs(B, Hq, Hkv, S, d, seed=13)
+    q = torch.zeros(B, Hq, S, d, dtype=torch.bfloat16, device=DEV)
+    k = torch.zeros(B, Hkv, S, d, dtype=torch.bfloat16, device=DEV)
+    q[..., 0] = 40.0
+    k[:, :, 64:, 0] = 40.0
+    t["q"], t["k"] = q, k
+    o, lse = ea.attn_fwd_ex(t["q"], t["k"], t["v"], d ** -0.5, causal, exp_mode=exp_mode, tau=8.0, variant=variant)
+    torch.cuda.synchronize()
+    ro, rlse = oracle_fwd(t, d ** -0.5, causal)
+    assert_bf16_close("o", o, ro, rel=EDGE_REL)
+    assert_lse_close(lse, rlse)
+
+
 @pytest.mark.parametrize("tau", [0.0, 8.0])
 def test_fwd_rescale_with_growing_scores(tau):
     """Scores that grow along the keys force the running maximum up on every tile:
