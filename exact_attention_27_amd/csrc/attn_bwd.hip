@@ -294,7 +294,7 @@ void bwd_main_kernel(BwdArgs a) {
 #pragma unroll
           for (int v = 0; v < 16; ++v) {
             if (v < e0 || v >= e1) continue;
-            float p = exp2_sm<EXPMODE>(fmaf(sacc[v], c, -l4[v >> 2][v & 3]));
+            float p = exp2_sm<EXPMODE, false>(fmaf(sacc[v], c, -l4[v >> 2][v & 3]));
             if constexpr (MASKED) {
               const int ev = (v >> 2) * 8 + (v & 3);
               p = (ev < lim_c || ev >= lim_s) ? 0.0f : p;
@@ -610,7 +610,7 @@ void bwd_dq_kernel(BwdArgs a) {
 #pragma unroll
         for (int e = 0; e < 2 * 16; ++e) {
           if (e < e0 || e >= e1) continue;
-          float p = exp2_sm<EXPMODE>(fmaf(s[e >> 4][e & 15], c, -lse2));
+          float p = exp2_sm<EXPMODE, false>(fmaf(s[e >> 4][e & 15], c, -lse2));
           if constexpr (MASKED) {
             const int ek = (e >> 4) * 32 + ((e & 15) >> 2) * 8 + (e & 3);  // key - k0 - half*4
             p = ek > lim ? 0.0f : p;

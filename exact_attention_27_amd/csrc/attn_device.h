@@ -51,8 +51,14 @@ constexpr float kExp2C1 = 0x1.62f5fap-1f;
 constexpr float kExp2C2 = 0x1.f00c4cp-3f;
 constexpr float kExp2C3 = 0x1.c2a216p-5f;
 
+// HIGH: clamp the argument above at 64 as well as below at -127.  Without the upper clamp
+// the result is still right for every x < 128 (2^127 is the largest power the exponent
+// field holds); the backward's arguments, s * c - LSE * log2(e) with the forward's LSE,
+// never exceed a few ulps above 0, so it skips that clamp and the register it costs.
+template <bool HIGH = true>
 __host__ __device__ inline float exp2_poly3(float x) {
-  x = fminf(fmaxf(x, -127.0f), 64.0f);
+  x = fmaxf(x, -127.0f);
+  if constexpr (HIGH) x = fminf(x, 64.0f);
   const float t = x + 12582912.0f;  // 1.5 * 2^23: rounds x to an integer in the low mantissa bits
   const float n = t - 12582912.0f;
   const float f = x - n;
@@ -61,12 +67,12 @@ __host__ __device__ inline float exp2_poly3(float x) {
   return __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, p) + (ti << 23));
 }
 
-template <int EXPMODE>
+template <int EXPMODE, bool HIGH = true>
 __device__ __forceinline__ float exp2_sm(float x) {
   if constexpr (EXPMODE == 0) {
     return __builtin_amdgcn_exp2f(x);
   } else {
-    return exp2_poly3(x);
+    return exp2_poly3<HIGH>(x);
   }
 }
 
