@@ -208,8 +208,11 @@ const char* attn_status_string(int status);
 
 /*
  * Evaluate the softmax's exp2 on the device, y[i] = 2^x[i] for i < n, with the
- * given exp_mode, exactly as the kernels do (device pointers x, y; n >= 0).
- * For testing the polynomial and the hardware instruction in isolation.
+ * given exp_mode, exactly as the forward does (device pointers x, y; n >= 0).
+ * For testing the polynomial and the hardware instruction in isolation.  The
+ * polynomial clamps x to [-127, 64]: below -127 it gives 0, above 64 it gives
+ * 2^64 (the backward, whose arguments stay near or below 0, omits the upper
+ * clamp).
  */
 int attn_exp2_eval(const float* x, float* y, long n, int exp_mode, void* stream);
 
