@@ -168,10 +168,17 @@ void bwd_main_kernel(BwdArgs a) {
   }
   // Step order: query tiles from the last one down, the group's heads innermost, so the
   // workgroups of one (batch, KV head), which share an XCD when B*Hkv is a multiple of
-  // 8, read the same Q/dO rows at about the same time.
-  auto stage_in = [&](int step, int st) {
-    const int g = step % G;
-    const int qt = nqt - 1 - step / G;
+  // 8, read the same Q/dO rows at about the same time.  Steps are staged in order, so the
+  // (head, query tile) of the next one is a pair of counters rather than a division per
+  // step (scalar work that every wave of the CU repeats right after the barrier).
+  int stage_g = 0, stage_qt = nqt - 1;
+  auto stage_in = [&](int st) {
+    const int g = stage_g;
+    const int qt = stage_qt;
+    if (++stage_g == G) {
+      stage_g = 0;
+      --stage_qt;
+    }
     const int hq = hkv * G + g;
     const size_t rbase = ((size_t)b * a.Hq + hq) * (size_t)S;
     const int q0 = qt * kBwdBM;
@@ -328,12 +335,17 @@ void bwd_main_kernel(BwdArgs a) {
     }
   };
 
+  int step_g = 0, step_qt = nqt - 1;  // query tile of the step being computed, as above
   auto do_step = [&](const int step, auto stage) {
     constexpr int ST = decltype(stage)::value;
     wait_dma();
     __syncthreads();  // this step's Q, dO, LSE, D are in LDS; every wave is done with the previous stage
-    if (step + 1 < steps) stage_in(step + 1, ST ^ 1);
-    const int qt = nqt - 1 - step / G;
+    if (step + 1 < steps) stage_in(ST ^ 1);
+    const int qt = step_qt;
+    if (++step_g == G) {
+      step_g = 0;
+      --step_qt;
+    }
     const int q0 = qt * kBwdBM;
     const int qs = q0 + qh * 32;  // first query of this wave's half
     if (!CAUSAL || kw <= qs + 31) {
@@ -346,7 +358,7 @@ void bwd_main_kernel(BwdArgs a) {
     }
   };
 
-  if (steps > 0) stage_in(0, 0);
+  if (steps > 0) stage_in(0);
   for (int step = 0; step < steps; step += 2) {
     do_step(step, std::integral_constant<int, 0>{});
     if (step + 1 < steps) do_step(step + 1, std::integral_constant<int, 1>{});
