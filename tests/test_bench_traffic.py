@@ -1,5 +1,6 @@
-"""bench.py's roofline.traffic comes from counter records committed under profiles/; it must
-be reported only while the measured kernel's sources are unchanged (CPU only)."""
+"""bench.py on the CPU: roofline.traffic comes from counter records committed under
+profiles/ and must be reported only while the measured kernel's sources are unchanged; a
+run asked for more than one GPU is refused."""
 
 import json
 import os
@@ -57,3 +58,16 @@ def test_mfma_ceiling_probe_is_optional_without_a_gpu():
     if torch.cuda.is_available():
         pytest.skip("a GPU is present: the probe would run")
     assert bench.mfma_ceiling() is None
+
+
+@pytest.mark.parametrize("n", [2, 8])
+def test_more_than_one_gpu_is_refused(n):
+    """One GPU is the scope: --gpus above 1 exits with status 2 and says so, before any GPU
+    work (this runs without one)."""
+    import subprocess
+    import sys
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", str(n)],
+                       capture_output=True, text=True, timeout=120, cwd=ROOT)
+    assert r.returncode == 2
+    assert "one GPU only" in (r.stdout + r.stderr)
+    assert '"metric"' not in r.stdout
