@@ -131,6 +131,37 @@ def test_brute_force_forward(causal, S):
     np.testing.assert_allclose(lse, blse, rtol=0, atol=1e-12)
 
 
+@pytest.mark.parametrize("causal", [False, True])
+def test_sampled_rows_match_brute_force(causal):
+    """head_forward(rows=r) evaluates only the requested query positions; each of them
+    must be what the pure-Python definition gives for that query (its causal mask is
+    keyed on the query's position, not on its index within r)."""
+    S, d, scale = 16, 4, 0.5
+    q, k, v = rnd((S, d), 41), rnd((S, d), 42), rnd((S, d), 43)
+    rows = np.array([13, 2, 15, 0, 7, 7, 9])  # unsorted, with a repeat
+    o, lse = oracle.head_forward(q, k, v, scale, causal, rows=rows)
+    bo, blse = brute_forward(q.tolist(), k.tolist(), v.tolist(), scale, causal)
+    np.testing.assert_allclose(o, bo[rows], rtol=0, atol=1e-12)
+    np.testing.assert_allclose(lse, blse[rows], rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_sampled_rows_across_row_blocks(causal, monkeypatch):
+    """Sparse, unsorted rows spread over several row blocks give the same values as the
+    full evaluation at those rows (row blocks of 64 here, so the sample crosses many)."""
+    monkeypatch.setattr(oa, "ROW_BLOCK", 64)
+    S, d, scale = 700, 8, 0.3
+    q, k, v = rnd((S, d), 44), rnd((S, d), 45), rnd((S, d), 46)
+    rows = np.random.default_rng(47).permutation(S)[:150]
+    rows = np.concatenate([rows, [0, S - 1, 63, 64, 65]])
+    o, lse = oracle.head_forward(q, k, v, scale, causal, rows=rows)
+    fo, flse = oracle.head_forward(q, k, v, scale, causal)
+    np.testing.assert_allclose(o, fo[rows], rtol=0, atol=1e-13)
+    np.testing.assert_allclose(lse, flse[rows], rtol=0, atol=1e-13)
+    if causal:  # row 0 sees key 0 only, wherever it sits in the sample
+        np.testing.assert_array_equal(o[rows == 0][0], v[0])
+
+
 # ---------------------------------------------------------- finite differences
 
 def loss(q, k, v, do, scale, causal):
@@ -271,6 +302,14 @@ def _mut_softmax_log2(s):
     return e / l, (m + np.log2(l))[:, 0]
 
 
+def _mut_head_forward_local_rows(q, k, v, scale, causal, rows=None):
+    """Sampled rows masked by their index in the sample instead of their position."""
+    q, k, v = (np.asarray(x, dtype=np.float64) for x in (q, k, v))
+    rows = np.arange(q.shape[0]) if rows is None else np.asarray(rows, dtype=np.int64)
+    p, lse = oa._softmax_rows(oa._scores(q[rows], k, np.arange(rows.shape[0]), scale, causal))
+    return p @ v, lse
+
+
 def _mut_backward(kind):
     def head_backward(q, k, v, do, scale, causal):
         q, k, v, do = (np.asarray(x, dtype=np.float64) for x in (q, k, v, do))
@@ -294,6 +333,7 @@ def _pins_pass():
         lambda: test_uniform_scores_give_mean_of_v(True, 1),
         lambda: test_rows_sum_to_one_and_lse_matches_fsum(True),
         lambda: test_brute_force_forward(True, 9),
+        lambda: test_sampled_rows_match_brute_force(True),
         lambda: test_finite_difference_gradients(True, 1),
         lambda: test_finite_difference_gradients(False, 2),
     ]
@@ -313,16 +353,17 @@ def test_pins_pass_on_the_oracle():
     ("_scores", _mut_scores_excluding_diagonal),
     ("_scores", _mut_scores_transposed_mask),
     ("_softmax_rows", _mut_softmax_log2),
+    ("head_forward", _mut_head_forward_local_rows),
     ("head_backward", _mut_backward("dropped_D")),
     ("head_backward", _mut_backward("dq_unscaled")),
     ("head_backward", _mut_backward("dk_uses_k")),
     ("head_backward", _mut_backward("dv_transposed")),
-], ids=["diag_excluded", "mask_transposed", "lse_log2", "dropped_D", "dq_unscaled", "dk_uses_k", "dv_transposed"])
+], ids=["diag_excluded", "mask_transposed", "lse_log2", "rows_masked_by_sample_index", "dropped_D", "dq_unscaled", "dk_uses_k", "dv_transposed"])
 def test_pins_catch_planted_mistake(monkeypatch, mutant):
     name, fn = mutant
     monkeypatch.setattr(oa, name, fn)
-    if name == "head_backward":
-        monkeypatch.setattr(oracle, "head_backward", fn)
+    if name in ("head_backward", "head_forward"):
+        monkeypatch.setattr(oracle, name, fn)
     assert not _pins_pass()
 
 
