@@ -309,7 +309,7 @@ def main():
         if ev:
             ev[1].record(stream)
         if do_bwd:
-            for ph, e in ((ea.ATTN_BWD_PREPROCESS, 2), (ea.ATTN_BWD_MAIN, 3), (ea.ATTN_BWD_DQ, 4)):
+            for ph, e in ((ea.ATTN_BWD_PREPROCESS, 2), (ea.ATTN_BWD_DQ, 3), (ea.ATTN_BWD_MAIN, 4)):
                 ea.attn_bwd_phase(ph, q, k, v, o, lse, do, w.scale, w.causal, dq, dk, dv, ws, opt=opt, stream=stream)
                 if ev:
                     ev[e].record(stream)
@@ -338,8 +338,8 @@ def main():
     phase_ms = {}
     if do_bwd:
         phase_ms["bwd_pre"] = sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps
-        phase_ms["bwd_main"] = sum(e[2].elapsed_time(e[3]) for e in evs) / args.steps
-        phase_ms["bwd_dq"] = sum(e[3].elapsed_time(e[4]) for e in evs) / args.steps
+        phase_ms["bwd_dq"] = sum(e[2].elapsed_time(e[3]) for e in evs) / args.steps
+        phase_ms["bwd_main"] = sum(e[3].elapsed_time(e[4]) for e in evs) / args.steps
     fwd_tf = w.fwd_flop() / (fwd_ms * 1e-3) / 1e12
     flop = w.fwd_flop() + (w.bwd_flop() if do_bwd else 0.0)
     value = flop / (ms_step * 1e-3) / 1e12

@@ -28,9 +28,8 @@ int check_sizes(int B, int Hq, int Hkv, int S, int d, bool* empty) {
   const int64_t tiles = ((int64_t)S + 127) / 128;
   if ((int64_t)B * Hq * tiles >= (int64_t)1 << 31) return ATTN_ERR_SHAPE;
   if ((int64_t)S * d >= (int64_t)1 << 31) return ATTN_ERR_SHAPE;
-  // The backward preprocess runs one thread per 8 elements of each padded row.
-  const int64_t pre_blocks = ((int64_t)B * Hq * ((S + 63) / 64 * 64) * (d / 8) + 255) / 256;
-  if (pre_blocks >= (int64_t)1 << 31) return ATTN_ERR_SHAPE;
+  // The backward preprocess launches 32 workgroups per (batch, KV head).
+  if ((int64_t)B * Hkv * 32 >= (int64_t)1 << 31) return ATTN_ERR_SHAPE;
   *empty = (B == 0 || S == 0);
   return ATTN_OK;
 }
@@ -66,6 +65,27 @@ int hip_status(hipError_t e) { return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP; 
 bool use_pingpong(int variant, bool packed, int B, int Hq, int S) {
   if (variant != ATTN_VARIANT_AUTO) return variant == ATTN_VARIANT_PINGPONG;
   return !packed && S >= 8192 && (int64_t)B * Hq * ((S + 255) / 256) >= 256;
+}
+
+// Backward workspace, in order, each part aligned to 256 bytes (S_pad = S rounded up to
+// 64): -D from the bf16 O, LSE log2(e), the exact -D in the dK/dV kernel's units (three fp32
+// [B*Hq][S_pad] arrays), the preprocess's partial maxima (fp32 [B*Hkv][32][4]), and dO and
+// Q in fp16 (two [B*Hq][S][d] arrays).
+struct BwdWorkspace {
+  size_t delta, lse2, ndx, pmax, do16, q16, total;
+};
+
+BwdWorkspace bwd_workspace(int B, int Hq, int Hkv, int S, int d) {
+  const size_t prows = (size_t)B * Hq * (((size_t)S + 63) / 64 * 64);
+  BwdWorkspace w;
+  w.delta = 0;
+  w.lse2 = w.delta + round_up(prows * sizeof(float));
+  w.ndx = w.lse2 + round_up(prows * sizeof(float));
+  w.pmax = w.ndx + round_up(prows * sizeof(float));
+  w.do16 = w.pmax + round_up((size_t)B * Hkv * 32 * 4 * sizeof(float));
+  w.q16 = w.do16 + round_up((size_t)B * Hq * S * d * sizeof(uint16_t));
+  w.total = w.q16 + round_up((size_t)B * Hq * S * d * sizeof(uint16_t));
+  return w;
 }
 
 }  // namespace
@@ -166,11 +186,11 @@ int attn_fwd_varlen(const void* q, const void* k, const void* v, void* o, float*
                                             static_cast<hipStream_t>(stream)));
 }
 
+
 size_t attn_bwd_workspace_bytes(int B, int Hq, int Hkv, int S, int d) {
   bool empty = false;
   if (check_sizes(B, Hq, Hkv, S, d, &empty) != ATTN_OK || empty) return 0;
-  const size_t prows = (size_t)B * Hq * (((size_t)S + 63) / 64 * 64);
-  return 2 * round_up(prows * sizeof(float));
+  return bwd_workspace(B, Hq, Hkv, S, d).total;
 }
 
 int attn_bwd_phase(int phase, const void* q, const void* k, const void* v, const void* o, const float* lse,
@@ -210,9 +230,14 @@ int attn_bwd_phase(int phase, const void* q, const void* k, const void* v, const
   a.dq = static_cast<uint16_t*>(dq);
   a.dk = static_cast<uint16_t*>(dk);
   a.dv = static_cast<uint16_t*>(dv);
-  const size_t prows = (size_t)B * Hq * (((size_t)S + 63) / 64 * 64);
-  a.delta = static_cast<float*>(workspace);
-  a.lse2 = reinterpret_cast<float*>(static_cast<char*>(workspace) + round_up(prows * sizeof(float)));
+  const BwdWorkspace wl = bwd_workspace(B, Hq, Hkv, S, d);
+  char* ws = static_cast<char*>(workspace);
+  a.delta = reinterpret_cast<float*>(ws + wl.delta);
+  a.lse2 = reinterpret_cast<float*>(ws + wl.lse2);
+  a.ndx = reinterpret_cast<float*>(ws + wl.ndx);
+  a.pmax = reinterpret_cast<float*>(ws + wl.pmax);
+  a.do16 = reinterpret_cast<uint16_t*>(ws + wl.do16);
+  a.q16 = reinterpret_cast<uint16_t*>(ws + wl.q16);
   a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.S = S;
   a.scale = scale;
   scale_setup(scale, &a.c, &a.q_and, &a.q_xor);

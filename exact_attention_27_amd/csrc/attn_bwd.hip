@@ -33,43 +33,160 @@ namespace {
 
 constexpr int kBwdBN = 128;  // keys per workgroup (4 waves x 32)
 constexpr int kBwdBM = 64;   // queries per step
+constexpr int kPreBlocks = 32;  // preprocess workgroups per KV group (partial maxima per group)
 
 // ------------------------------------------------------------------ preprocess
 // Rows are taken in the padded layout [B*Hq][S_pad] (S_pad = S rounded up to a multiple
 // of the 64-query step): -D_i = -<dO_i, O_i> and LSE_i log2(e) go to the workspace there and
-// padding rows get 0.  The main kernel then moves whole 64-row blocks of -D and LSE into
-// LDS with no bounds checks; the dQ kernel reads one of each per lane.  Both start their
-// dP products from -D, so dS = P (dP - D) is one multiply.
-template <int D>
-__global__ __launch_bounds__(256) void bwd_pre_kernel(const uint16_t* __restrict__ o, const uint16_t* __restrict__ dO,
-                                                      const float* __restrict__ lse, float* __restrict__ delta,
-                                                      float* __restrict__ lse2, long prows, int S, int S_pad) {
-  constexpr int LPR = D / 8;  // lanes per row, 8 bf16 each
-  const long gid = (long)blockIdx.x * 256 + threadIdx.x;
-  const long prow = gid / LPR;
-  const int part = (int)(gid % LPR);
-  const long bhr = prow / S_pad;
-  const int srow = (int)(prow - bhr * S_pad);
-  const bool real = prow < prows && srow < S;
-  const long row = bhr * S + srow;  // row in the unpadded [B*Hq][S] tensors
-  float acc = 0.0f;
-  if (real) {
-    const u32x4 ov = *(const u32x4*)(o + row * D + part * 8);
-    const u32x4 dv = *(const u32x4*)(dO + row * D + part * 8);
+// padding rows get 0.  The dQ kernel reads one of each per lane and starts its dP
+// products from -D, so dS = P (dP - D) is one multiply.
+//
+// The launch is kPreBlocks workgroups per KV group (b, hkv): workgroup nb takes an equal
+// share of the group's G * S_pad padded rows of O, dO and Q and of its S rows of K and V,
+// and writes the largest |dO|, |V|, |Q| and |K| it saw to pmax[group][nb][0..3] (no
+// atomics, so nothing needs clearing beforehand).  The later kernels reduce those to the
+// power-of-two scales that put the group's operands into fp16 exactly (fp16_exponent).
+constexpr int kMaxDO = 0, kMaxV = 1, kMaxQ = 2, kMaxK = 3, kMaxes = 4;
+
+__device__ __forceinline__ float absmax8(float m, const u32x4& w) {
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const float o0 = __builtin_bit_cast(float, ov[e] << 16), o1 = __builtin_bit_cast(float, ov[e] & 0xffff0000u);
-      const float d0 = __builtin_bit_cast(float, dv[e] << 16), d1 = __builtin_bit_cast(float, dv[e] & 0xffff0000u);
-      acc = fmaf(o0, d0, acc);
-      acc = fmaf(o1, d1, acc);
+  for (int e = 0; e < 4; ++e)
+    m = fmaxf(m, fmaxf(fabsf(__builtin_bit_cast(float, w[e] << 16)), fabsf(__builtin_bit_cast(float, w[e] & 0xffff0000u))));
+  return m;
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void bwd_pre_kernel(BwdArgs a, int S_pad) {
+  constexpr int LPR = D / 8;     // lanes per row, 8 bf16 each
+  constexpr int RPI = 256 / LPR;  // rows per pass of the workgroup
+  const int tid = threadIdx.x;
+  const int part = tid % LPR;
+  const int G = a.Hq / a.Hkv;
+  const int grp = blockIdx.x / kPreBlocks;  // b * Hkv + hkv
+  const int nb = blockIdx.x - grp * kPreBlocks;
+  const int b = grp / a.Hkv;
+  const int hkv = grp - b * a.Hkv;
+  const int S = a.S;
+
+  // O, dO, Q: the group's padded rows [row0, row0 + G * S_pad), this workgroup's share.
+  const long row0 = ((long)b * a.Hq + (long)hkv * G) * S_pad;
+  const long nrows = (long)G * S_pad;
+  const long per = ((nrows + kPreBlocks - 1) / kPreBlocks + RPI - 1) / RPI * RPI;
+  const long r_end = min(nrows, (nb + 1) * per);
+  float mdo = 0.0f, mq = 0.0f;
+  for (long r0 = nb * per; r0 < r_end; r0 += RPI) {
+    const long r = r0 + tid / LPR;  // group-relative padded row
+    const int hl = (int)(r / S_pad);
+    const int srow = (int)(r - (long)hl * S_pad);
+    const bool real = r < r_end && srow < S;
+    const long row = ((long)b * a.Hq + (long)hkv * G + hl) * S + srow;  // unpadded [B*Hq][S] row
+    float acc = 0.0f;
+    if (real) {
+      const u32x4 ov = *(const u32x4*)(a.o + row * D + part * 8);
+      const u32x4 dv = *(const u32x4*)(a.dO + row * D + part * 8);
+      const u32x4 qv = *(const u32x4*)(a.q + row * D + part * 8);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float o0 = __builtin_bit_cast(float, ov[e] << 16), o1 = __builtin_bit_cast(float, ov[e] & 0xffff0000u);
+        const float d0 = __builtin_bit_cast(float, dv[e] << 16), d1 = __builtin_bit_cast(float, dv[e] & 0xffff0000u);
+        acc = fmaf(o0, d0, acc);
+        acc = fmaf(o1, d1, acc);
+      }
+      mdo = absmax8(mdo, dv);
+      mq = absmax8(mq, qv);
+    }
+#pragma unroll
+    for (int off = LPR / 2; off >= 1; off >>= 1) acc += __shfl_xor(acc, off);
+    if (r < r_end && part == 0) {
+      a.delta[row0 + r] = -acc;  // -D: the dQ kernel's dP products start from it
+      a.lse2[row0 + r] = real ? a.lse[row] * kLog2e : 0.0f;
     }
   }
-#pragma unroll
-  for (int off = LPR / 2; off >= 1; off >>= 1) acc += __shfl_xor(acc, off);
-  if (prow < prows && part == 0) {
-    delta[prow] = -acc;  // -D: the dP products start from it
-    lse2[prow] = real ? lse[row] * kLog2e : 0.0f;
+  // K, V: the group's S rows, this workgroup's share.
+  const long vper = (((long)S + kPreBlocks - 1) / kPreBlocks + RPI - 1) / RPI * RPI;
+  const long v_end = min((long)S, (nb + 1) * vper);
+  const size_t kvb = (size_t)grp * S * D;
+  float mv = 0.0f, mk = 0.0f;
+  for (long r = nb * vper + tid / LPR; r < v_end; r += RPI) {
+    mv = absmax8(mv, *(const u32x4*)(a.v + kvb + r * D + part * 8));
+    mk = absmax8(mk, *(const u32x4*)(a.k + kvb + r * D + part * 8));
   }
+  // Workgroup maxima: within each wave, then across the 4 waves through LDS.
+  float m[kMaxes];
+  m[kMaxDO] = mdo;
+  m[kMaxV] = mv;
+  m[kMaxQ] = mq;
+  m[kMaxK] = mk;
+  __shared__ float red[4][kMaxes];
+#pragma unroll
+  for (int i = 0; i < kMaxes; ++i) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) m[i] = fmaxf(m[i], __shfl_xor(m[i], off));
+    if ((tid & 63) == 0) red[tid >> 6][i] = m[i];
+  }
+  __syncthreads();
+  if (tid < kMaxes) {
+    const float x = fmaxf(fmaxf(red[0][tid], red[1][tid]), fmaxf(red[2][tid], red[3][tid]));
+    a.pmax[((size_t)grp * kPreBlocks + nb) * kMaxes + tid] = x;
+  }
+}
+
+// Power of two 2^e that brings a group's largest magnitude mx into [2^(top-1), 2^top):
+// every bf16 value x of the group then has x 2^e exactly representable in fp16 (top <= 15),
+// unless |x| < 2^(-16-top) mx: its scaled value then lies below 2^-17, where fp16's
+// subnormal spacing 2^-24 no longer holds bf16's 8 significant bits (the rounding error
+// there is at most 2^-25, below 2^(-24-top) mx after unscaling).  0 for an all-zero group
+// and for inf or NaN (the results are then inf or NaN anyway); at most 60 either way.
+__device__ __forceinline__ int fp16_exponent(float mx, int top) {
+  if (!(mx > 0.0f) || !(mx < INFINITY)) return 0;
+  int e;
+  (void)frexpf(mx, &e);  // mx = f 2^e, f in [1/2, 1)
+  return min(max(top - e, -60), 60);
+}
+
+// Scale exponents of a group's fp16 operands.  dO and V are brought under 2^3, so that in
+// the dK/dV kernel |dP| <= d 2^6 and |dS| = P |dP - D| <= 2 d 2^6 <= 2^14 stay within fp16
+// (D is a P-weighted mean of dP); Q and K use fp16's whole range (their products are only
+// accumulated in fp32).
+struct GroupScales {
+  int e_do, e_v, e_q, e_k;
+};
+
+// The reduction runs over the wave, so the result is the same in every lane (and is moved
+// to scalar registers).
+__device__ __forceinline__ GroupScales group_scales(const float* __restrict__ pmax, int grp) {
+  const int lane = threadIdx.x & 63;
+  float m[kMaxes];
+#pragma unroll
+  for (int i = 0; i < kMaxes; ++i) {
+    m[i] = lane < kPreBlocks ? pmax[((size_t)grp * kPreBlocks + lane) * kMaxes + i] : 0.0f;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) m[i] = fmaxf(m[i], __shfl_xor(m[i], off));
+  }
+  GroupScales g;
+  g.e_do = __builtin_amdgcn_readfirstlane(fp16_exponent(m[kMaxDO], 3));
+  g.e_v = __builtin_amdgcn_readfirstlane(fp16_exponent(m[kMaxV], 3));
+  g.e_q = __builtin_amdgcn_readfirstlane(fp16_exponent(m[kMaxQ], 15));
+  g.e_k = __builtin_amdgcn_readfirstlane(fp16_exponent(m[kMaxK], 15));
+  return g;
+}
+
+// Two floats (exact in fp16, or rounded to nearest even) packed as an fp16 pair.
+__device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
+  typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+  f16x2 r;
+  r[0] = (_Float16)lo;
+  r[1] = (_Float16)hi;
+  return __builtin_bit_cast(uint32_t, r);
+}
+
+// Eight bf16 (one 16-byte chunk) times 2^e (sc) as eight fp16.
+__device__ __forceinline__ u32x4 bf16x8_to_f16x8(u32x4 w, float sc) {
+  u32x4 r;
+#pragma unroll
+  for (int e = 0; e < 4; ++e)
+    r[e] = pack_f16x2(__builtin_bit_cast(float, w[e] << 16) * sc, __builtin_bit_cast(float, w[e] & 0xffff0000u) * sc);
+  return r;
 }
 
 // ------------------------------------------------------------------ main
@@ -182,8 +299,8 @@ void bwd_main_kernel(BwdArgs a) {
     const int hq = hkv * G + g;
     const size_t rbase = ((size_t)b * a.Hq + hq) * (size_t)S;
     const int q0 = qt * kBwdBM;
-    const char* qb = (const char*)(a.q + (rbase + q0) * D);
-    const char* ob = (const char*)(a.dO + (rbase + q0) * D);
+    const char* qb = (const char*)(a.q16 + (rbase + q0) * D);
+    const char* ob = (const char*)(a.do16 + (rbase + q0) * D);
     if (q0 + kBwdBM <= S) {
 #pragma unroll
       for (int i = 0; i < QDMAS; ++i) {
@@ -205,7 +322,7 @@ void bwd_main_kernel(BwdArgs a) {
     // LSE log2e (wave 0) and D (wave 1) of the 64 queries: 16 lanes x 16 bytes each.
     if (wave_u < 2) {
       const size_t pbase = ((size_t)b * a.Hq + hq) * (size_t)S_pad + q0;
-      const void* src = uniform_ptr((wave_u == 0 ? a.lse2 : a.delta) + pbase);
+      const void* src = uniform_ptr((wave_u == 0 ? a.lse2 : a.ndx) + pbase);
       if (lane < 16) dma16_s(src, (uint32_t)lane * 16u, &sd_lds[st][wave_u * kBwdBM]);
     }
   };
@@ -231,7 +348,11 @@ void bwd_main_kernel(BwdArgs a) {
     dk_acc[db] = f32x16{};
     dv_acc[db] = f32x16{};
   }
-  const float c = a.scale * kLog2e;  // signed: no running maximum is needed here
+  // The group's fp16 scales (see the conversion before the step loop).  S is computed from
+  // Q 2^e_q and K 2^e_k, so c carries 2^-(e_q + e_k); c is signed: no running maximum is
+  // needed here.
+  const GroupScales gs = group_scales(a.pmax, bh);
+  const float c = ldexpf(a.scale * kLog2e, -(gs.e_q + gs.e_k));
 
   // One step on stage ST; MASKED adds the causal / end-of-sequence mask to P.
   auto compute = [&](const int q0, auto stage, auto masked) {
@@ -285,14 +406,14 @@ void bwd_main_kernel(BwdArgs a) {
     for (int i = 0; i < NS; ++i) {
       issue(i + PD);
       if (i < KSTEPS) {
-        sacc = mfma32(fa[i], fb[i], sacc);
+        sacc = mfma32_f16(fa[i], fb[i], sacc);
       } else if (i < 2 * KSTEPS) {
         if (i == KSTEPS) {
           const f32x16 nd = {d4[0][0], d4[0][1], d4[0][2], d4[0][3], d4[1][0], d4[1][1], d4[1][2], d4[1][3],
                              d4[2][0], d4[2][1], d4[2][2], d4[2][3], d4[3][0], d4[3][1], d4[3][2], d4[3][3]};
-          dpacc = mfma32(fa[i], fb[i], nd);
+          dpacc = mfma32_f16(fa[i], fb[i], nd);
         } else {
-          dpacc = mfma32(fa[i], fb[i], dpacc);
+          dpacc = mfma32_f16(fa[i], fb[i], dpacc);
         }
         // P for a share of the 16 registers, once S has had two slots to finish.
         const int j = i - KSTEPS - 2;
@@ -301,19 +422,19 @@ void bwd_main_kernel(BwdArgs a) {
 #pragma unroll
           for (int v = 0; v < 16; ++v) {
             if (v < e0 || v >= e1) continue;
-            float p = exp2_sm<EXPMODE, false>(fmaf(sacc[v], c, -l4[v >> 2][v & 3]));
+            float p = exp2_sm<EXPMODE>(fmaf(sacc[v], c, -l4[v >> 2][v & 3]));
             if constexpr (MASKED) {
               const int ev = (v >> 2) * 8 + (v & 3);
               p = (ev < lim_c || ev >= lim_s) ? 0.0f : p;
             }
             sacc[v] = p;
-            if (v & 1) pw[v >> 3][(v & 7) >> 1] = pack_bf16x2(sacc[v - 1], p);
+            if (v & 1) pw[v >> 3][(v & 7) >> 1] = pack_f16x2(sacc[v - 1], p);
           }
         }
       } else if (i < 3 * KSTEPS) {
         const int p = i - 2 * KSTEPS, t = p / DBLK, db = p % DBLK;
         const u32x4 w = {pw[t][0], pw[t][1], pw[t][2], pw[t][3]};
-        dv_acc[db] = mfma32(join(tlo[i], thi[i]), __builtin_bit_cast(bf16x8, w), dv_acc[db]);
+        dv_acc[db] = mfma32_f16(join(tlo[i], thi[i]), __builtin_bit_cast(bf16x8, w), dv_acc[db]);
         // dS for a share of the 16 registers, once dP has had two slots to finish.
         const int j = p - 2;
         if (j >= 0) {
@@ -323,13 +444,13 @@ void bwd_main_kernel(BwdArgs a) {
             if (v < e0 || v >= e1) continue;
             const float ds = sacc[v] * dpacc[v];
             dpacc[v] = ds;
-            if (v & 1) sw[v >> 3][(v & 7) >> 1] = pack_bf16x2(dpacc[v - 1], ds);
+            if (v & 1) sw[v >> 3][(v & 7) >> 1] = pack_f16x2(dpacc[v - 1], ds);
           }
         }
       } else {
         const int p = i - 3 * KSTEPS, t = p / DBLK, db = p % DBLK;
         const u32x4 w = {sw[t][0], sw[t][1], sw[t][2], sw[t][3]};
-        dk_acc[db] = mfma32(join(tlo[i], thi[i]), __builtin_bit_cast(bf16x8, w), dk_acc[db]);
+        dk_acc[db] = mfma32_f16(join(tlo[i], thi[i]), __builtin_bit_cast(bf16x8, w), dk_acc[db]);
       }
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -359,6 +480,23 @@ void bwd_main_kernel(BwdArgs a) {
   };
 
   if (steps > 0) stage_in(0);
+  // K and V into fp16 in place, times 2^e_k and 2^e_v (exact, see fp16_exponent).  Every
+  // product runs in fp16, on Q 2^e_q and dO 2^e_do staged from the dQ kernel's copies: S
+  // carries 2^(e_q + e_k) (taken out through c), dP, -D and dS 2^(e_do + e_v), dV 2^e_do
+  // and dK 2^(e_q + e_do + e_v); the last two are taken out at the end.
+  wait_dma();
+  __syncthreads();  // K and V are in LDS
+  {
+    const float sk = ldexpf(1.0f, gs.e_k), sv = ldexpf(1.0f, gs.e_v);
+    u32x4* kk = (u32x4*)k_lds;
+    u32x4* vv = (u32x4*)v_lds;
+#pragma unroll
+    for (int i = 0; i < KT / 8 / 512; ++i) {
+      kk[i * 512 + tid] = bf16x8_to_f16x8(kk[i * 512 + tid], sk);
+      vv[i * 512 + tid] = bf16x8_to_f16x8(vv[i * 512 + tid], sv);
+    }
+  }
+  // (the first step's barrier orders these writes before any read of V)
   for (int step = 0; step < steps; step += 2) {
     do_step(step, std::integral_constant<int, 0>{});
     if (step + 1 < steps) do_step(step + 1, std::integral_constant<int, 1>{});
@@ -390,7 +528,10 @@ void bwd_main_kernel(BwdArgs a) {
     __syncthreads();
   }
   if (qh == 0 && key < S) {
-    const float ks = a.scale;
+    // dK = scale 2^-(e_do + e_v) (2^-e_q acc), in two factors that each stay in range.
+    const float kq = ldexpf(1.0f, -gs.e_q);
+    const float ks = ldexpf(a.scale, -(gs.e_do + gs.e_v));
+    const float vs = ldexpf(1.0f, -gs.e_do);
     // The lane's half, recomputed here rather than kept live across the loop.
     const int half = __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u)) >> 5;
     uint16_t* dkr = a.dk + kvbase + (size_t)key * D;
@@ -400,10 +541,10 @@ void bwd_main_kernel(BwdArgs a) {
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4) {
         u32x2 wk, wv;
-        wk[0] = pack_bf16x2(dk_acc[db][g4 * 4 + 0] * ks, dk_acc[db][g4 * 4 + 1] * ks);
-        wk[1] = pack_bf16x2(dk_acc[db][g4 * 4 + 2] * ks, dk_acc[db][g4 * 4 + 3] * ks);
-        wv[0] = pack_bf16x2(dv_acc[db][g4 * 4 + 0], dv_acc[db][g4 * 4 + 1]);
-        wv[1] = pack_bf16x2(dv_acc[db][g4 * 4 + 2], dv_acc[db][g4 * 4 + 3]);
+        wk[0] = pack_bf16x2(dk_acc[db][g4 * 4 + 0] * kq * ks, dk_acc[db][g4 * 4 + 1] * kq * ks);
+        wk[1] = pack_bf16x2(dk_acc[db][g4 * 4 + 2] * kq * ks, dk_acc[db][g4 * 4 + 3] * kq * ks);
+        wv[0] = pack_bf16x2(dv_acc[db][g4 * 4 + 0] * vs, dv_acc[db][g4 * 4 + 1] * vs);
+        wv[1] = pack_bf16x2(dv_acc[db][g4 * 4 + 2] * vs, dv_acc[db][g4 * 4 + 3] * vs);
         *(u32x2*)(dkr + db * 32 + g4 * 8 + half * 4) = wk;
         *(u32x2*)(dvr + db * 32 + g4 * 8 + half * 4) = wv;
       }
@@ -421,6 +562,16 @@ void bwd_main_kernel(BwdArgs a) {
 //     dQ^T += K^T dS^T                              (K^T by LDS transpose reads)
 // It recomputes S and dP (two of the backward's five products) instead of adding
 // partial dQ blocks from every key tile with fp32 atomics, and it is deterministic.
+//
+// Two by-products for the dK/dV kernel, which runs after this one:
+//  * the exact row term D_i = sum_j P_ij dP_ij.  The -D the dP chains start from comes
+//    from the stored bf16 O (<dO_i, O_i>), so the dS row sums are D_i - D_i(bf16 O) (the
+//    probabilities of a row sum to one); adding them gives D without O's rounding.  It is
+//    stored negated and times 2^(e_dO + e_V) in the units of the dK/dV kernel's dP.
+//  * dO and Q in fp16, each times its group's power of two (exact, see fp16_exponent),
+//    from the fragments this kernel holds anyway: the dK/dV kernel's products run in
+//    fp16, so that P enters dV^T += dO^T P, and dS enters dK^T += Q^T dS, with fp16's
+//    11-bit significand instead of bf16's 8.
 //
 // K and V tiles sit in LDS as XOR chunk-inner blocks (attn_device.h), filled by coalesced
 // DMA; both the operand reads of K and V and the transpose reads of K^T are free of bank
@@ -482,6 +633,10 @@ void bwd_dq_kernel(BwdArgs a) {
   const int qw = q0 + wave * 32;
   const int qi = qw + col;  // this lane's query
   const int qc = min(qi, S - 1);  // rows past the end read the last row; never stored
+  // Causal bound of the wave's first query.  The non-causal kernels use the same tests
+  // against a bound past any sequence (kept opaque): with the tests folded away at compile
+  // time the compiler's allocation for them exceeds the 256 registers and spills.
+  const int qhi = CAUSAL ? qw : opaque(0x3fffffff);
   const size_t qbase = ((size_t)b * a.Hq + hq) * (size_t)S * D;
   const size_t kvbase = ((size_t)b * a.Hkv + hkv) * (size_t)S * D;
   const uint16_t* __restrict__ Kg = a.k + kvbase;
@@ -498,14 +653,34 @@ void bwd_dq_kernel(BwdArgs a) {
       of[ks] = __builtin_bit_cast(bf16x8, orow[ks * 2]);
     }
   }
+  // The group's fp16 scales; this workgroup's rows of dO and Q in fp16 (scaled) for the
+  // dK/dV kernel, from the fragments held here anyway.
+  const GroupScales gs = group_scales(a.pmax, kvg);
+  if (qi < S) {
+    const float so = ldexpf(1.0f, gs.e_do), sq = ldexpf(1.0f, gs.e_q);
+    u32x4* dst_o = (u32x4*)(a.do16 + qbase + (size_t)qi * D + half * 8);
+    u32x4* dst_q = (u32x4*)(a.q16 + qbase + (size_t)qi * D + half * 8);
+#pragma unroll
+    for (int ks = 0; ks < KSTEPS; ++ks) {
+      dst_o[ks * 2] = bf16x8_to_f16x8(__builtin_bit_cast(u32x4, of[ks]), so);
+      dst_q[ks * 2] = bf16x8_to_f16x8(__builtin_bit_cast(u32x4, qf[ks]), sq);
+    }
+  }
   const size_t prow = ((size_t)b * a.Hq + hq) * (size_t)S_pad + qc;
   const float lse2 = a.lse2[prow];
-  const float nd = a.delta[prow];  // -D
-  // dP^T chains start from -D (every register of a lane belongs to its query), so the
-  // products give dP^T - D directly and dS^T = P^T (dP^T - D) is one multiply.
-  f32x16 negd;
+  float dsum = 0.0f;  // this lane's part of sum_j dS_ij
+  // dP^T chains start from -D (from the bf16 O; every register of a lane belongs to its
+  // query), so the products give dP^T - D directly and dS^T = P^T (dP^T - D) is one
+  // multiply.  The cubic exponential needs more registers than the hardware one; its
+  // kernels keep -D in one register and subtract it in dS instead of holding the 16
+  // copies the chain start needs, which would not fit without spilling.
+  constexpr bool NEGD = EXPMODE == 0;
+  f32x16 negd = f32x16{};
+  const float nd0 = a.delta[prow];
+  if constexpr (NEGD) {
 #pragma unroll
-  for (int v = 0; v < 16; ++v) negd[v] = nd;
+    for (int v = 0; v < 16; ++v) negd[v] = nd0;
+  }
   const float c = a.scale * kLog2e;  // signed: no running maximum is needed here
 
   const int kv_end = CAUSAL ? min(S, q0 + kDqBM) : S;
@@ -566,7 +741,7 @@ void bwd_dq_kernel(BwdArgs a) {
     int lim = BN;  // keys at tile positions e > lim are masked
     if constexpr (MASKED) {
       const int lim_s = S - 1 - k0 - half * 4;
-      lim = CAUSAL ? min(lim_s, qi - k0 - half * 4) : lim_s;
+      lim = min(lim_s, qhi + col - k0 - half * 4);
     }
     bf16x8 fr[2 * NA];      // K / V fragments of the S^T and dP^T slots
     i16x4 tlo[NC], thi[NC];  // K^T transpose-read halves of the dQ^T slots
@@ -595,8 +770,9 @@ void bwd_dq_kernel(BwdArgs a) {
       for (int vv = 0; vv < 8; ++vv) {
         if (vv < v0 || vv >= v1) continue;
         const int v = (u & 1) * 8 + vv;
-        const float ds = s[kb][v] * dp[kb][v];
+        const float ds = NEGD ? s[kb][v] * dp[kb][v] : s[kb][v] * (dp[kb][v] + nd0);
         dp[kb][v] = ds;
+        dsum += ds;
         if (v & 1) dw[u][(v & 7) >> 1] = pack_bf16x2(dp[kb][v - 1], ds);
       }
     };
@@ -622,7 +798,7 @@ void bwd_dq_kernel(BwdArgs a) {
 #pragma unroll
         for (int e = 0; e < 2 * 16; ++e) {
           if (e < e0 || e >= e1) continue;
-          float p = exp2_sm<EXPMODE, false>(fmaf(s[e >> 4][e & 15], c, -lse2));
+          float p = exp2_sm<EXPMODE>(fmaf(s[e >> 4][e & 15], c, -lse2));
           if constexpr (MASKED) {
             const int ek = (e >> 4) * 32 + ((e & 15) >> 2) * 8 + (e & 3);  // key - k0 - half*4
             p = ek > lim ? 0.0f : p;
@@ -656,8 +832,8 @@ void bwd_dq_kernel(BwdArgs a) {
       dma_tile(Vg, j + 1, Vring + (1 - P) * TILE);
     }
     const int k0 = j * BN;
-    if (!CAUSAL || k0 <= qw + 31) {
-      const bool need_mask = (k0 + BN > S) || (CAUSAL && k0 + BN - 1 > qw);
+    if (k0 <= qhi + 31) {
+      const bool need_mask = (k0 + BN > S) || (k0 + BN - 1 > qhi);
       if (need_mask) {
         compute(j, parity, std::true_type{});
       } else {
@@ -677,6 +853,13 @@ void bwd_dq_kernel(BwdArgs a) {
     if (j + 1 < nkv) step(j + 1, std::integral_constant<int, 1>{});
   }
 
+  // -D_i = -(D_i(bf16 O) + sum_j dS_ij) for the dK/dV kernel, in its dP units; 0 on the
+  // padding rows up to S_pad (that kernel moves whole 64-row blocks of it into LDS).
+  const float dtot = sum_halves(dsum);
+  if (half == 0 && qi < S_pad) {
+    const size_t pr = ((size_t)b * a.Hq + hq) * (size_t)S_pad + qi;
+    a.ndx[pr] = qi < S ? (nd0 - dtot) * ldexpf(1.0f, gs.e_do + gs.e_v) : 0.0f;
+  }
   if (qi < S) {
     uint16_t* dqr = a.dq + qbase + (size_t)qi * D;
     const float sc = a.scale;
@@ -696,23 +879,22 @@ void bwd_dq_kernel(BwdArgs a) {
 template <int D, bool CAUSAL, int EXPMODE>
 hipError_t launch_bwd_t(const BwdArgs& a, int phases, hipStream_t stream) {
   hipError_t e = hipSuccess;
+  // Order: preprocess, dQ (which also writes the exact -D and the fp16 dO that the dK/dV
+  // kernel reads), dK/dV.
   if (phases & 1) {
     const int S_pad = (a.S + kBwdBM - 1) / kBwdBM * kBwdBM;
-    const long prows = (long)a.B * a.Hq * S_pad;
-    const long pre_threads = prows * (D / 8);
-    hipLaunchKernelGGL(bwd_pre_kernel<D>, dim3((unsigned)((pre_threads + 255) / 256)), dim3(256), 0, stream,
-                       a.o, a.dO, a.lse, a.delta, a.lse2, prows, a.S, S_pad);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-  }
-  if (phases & 2) {
-    const int nkt = (a.S + kBwdBN - 1) / kBwdBN;
-    hipLaunchKernelGGL((bwd_main_kernel<D, CAUSAL, EXPMODE>), dim3((unsigned)(nkt * a.B * a.Hkv)), dim3(512), 0,
-                       stream, a);
+    hipLaunchKernelGGL(bwd_pre_kernel<D>, dim3((unsigned)(a.B * a.Hkv * kPreBlocks)), dim3(256), 0, stream, a, S_pad);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   if (phases & 4) {
     const int nqt = (a.S + kDqBM - 1) / kDqBM;
     hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL, EXPMODE>), dim3((unsigned)(nqt * a.B * a.Hq)), dim3(256), 0,
+                       stream, a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  if (phases & 2) {
+    const int nkt = (a.S + kBwdBN - 1) / kBwdBN;
+    hipLaunchKernelGGL((bwd_main_kernel<D, CAUSAL, EXPMODE>), dim3((unsigned)(nkt * a.B * a.Hkv)), dim3(512), 0,
                        stream, a);
     e = hipGetLastError();
   }

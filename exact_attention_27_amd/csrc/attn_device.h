@@ -53,8 +53,9 @@ constexpr float kExp2C3 = 0x1.c2a216p-5f;
 
 // HIGH: clamp the argument above at 64 as well as below at -127.  Without the upper clamp
 // the result is still right for every x < 128 (2^127 is the largest power the exponent
-// field holds); the backward's arguments, s * c - LSE * log2(e) with the forward's LSE,
-// never exceed a few ulps above 0, so it skips that clamp and the register it costs.
+// field holds) and wraps into the sign bit above; every kernel keeps the clamp, so an
+// argument out of range saturates instead (the backward's arguments stay near or below 0
+// for an LSE that matches its inputs, but the clamp costs one v_min).
 template <bool HIGH = true>
 __host__ __device__ inline float exp2_poly3(float x) {
   x = fmaxf(x, -127.0f);
@@ -107,6 +108,13 @@ __device__ __forceinline__ bool wave_any(bool p) { return __builtin_amdgcn_ballo
 // ---------------------------------------------------------------------------------
 __device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const f32x16& c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// v_mfma_f32_32x32x16_f16: the same shape and lane layouts with fp16 operands; the
+// operands arrive as 16-bit lanes in the same vector type as the bf16 ones.
+__device__ __forceinline__ f32x16 mfma32_f16(const bf16x8& a, const bf16x8& b, const f32x16& c) {
+  typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
 }
 
 __device__ __forceinline__ i16x4 lds_read_tr16(const uint16_t* p) {

@@ -39,8 +39,13 @@ struct BwdArgs {
   uint16_t* dq;
   uint16_t* dk;
   uint16_t* dv;
-  float* delta;   // [B*Hq][S_pad] fp32 workspace: -D_i = -<dO_i, O_i> (S_pad = S rounded up to 64)
-  float* lse2;    // [B*Hq][S_pad] fp32 workspace: LSE_i * log2(e)
+  // Workspace (S_pad = S rounded up to 64; a "group" is one (batch, KV head)):
+  float* delta;   // [B*Hq][S_pad] fp32: -D_i = -<dO_i, O_i> from the stored bf16 O (preprocess)
+  float* lse2;    // [B*Hq][S_pad] fp32: LSE_i * log2(e) (preprocess)
+  float* ndx;     // [B*Hq][S_pad] fp32: -D_i = -sum_j P_ij dP_ij, times 2^(e_dO + e_V) (dQ kernel)
+  float* pmax;    // [B*Hkv][32][4] fp32: partial maxima of |dO|, |V|, |Q|, |K| per group (preprocess)
+  uint16_t* do16; // [B*Hq][S][d] fp16: dO * 2^e_dO (dQ kernel), the dK/dV kernel's dO operand
+  uint16_t* q16;  // [B*Hq][S][d] fp16: Q * 2^e_Q (dQ kernel), the dK/dV kernel's Q operand
   int B, Hq, Hkv, S;
   float c;        // |scale| * log2(e) (1 for a zero scale)
   float scale;    // the caller's scale (dQ and dK carry it)

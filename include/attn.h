@@ -155,20 +155,34 @@ int attn_fwd_varlen(const void* q, const void* k, const void* v, void* o, float*
                     const attn_options* opt, void* stream);
 
 /*
- * Bytes of device workspace attn_bwd needs for these sizes: two fp32 row arrays
- * [B*Hq][S_pad] (the row terms -D_i = -<dO_i, O_i> and LSE_i log2(e), S_pad = S
- * rounded up to a multiple of 64), each rounded up to 256 bytes.  Returns 0 for invalid or
- * empty sizes.
+ * Bytes of device workspace attn_bwd needs for these sizes, each part rounded up to 256
+ * bytes (S_pad = S rounded up to a multiple of 64): three fp32 row arrays [B*Hq][S_pad]
+ * (the row term -D_i = -<dO_i, O_i> from the stored O, LSE_i log2(e), and -D_i formed
+ * from its definition sum_j P_ij dP_ij, scaled), the preprocess's partial maxima of |dO|,
+ * |V|, |Q| and |K| (fp32 [B*Hkv][32][4]), and dO scaled by a power of two per (batch, KV head) in
+ * fp16 ([B*Hq][S][d], 2 bytes per element), and Q likewise.  About B*Hq*S*(4d + 12) bytes.
+ * Returns 0 for invalid or empty sizes.
  */
 size_t attn_bwd_workspace_bytes(int B, int Hq, int Hkv, int S, int d);
 
 /*
- * Backward pass.  Inputs: q, k, v, the forward outputs o and lse (as written by
- * attn_fwd, or any consistent pair), and the upstream gradient dO.  Outputs dq,
- * dk, dv are written in full.  workspace: device memory of at least
+ * Backward pass.  Inputs: q, k, v, the forward outputs o and lse, and the upstream
+ * gradient dO.  lse must be the logsumexp of these q, k and scale up to fp32 rounding (as
+ * attn_fwd writes it) and o the matching output in bf16; with an lse far from that (say
+ * 80 below) the recomputed probabilities overflow and the outputs are not meaningful.
+ * Outputs dq, dk, dv are written in full.  workspace: device memory of at least
  * attn_bwd_workspace_bytes(...) bytes, 256-byte aligned, owned by the caller;
  * its contents on entry do not matter and on exit are unspecified.  All outputs
  * are deterministic (no atomics).
+ *
+ * Rounding: the products run on the MFMA units with fp32 accumulation.  The products
+ * that give dK and dV (S = Q K^T, dP = dO V^T, dV^T += dO^T P, dK^T += Q^T dS) take their
+ * operands in fp16: Q, K, V and dO are scaled by a power of two per (batch, KV head),
+ * found by the preprocess, that makes every value exact in fp16 (bar values more than
+ * 2^19 below the group's largest, whose rounding there is far below the outputs'), and P
+ * and dS are rounded to fp16 (11 significant bits).  The dQ products take bf16 operands,
+ * with dS rounded to bf16.  dK and dV use the row term D_i = sum_j P_ij dP_ij as defined;
+ * dQ uses D_i = <dO_i, O_i> with the stored bf16 O.
  */
 int attn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
              const void* dO, void* dq, void* dk, void* dv,
@@ -183,13 +197,16 @@ int attn_bwd_ex(const void* q, const void* k, const void* v, const void* o, cons
 
 /*
  * One phase of attn_bwd_ex, for callers that schedule or time the backward's launches
- * separately.  Running ATTN_BWD_PREPROCESS, ATTN_BWD_MAIN and ATTN_BWD_DQ in that
+ * separately.  Running ATTN_BWD_PREPROCESS, ATTN_BWD_DQ and ATTN_BWD_MAIN in that
  * order on one stream, with the same arguments and workspace, is exactly attn_bwd_ex
- * (ATTN_BWD_ALL); MAIN and DQ are independent of each other.  The phases communicate
- * through the workspace:
- *   PREPROCESS  reads o, dO, lse; writes -D = -rowsum(dO * O) and LSE log2(e);
- *   MAIN        reads q, k, v, dO, D and LSE log2(e); writes dk, dv;
- *   DQ          reads q, k, v, dO, D and LSE log2(e); writes dq.
+ * (ATTN_BWD_ALL); each phase needs the ones before it.  The phases communicate through
+ * the workspace:
+ *   PREPROCESS  reads o, dO, lse, q, k, v; writes -D = -rowsum(dO * O), LSE log2(e) and
+ *               the partial maxima of |dO|, |V|, |Q|, |K|;
+ *   DQ          reads q, k, v, dO and the above; writes dq, the defined -D (scaled) and
+ *               dO and Q in fp16 (scaled);
+ *   MAIN        reads k, v, LSE log2(e), the maxima and the DQ phase's -D, fp16 dO and
+ *               fp16 Q; writes dk, dv.
  * Arguments are validated as for attn_bwd_ex; an unknown phase is ATTN_ERR_UNSUPPORTED.
  */
 enum {
@@ -208,11 +225,10 @@ const char* attn_status_string(int status);
 
 /*
  * Evaluate the softmax's exp2 on the device, y[i] = 2^x[i] for i < n, with the
- * given exp_mode, exactly as the forward does (device pointers x, y; n >= 0).
- * For testing the polynomial and the hardware instruction in isolation.  The
- * polynomial clamps x to [-127, 64]: below -127 it gives 0, above 64 it gives
- * 2^64 (the backward, whose arguments stay near or below 0, omits the upper
- * clamp).
+ * given exp_mode, exactly as the forward and backward do (device pointers x, y;
+ * n >= 0).  For testing the polynomial and the hardware instruction in isolation.
+ * The polynomial clamps x to [-127, 64]: below -127 it gives 0, above 64 it gives
+ * 2^64.
  */
 int attn_exp2_eval(const float* x, float* y, long n, int exp_mode, void* stream);
 

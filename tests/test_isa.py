@@ -6,8 +6,7 @@
 * no packed-fp32 VALU instructions (v_pk_add/mul/fma_f32), which the build disables;
 * nothing is written through the scalar data cache (no s_store / s_buffer_store /
   scalar atomics);
-* no kernel uses scratch (register spills) except the non-causal d=128 dQ kernels, a
-  known limitation.
+* no kernel uses scratch (register spills).
 """
 
 import os
@@ -67,7 +66,7 @@ def test_no_packed_fp32_and_no_scalar_stores(isa):
             assert not s.startswith(("s_dcache_wb", "s_dcache_discard")), f"{name}: {s}"
 
 
-def test_no_scratch_except_noncausal_dq(isa):
+def test_no_scratch(isa):
     scratch = {}
     for text in isa.values():
         # kernel metadata: ".name: <symbol>" followed by ".private_segment_fixed_size: <bytes>"
@@ -76,6 +75,4 @@ def test_no_scratch_except_noncausal_dq(isa):
     assert len([k for k in scratch if "fwd_kernel" in k]) == 32, sorted(scratch)  # 2 d x 2 causal x 2 exp x 2 layouts x 2 schedules
     assert len([k for k in scratch if "bwd_" in k]) == 18, sorted(scratch)
     for kernel, n in scratch.items():
-        if "bwd_dq_kernelILi128ELb0E" in kernel:  # known: ~100 bytes (VGPR budget), ~1% of its time
-            continue
         assert n == 0, f"{kernel} uses {n} bytes of scratch"

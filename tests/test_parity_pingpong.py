@@ -13,7 +13,7 @@ import torch
 import exact_attention_27_amd as ea
 import oracle
 import workloads
-from helpers import EDGE_REL, assert_bf16_close, assert_lse_close, f64
+from helpers import assert_bf16_close, assert_lse_close, f64
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -37,7 +37,7 @@ def test_pingpong_edge_shapes(case, causal):
     o, lse = ea.attn_fwd_ex(t["q"], t["k"], t["v"], scale, causal, variant=PP)
     torch.cuda.synchronize()
     ro, rl = oracle.attention_forward(f64(t["q"]), f64(t["k"]), f64(t["v"]), scale, causal)
-    assert_bf16_close("o", o, ro, rel=EDGE_REL)
+    assert_bf16_close("o", o, ro)
     assert_lse_close(lse, rl)
     o0, l0 = ea.attn_fwd_ex(t["q"], t["k"], t["v"], scale, causal, variant=FW)
     torch.cuda.synchronize()
@@ -103,5 +103,5 @@ def test_pingpong_varlen(causal):
             x, y = oracle.head_forward(f64(t["q"][a:a + n, h]), f64(t["k"][a:a + n, h // 2]),
                                        f64(t["v"][a:a + n, h // 2]), d ** -0.5, causal, rows=rows)
             go.append(o[a + rows, h]); gl.append(lse[h, a + rows]); ro.append(x); rl.append(y)
-    assert_bf16_close("o", torch.cat(go), np.concatenate(ro), rel=EDGE_REL)
+    assert_bf16_close("o", torch.cat(go), np.concatenate(ro))
     assert_lse_close(torch.cat(gl), np.concatenate(rl))

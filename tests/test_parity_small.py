@@ -12,7 +12,7 @@ import torch
 import exact_attention_27_amd as ea
 import oracle
 import workloads
-from helpers import EDGE_REL, assert_bf16_close, assert_lse_close, f64
+from helpers import assert_bf16_close, assert_lse_close, f64
 
 pytestmark = pytest.mark.gpu
 
@@ -45,7 +45,7 @@ def test_fwd_edge_shapes(case, causal):
     o, lse = ea.attn_fwd(t["q"], t["k"], t["v"], scale, causal)
     torch.cuda.synchronize()
     ro, rlse = oracle_fwd(t, scale, causal)
-    assert_bf16_close("o", o, ro, rel=EDGE_REL)
+    assert_bf16_close("o", o, ro)
     assert_lse_close(lse, rlse)
     if causal:  # query 0 sees key 0 only: O_0 is V_0 bit for bit
         G = Hq // Hkv
@@ -63,7 +63,7 @@ def test_fwd_options(exp_mode, tau, causal):
     o, lse = ea.attn_fwd_ex(t["q"], t["k"], t["v"], d ** -0.5, causal, exp_mode=exp_mode, tau=tau)
     torch.cuda.synchronize()
     ro, rlse = oracle_fwd(t, d ** -0.5, causal)
-    assert_bf16_close("o", o, ro, rel=EDGE_REL)
+    assert_bf16_close("o", o, ro)
     assert_lse_close(lse, rlse)
 
 
@@ -86,7 +86,7 @@ def test_fwd_huge_score_jump(causal, exp_mode, variant):
     o, lse = ea.attn_fwd_ex(t["q"], t["k"], t["v"], d ** -0.5, causal, exp_mode=exp_mode, tau=8.0, variant=variant)
     torch.cuda.synchronize()
     ro, rlse = oracle_fwd(t, d ** -0.5, causal)
-    assert_bf16_close("o", o, ro, rel=EDGE_REL)
+    assert_bf16_close("o", o, ro)
     assert_lse_close(lse, rlse)
 
 
@@ -102,7 +102,7 @@ def test_fwd_rescale_with_growing_scores(tau):
     o, lse = ea.attn_fwd_ex(t["q"], t["k"], t["v"], d ** -0.5, True, tau=tau)
     torch.cuda.synchronize()
     ro, rlse = oracle_fwd(t, d ** -0.5, True)
-    assert_bf16_close("o", o, ro, rel=EDGE_REL)
+    assert_bf16_close("o", o, ro)
     assert_lse_close(lse, rlse)
 
 
@@ -115,8 +115,8 @@ def test_fwd_scales(scale):
     o, lse = ea.attn_fwd(t["q"], t["k"], t["v"], scale, True)
     torch.cuda.synchronize()
     ro, rlse = oracle_fwd(t, scale, True)
-    assert_bf16_close("o", o, ro, rel=EDGE_REL)
-    assert_lse_close(lse, rlse, max_abs=1e-3 * max(1.0, abs(scale) * 4))
+    assert_bf16_close("o", o, ro)
+    assert_lse_close(lse, rlse)
 
 
 def test_fwd_deterministic_and_stream():
@@ -154,13 +154,12 @@ BWD_CASES = [
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("case", BWD_CASES, ids=lambda c: "B%dHq%dHkv%dS%dd%d" % c)
 def test_bwd_edge_shapes(case, causal):
-    """GPU forward then GPU backward (as in training), against the oracle's fp64 gradients.
-
-    With 8 query heads per KV head on a short causal sequence, the first keys gather
-    attention from every query of all 8 heads, and D_i = <dO_i, O_i> computed from the
-    stored bf16 O (the only O the backward has) moves their dK by up to 1.5e-2 before
-    output rounding; a CPU emulation of exactly that step alone reproduces the GPU's
-    error (0.0197 vs 0.0208).  Those cases use a 3e-2 bar."""
+    """GPU forward then GPU backward (as in training), against the oracle's fp64 gradients,
+    at the plain bar.  These include 8 query heads per KV head on short causal sequences,
+    where the first keys gather attention from every query of all 8 heads: there the
+    rounding model (tests/rounding_model.py) puts the errors of bf16 P in dV and of D from
+    the bf16 O in dK above 2e-2, which is why the kernels take P into dV in fp16 and form
+    D for dK/dV from its definition."""
     B, Hq, Hkv, S, d = case
     print(f"\n[bwd] {case} causal={causal}", flush=True)
     t = inputs(B, Hq, Hkv, S, d, seed=100 + sum(case))
@@ -169,10 +168,9 @@ def test_bwd_edge_shapes(case, causal):
     dq, dk, dv = ea.attn_bwd(t["q"], t["k"], t["v"], o, lse, t["do"], scale, causal)
     torch.cuda.synchronize()
     rdq, rdk, rdv = oracle_bwd(t, scale, causal)
-    bar = 3e-2 if Hq // Hkv >= 8 else 2e-2
-    assert_bf16_close("dq", dq, rdq, max_abs=bar, rel=EDGE_REL)
-    assert_bf16_close("dk", dk, rdk, max_abs=bar, rel=EDGE_REL)
-    assert_bf16_close("dv", dv, rdv, max_abs=bar, rel=EDGE_REL)
+    assert_bf16_close("dq", dq, rdq)
+    assert_bf16_close("dk", dk, rdk)
+    assert_bf16_close("dv", dv, rdv)
 
 
 @pytest.mark.parametrize("exp_mode", [ea.ATTN_EXP_HW, ea.ATTN_EXP_POLY3])
@@ -189,9 +187,9 @@ def test_bwd_from_oracle_forward(exp_mode, causal):
     dq, dk, dv = ea.attn_bwd_ex(t["q"], t["k"], t["v"], o, lse, t["do"], scale, causal, exp_mode=exp_mode)
     torch.cuda.synchronize()
     rdq, rdk, rdv = oracle_bwd(t, scale, causal)
-    assert_bf16_close("dq", dq, rdq, rel=EDGE_REL)
-    assert_bf16_close("dk", dk, rdk, rel=EDGE_REL)
-    assert_bf16_close("dv", dv, rdv, rel=EDGE_REL)
+    assert_bf16_close("dq", dq, rdq)
+    assert_bf16_close("dk", dk, rdk)
+    assert_bf16_close("dv", dv, rdv)
 
 
 @pytest.mark.parametrize("scale", [-0.2, 0.0, 0.4])
@@ -208,7 +206,7 @@ def test_bwd_scales(scale):
     rdq, rdk, rdv = oracle_bwd(t, scale, True)
     ratio = max(1.0, abs(scale) * d ** 0.5)
     for name, g, r in (("dq", dq, rdq), ("dk", dk, rdk), ("dv", dv, rdv)):
-        assert_bf16_close(name, g, r, max_abs=2e-2 * ratio, mean_abs=2e-3 * ratio, rel=EDGE_REL)
+        assert_bf16_close(name, g, r, max_abs=2e-2 * ratio, mean_abs=2e-3 * ratio)
 
 
 def test_bwd_gradient_identities_and_determinism():
@@ -237,20 +235,21 @@ def test_bwd_workspace_contents_do_not_matter():
     dq, dk, dv = ea.attn_bwd(t["q"], t["k"], t["v"], o, lse, t["do"], None, False, workspace=ws)
     torch.cuda.synchronize()
     rdq, rdk, rdv = oracle_bwd(t, d ** -0.5, False)
-    assert_bf16_close("dq", dq, rdq, rel=EDGE_REL)
-    assert_bf16_close("dk", dk, rdk, rel=EDGE_REL)
-    assert_bf16_close("dv", dv, rdv, rel=EDGE_REL)
+    assert_bf16_close("dq", dq, rdq)
+    assert_bf16_close("dk", dk, rdk)
+    assert_bf16_close("dv", dv, rdv)
 
 
 def test_bwd_phases_equal_whole():
-    """The three ATTN_BWD_* phases run in order equal attn_bwd, bit for bit."""
+    """The three ATTN_BWD_* phases run in their order (preprocess, dQ, dK/dV) equal
+    attn_bwd, bit for bit."""
     B, Hq, Hkv, S, d = 1, 4, 2, 260, 128
     t = inputs(B, Hq, Hkv, S, d, seed=37)
     o, lse = ea.attn_fwd(t["q"], t["k"], t["v"], None, True)
     g1 = ea.attn_bwd(t["q"], t["k"], t["v"], o, lse, t["do"], None, True)
     dq, dk, dv = torch.empty_like(t["q"]), torch.empty_like(t["k"]), torch.empty_like(t["v"])
     ws = torch.empty(ea.attn_bwd_workspace_bytes(B, Hq, Hkv, S, d), dtype=torch.uint8, device=DEV)
-    for ph in (ea.ATTN_BWD_PREPROCESS, ea.ATTN_BWD_MAIN, ea.ATTN_BWD_DQ):
+    for ph in (ea.ATTN_BWD_PREPROCESS, ea.ATTN_BWD_DQ, ea.ATTN_BWD_MAIN):
         ea.attn_bwd_phase(ph, t["q"], t["k"], t["v"], o, lse, t["do"], None, True, dq, dk, dv, ws)
     torch.cuda.synchronize()
     assert torch.equal(g1[0], dq) and torch.equal(g1[1], dk) and torch.equal(g1[2], dv)
