@@ -28,8 +28,8 @@ int check_sizes(int B, int Hq, int Hkv, int S, int d, bool* empty) {
   const int64_t tiles = ((int64_t)S + 127) / 128;
   if ((int64_t)B * Hq * tiles >= (int64_t)1 << 31) return ATTN_ERR_SHAPE;
   if ((int64_t)S * d >= (int64_t)1 << 31) return ATTN_ERR_SHAPE;
-  // The backward preprocess launches 32 workgroups per (batch, KV head).
-  if ((int64_t)B * Hkv * 32 >= (int64_t)1 << 31) return ATTN_ERR_SHAPE;
+  // The backward preprocess launches kPreBlocks workgroups per (batch, KV head).
+  if ((int64_t)B * Hkv * attn::kPreBlocks >= (int64_t)1 << 31) return ATTN_ERR_SHAPE;
   *empty = (B == 0 || S == 0);
   return ATTN_OK;
 }
@@ -69,7 +69,7 @@ bool use_pingpong(int variant, bool packed, int B, int Hq, int S) {
 
 // Backward workspace, in order, each part aligned to 256 bytes (S_pad = S rounded up to
 // 64): -D from the bf16 O, LSE log2(e), the exact -D in the dK/dV kernel's units (three fp32
-// [B*Hq][S_pad] arrays), the preprocess's partial maxima (fp32 [B*Hkv][32][4]), and dO and
+// [B*Hq][S_pad] arrays), the preprocess's partial maxima (fp32 [B*Hkv][64][4]), and dO and
 // Q in fp16 (two [B*Hq][S][d] arrays).
 struct BwdWorkspace {
   size_t delta, lse2, ndx, pmax, do16, q16, total;
@@ -82,7 +82,7 @@ BwdWorkspace bwd_workspace(int B, int Hq, int Hkv, int S, int d) {
   w.lse2 = w.delta + round_up(prows * sizeof(float));
   w.ndx = w.lse2 + round_up(prows * sizeof(float));
   w.pmax = w.ndx + round_up(prows * sizeof(float));
-  w.do16 = w.pmax + round_up((size_t)B * Hkv * 32 * 4 * sizeof(float));
+  w.do16 = w.pmax + round_up((size_t)B * Hkv * attn::kPreBlocks * 4 * sizeof(float));
   w.q16 = w.do16 + round_up((size_t)B * Hq * S * d * sizeof(uint16_t));
   w.total = w.q16 + round_up((size_t)B * Hq * S * d * sizeof(uint16_t));
   return w;

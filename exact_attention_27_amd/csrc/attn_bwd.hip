@@ -33,7 +33,6 @@ namespace {
 
 constexpr int kBwdBN = 128;  // keys per workgroup (4 waves x 32)
 constexpr int kBwdBM = 64;   // queries per step
-constexpr int kPreBlocks = 32;  // preprocess workgroups per KV group (partial maxima per group)
 
 // ------------------------------------------------------------------ preprocess
 // Rows are taken in the padded layout [B*Hq][S_pad] (S_pad = S rounded up to a multiple
@@ -74,32 +73,45 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdArgs a, int S_pad) {
   const long per = ((nrows + kPreBlocks - 1) / kPreBlocks + RPI - 1) / RPI * RPI;
   const long r_end = min(nrows, (nb + 1) * per);
   float mdo = 0.0f, mq = 0.0f;
-  for (long r0 = nb * per; r0 < r_end; r0 += RPI) {
-    const long r = r0 + tid / LPR;  // group-relative padded row
-    const int hl = (int)(r / S_pad);
-    const int srow = (int)(r - (long)hl * S_pad);
-    const bool real = r < r_end && srow < S;
-    const long row = ((long)b * a.Hq + (long)hkv * G + hl) * S + srow;  // unpadded [B*Hq][S] row
-    float acc = 0.0f;
-    if (real) {
-      const u32x4 ov = *(const u32x4*)(a.o + row * D + part * 8);
-      const u32x4 dv = *(const u32x4*)(a.dO + row * D + part * 8);
-      const u32x4 qv = *(const u32x4*)(a.q + row * D + part * 8);
+  // Two rows per thread and pass, their loads issued together.
+  for (long r0 = nb * per; r0 < r_end; r0 += 2 * RPI) {
+    long row[2];
+    bool real[2];
+    u32x4 ov[2], dv[2], qv[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const long r = r0 + u * RPI + tid / LPR;  // group-relative padded row
+      const int hl = (int)(r / S_pad);
+      const int srow = (int)(r - (long)hl * S_pad);
+      real[u] = r < r_end && srow < S;
+      row[u] = ((long)b * a.Hq + (long)hkv * G + hl) * S + srow;  // unpadded [B*Hq][S] row
+      if (real[u]) {
+        ov[u] = *(const u32x4*)(a.o + row[u] * D + part * 8);
+        dv[u] = *(const u32x4*)(a.dO + row[u] * D + part * 8);
+        qv[u] = *(const u32x4*)(a.q + row[u] * D + part * 8);
+      } else {
+        ov[u] = dv[u] = qv[u] = u32x4{0u, 0u, 0u, 0u};
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const long r = r0 + u * RPI + tid / LPR;
+      float acc = 0.0f;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const float o0 = __builtin_bit_cast(float, ov[e] << 16), o1 = __builtin_bit_cast(float, ov[e] & 0xffff0000u);
-        const float d0 = __builtin_bit_cast(float, dv[e] << 16), d1 = __builtin_bit_cast(float, dv[e] & 0xffff0000u);
+        const float o0 = __builtin_bit_cast(float, ov[u][e] << 16), o1 = __builtin_bit_cast(float, ov[u][e] & 0xffff0000u);
+        const float d0 = __builtin_bit_cast(float, dv[u][e] << 16), d1 = __builtin_bit_cast(float, dv[u][e] & 0xffff0000u);
         acc = fmaf(o0, d0, acc);
         acc = fmaf(o1, d1, acc);
       }
-      mdo = absmax8(mdo, dv);
-      mq = absmax8(mq, qv);
-    }
+      mdo = absmax8(mdo, dv[u]);
+      mq = absmax8(mq, qv[u]);
 #pragma unroll
-    for (int off = LPR / 2; off >= 1; off >>= 1) acc += __shfl_xor(acc, off);
-    if (r < r_end && part == 0) {
-      a.delta[row0 + r] = -acc;  // -D: the dQ kernel's dP products start from it
-      a.lse2[row0 + r] = real ? a.lse[row] * kLog2e : 0.0f;
+      for (int off = LPR / 2; off >= 1; off >>= 1) acc += __shfl_xor(acc, off);
+      if (r < r_end && part == 0) {
+        a.delta[row0 + r] = -acc;  // -D: the dQ kernel's dP products start from it
+        a.lse2[row0 + r] = real[u] ? a.lse[row[u]] * kLog2e : 0.0f;
+      }
     }
   }
   // K, V: the group's S rows, this workgroup's share.
@@ -669,18 +681,11 @@ void bwd_dq_kernel(BwdArgs a) {
   const size_t prow = ((size_t)b * a.Hq + hq) * (size_t)S_pad + qc;
   const float lse2 = a.lse2[prow];
   float dsum = 0.0f;  // this lane's part of sum_j dS_ij
-  // dP^T chains start from -D (from the bf16 O; every register of a lane belongs to its
-  // query), so the products give dP^T - D directly and dS^T = P^T (dP^T - D) is one
-  // multiply.  The cubic exponential needs more registers than the hardware one; its
-  // kernels keep -D in one register and subtract it in dS instead of holding the 16
-  // copies the chain start needs, which would not fit without spilling.
-  constexpr bool NEGD = EXPMODE == 0;
-  f32x16 negd = f32x16{};
+  // -D from the bf16 O (every register of a lane belongs to its query), subtracted as dS
+  // is formed.  (Starting each dP chain from -D instead saves that subtraction but holds
+  // 16 copies of it in registers, which the kernel, with the fp16 copies and the D sums it
+  // now also produces, cannot spare without spilling.)
   const float nd0 = a.delta[prow];
-  if constexpr (NEGD) {
-#pragma unroll
-    for (int v = 0; v < 16; ++v) negd[v] = nd0;
-  }
   const float c = a.scale * kLog2e;  // signed: no running maximum is needed here
 
   const int kv_end = CAUSAL ? min(S, q0 + kDqBM) : S;
@@ -770,7 +775,7 @@ void bwd_dq_kernel(BwdArgs a) {
       for (int vv = 0; vv < 8; ++vv) {
         if (vv < v0 || vv >= v1) continue;
         const int v = (u & 1) * 8 + vv;
-        const float ds = NEGD ? s[kb][v] * dp[kb][v] : s[kb][v] * (dp[kb][v] + nd0);
+        const float ds = s[kb][v] * (dp[kb][v] + nd0);
         dp[kb][v] = ds;
         dsum += ds;
         if (v & 1) dw[u][(v & 7) >> 1] = pack_bf16x2(dp[kb][v - 1], ds);
@@ -791,7 +796,7 @@ void bwd_dq_kernel(BwdArgs a) {
     for (int i = NA; i < 2 * NA; ++i) {
       issue(i + PD);
       const int k = i - NA, kb = k % KB, ks = k / KB;
-      dp[kb] = mfma32(fr[i], of[ks], ks == 0 ? negd : dp[kb]);
+      dp[kb] = mfma32(fr[i], of[ks], ks == 0 ? f32x16{} : dp[kb]);
       // P^T for a share of the 32 scores, once S^T has had a slot to finish.
       if (k >= 1) {
         const int n = NA - 1, e0 = (k - 1) * 2 * 16 / n, e1 = k * 2 * 16 / n;

@@ -29,6 +29,10 @@ struct FwdArgs {
   int total;
 };
 
+// Workgroups of the backward preprocess per (batch, KV head); each leaves one set of
+// partial maxima in the workspace (BwdArgs::pmax), so the later kernels reduce this many.
+constexpr int kPreBlocks = 64;
+
 struct BwdArgs {
   const uint16_t* q;
   const uint16_t* k;
@@ -43,7 +47,7 @@ struct BwdArgs {
   float* delta;   // [B*Hq][S_pad] fp32: -D_i = -<dO_i, O_i> from the stored bf16 O (preprocess)
   float* lse2;    // [B*Hq][S_pad] fp32: LSE_i * log2(e) (preprocess)
   float* ndx;     // [B*Hq][S_pad] fp32: -D_i = -sum_j P_ij dP_ij, times 2^(e_dO + e_V) (dQ kernel)
-  float* pmax;    // [B*Hkv][32][4] fp32: partial maxima of |dO|, |V|, |Q|, |K| per group (preprocess)
+  float* pmax;    // [B*Hkv][kPreBlocks][4] fp32: partial maxima of |dO|, |V|, |Q|, |K| per group (preprocess)
   uint16_t* do16; // [B*Hq][S][d] fp16: dO * 2^e_dO (dQ kernel), the dK/dV kernel's dO operand
   uint16_t* q16;  // [B*Hq][S][d] fp16: Q * 2^e_Q (dQ kernel), the dK/dV kernel's Q operand
   int B, Hq, Hkv, S;

@@ -159,7 +159,7 @@ int attn_fwd_varlen(const void* q, const void* k, const void* v, void* o, float*
  * bytes (S_pad = S rounded up to a multiple of 64): three fp32 row arrays [B*Hq][S_pad]
  * (the row term -D_i = -<dO_i, O_i> from the stored O, LSE_i log2(e), and -D_i formed
  * from its definition sum_j P_ij dP_ij, scaled), the preprocess's partial maxima of |dO|,
- * |V|, |Q| and |K| (fp32 [B*Hkv][32][4]), and dO scaled by a power of two per (batch, KV head) in
+ * |V|, |Q| and |K| (fp32 [B*Hkv][64][4]), and dO scaled by a power of two per (batch, KV head) in
  * fp16 ([B*Hq][S][d], 2 bytes per element), and Q likewise.  About B*Hq*S*(4d + 12) bytes.
  * Returns 0 for invalid or empty sizes.
  */

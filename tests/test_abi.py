@@ -93,11 +93,11 @@ def test_fwd_rejects_options(opt, status):
 
 def test_grid_limits():
     """Sizes whose launch grids would not fit in 31 bits are rejected before any launch
-    (the first passes every other limit but the backward preprocess grid, 32 workgroups
+    (the first passes every other limit but the backward preprocess grid, 64 workgroups
     per (batch, KV head))."""
-    assert ea.attn_bwd_workspace_bytes(1 << 26, 1, 1, 1, 64) == 0
-    assert fwd(B=1 << 26, Hq=1, Hkv=1, S=1, d=64) == SHAPE
-    assert ea.attn_bwd_workspace_bytes((1 << 26) - 1, 1, 1, 1, 64) > 0
+    assert ea.attn_bwd_workspace_bytes(1 << 25, 1, 1, 1, 64) == 0
+    assert fwd(B=1 << 25, Hq=1, Hkv=1, S=1, d=64) == SHAPE
+    assert ea.attn_bwd_workspace_bytes((1 << 25) - 1, 1, 1, 1, 64) > 0
     assert fwd(B=1, Hq=1, Hkv=1, S=1 << 24, d=128) == SHAPE  # row offsets within a head
     assert fwd(B=1 << 20, Hq=1 << 10, Hkv=1, S=1 << 8, d=64) == SHAPE
 
@@ -107,7 +107,7 @@ def test_workspace_bytes():
     rup = lambda x: (x + 255) // 256 * 256
     prows = B * Hq * ((S + 63) // 64 * 64)
     rows = 3 * rup(prows * 4)                    # -D from O, LSE log2 e, -D defined
-    maxima = rup(B * Hkv * 32 * 4 * 4)           # partial maxima of |dO|, |V|, |Q|, |K|
+    maxima = rup(B * Hkv * 64 * 4 * 4)           # partial maxima of |dO|, |V|, |Q|, |K|
     f16 = 2 * rup(B * Hq * S * d * 2)            # dO and Q in fp16
     assert ea.attn_bwd_workspace_bytes(B, Hq, Hkv, S, d) == rows + maxima + f16
     assert ea.attn_bwd_workspace_bytes(0, Hq, Hkv, S, d) == 0
