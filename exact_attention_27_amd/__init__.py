@@ -6,7 +6,7 @@ if libattn.so is missing or fails to load, every call raises.
 
 The functions carry the C names:
     attn_fwd, attn_fwd_ex, attn_fwd_varlen, attn_bwd, attn_bwd_ex, attn_bwd_phase, attn_bwd_workspace_bytes,
-    attn_default_options, attn_status_string, attn_exp2_eval, attn_exp2_poly_host
+    attn_bwd_noalloc, attn_default_options, attn_status_string, attn_exp2_eval, attn_exp2_poly_host
 """
 
 from __future__ import annotations
@@ -21,6 +21,7 @@ import torch
 __all__ = [
     "AttnError", "attn_options", "library_path", "lib",
     "attn_fwd", "attn_fwd_ex", "attn_fwd_varlen", "attn_bwd", "attn_bwd_ex", "attn_bwd_phase", "attn_bwd_workspace_bytes",
+    "attn_bwd_noalloc", "ATTN_ERR_SCRATCH",
     "attn_default_options", "attn_status_string", "attn_exp2_eval", "attn_exp2_poly_host",
     "ATTN_EXP_HW", "ATTN_EXP_POLY3", "ATTN_VARIANT_AUTO", "ATTN_VARIANT_PINGPONG", "ATTN_VARIANT_FOURWAVE",
 ]
@@ -87,6 +88,8 @@ def lib() -> ctypes.CDLL:
         L.attn_bwd_phase.restype = _I
         L.attn_bwd_phase.argtypes = [_I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I,
                                      _P, ctypes.c_size_t, ctypes.POINTER(attn_options), _P]
+        L.attn_bwd_noalloc.restype = _I
+        L.attn_bwd_noalloc.argtypes = [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _P]
         L.attn_exp2_eval.restype = _I
         L.attn_exp2_eval.argtypes = [_P, _P, ctypes.c_long, _I, _P]
         L.attn_exp2_poly_host.restype = None
@@ -315,6 +318,38 @@ def attn_bwd(q, k, v, o, lse, do, scale: Optional[float] = None, causal: bool = 
              dq=None, dk=None, dv=None, workspace=None, stream=None):
     """Backward pass with the default options (see attn_bwd_ex)."""
     return attn_bwd_ex(q, k, v, o, lse, do, scale, causal, dq, dk, dv, workspace, stream=stream)
+
+
+ATTN_ERR_SCRATCH = 8
+
+
+def attn_bwd_noalloc(q, k, v, o, lse, do, scale: Optional[float] = None, causal: bool = False,
+                     dq=None, dk=None, dv=None, stream=None):
+    """attn_bwd whose scratch is the library's static per-device buffer (64 MiB): no
+    workspace argument and no allocation in the library.  Returns (dq, dk, dv); outputs
+    not given are allocated here with torch.  Raises AttnError(ATTN_ERR_SCRATCH) for
+    problems whose workspace exceeds the buffer.  Calls that overlap in time on one GPU
+    race on the shared buffer."""
+    B, Hq, Hkv, S, d = _dims(q, k)
+    _need(q, "q", torch.bfloat16, (B, Hq, S, d))
+    _need(k, "k", torch.bfloat16, (B, Hkv, S, d))
+    _need(v, "v", torch.bfloat16, (B, Hkv, S, d))
+    _need(o, "o", torch.bfloat16, (B, Hq, S, d))
+    _need(lse, "lse", torch.float32, (B, Hq, S))
+    _need(do, "do", torch.bfloat16, (B, Hq, S, d))
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    _need(dq, "dq", torch.bfloat16, (B, Hq, S, d))
+    _need(dk, "dk", torch.bfloat16, (B, Hkv, S, d))
+    _need(dv, "dv", torch.bfloat16, (B, Hkv, S, d))
+    _same_gpu(q=q, k=k, v=v, o=o, lse=lse, do=do, dq=dq, dk=dk, dv=dv)
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    with _on(q.device):
+        st = lib().attn_bwd_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(do), _ptr(dq), _ptr(dk),
+                                    _ptr(dv), B, Hq, Hkv, S, d, scale, int(bool(causal)), _stream(stream))
+    _check(st)
+    return dq, dk, dv
 
 
 def attn_exp2_eval(x: torch.Tensor, exp_mode: int = ATTN_EXP_HW, stream=None) -> torch.Tensor:

@@ -6,6 +6,7 @@
 #include <cmath>
 #include <cstdint>
 #include <cstring>
+#include <mutex>
 
 #include "attn.h"
 #include "attn_device.h"
@@ -88,6 +89,33 @@ BwdWorkspace bwd_workspace(int B, int Hq, int Hkv, int S, int d) {
   return w;
 }
 
+// ---------------------------------------------------------------------------------
+// Scratch for attn_bwd_noalloc: a file-scope device array (each GPU the library runs on
+// holds its own copy until the process ends).  In host code `scratch` names a host-side
+// stand-in, not device memory: its device address is looked up once per device with
+// hipGetSymbolAddress (with that device current) and kept in scratch_ptr; only that
+// address is ever handed to kernels.
+constexpr size_t kScratchBytes = (size_t)64 << 20;
+constexpr int kMaxDevices = 64;
+__device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+std::mutex scratch_mu;
+void* scratch_ptr[kMaxDevices] = {};
+
+// The current device's scratch address (looked up on its first use), or an error.
+int current_scratch(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return ATTN_ERR_HIP;
+  std::lock_guard<std::mutex> lock(scratch_mu);
+  if (scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return ATTN_ERR_HIP;
+    scratch_ptr[dev] = p;
+  }
+  *out = scratch_ptr[dev];
+  return ATTN_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -110,6 +138,8 @@ const char* attn_status_string(int status) {
     case ATTN_ERR_WORKSPACE: return "ATTN_ERR_WORKSPACE: backward workspace missing, misaligned or too small";
     case ATTN_ERR_HIP: return "ATTN_ERR_HIP: the HIP runtime reported an error";
     case ATTN_ERR_VALUE: return "ATTN_ERR_VALUE: scale or tau not finite or out of range";
+    case ATTN_ERR_SCRATCH:
+      return "ATTN_ERR_SCRATCH: the backward needs more scratch than attn_bwd_noalloc's static 64 MiB";
     default: return "unknown attn status";
   }
 }
@@ -243,6 +273,27 @@ int attn_bwd_phase(int phase, const void* q, const void* k, const void* v, const
   scale_setup(scale, &a.c, &a.q_and, &a.q_xor);
   (void)hipGetLastError();
   return hip_status(attn::launch_bwd(a, d, causal != 0, o_.exp_mode, phases, static_cast<hipStream_t>(stream)));
+}
+
+int attn_bwd_noalloc(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                     const void* dO, void* dq, void* dk, void* dv,
+                     int B, int Hq, int Hkv, int S, int d, float scale, int causal, void* stream) {
+  // Every check before any HIP call, as for attn_bwd; then the size against the scratch.
+  bool empty = false;
+  int st = check_sizes(B, Hq, Hkv, S, d, &empty);
+  if (st != ATTN_OK) return st;
+  if (!std::isfinite(scale)) return ATTN_ERR_VALUE;
+  if (empty) return ATTN_OK;
+  if (!q || !k || !v || !o || !lse || !dO || !dq || !dk || !dv) return ATTN_ERR_NULL;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse) ||
+      !aligned16(dO) || !aligned16(dq) || !aligned16(dk) || !aligned16(dv))
+    return ATTN_ERR_ALIGN;
+  const size_t need = attn_bwd_workspace_bytes(B, Hq, Hkv, S, d);
+  if (need > kScratchBytes) return ATTN_ERR_SCRATCH;
+  void* ws = nullptr;
+  if ((st = current_scratch(&ws)) != ATTN_OK) return st;
+  return attn_bwd_phase(ATTN_BWD_ALL, q, k, v, o, lse, dO, dq, dk, dv, B, Hq, Hkv, S, d, scale, causal, ws,
+                        kScratchBytes, nullptr, stream);
 }
 
 int attn_bwd_ex(const void* q, const void* k, const void* v, const void* o, const float* lse,

@@ -60,7 +60,9 @@ typedef enum attn_status {
     ATTN_ERR_ALIGN = 4,       /* a tensor pointer is not 16-byte aligned          */
     ATTN_ERR_WORKSPACE = 5,   /* backward workspace NULL or smaller than required */
     ATTN_ERR_HIP = 6,         /* the HIP runtime reported an error                */
-    ATTN_ERR_VALUE = 7        /* scale (or tau) is not finite / out of range      */
+    ATTN_ERR_VALUE = 7,       /* scale (or tau) is not finite / out of range      */
+    ATTN_ERR_SCRATCH = 8      /* attn_bwd_noalloc: the problem needs more scratch
+                                 than its static buffer holds                     */
 } attn_status;
 
 /* exp2 evaluation used by the softmax. */
@@ -194,6 +196,25 @@ int attn_bwd_ex(const void* q, const void* k, const void* v, const void* o, cons
                 const void* dO, void* dq, void* dk, void* dv,
                 int B, int Hq, int Hkv, int S, int d, float scale, int causal,
                 void* workspace, size_t workspace_bytes, const attn_options* opt, void* stream);
+
+/*
+ * attn_bwd for callers that cannot allocate device memory or pass a workspace: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid allocation.  It
+ * calls no allocating routine.  Its scratch is a static device array of 64 MiB that the
+ * library holds on each GPU it runs on until the process ends (the array's device
+ * address is looked up on the first call on each device; the current device's array is
+ * used, so stream must belong to the current device).  Problems whose workspace
+ * (attn_bwd_workspace_bytes) exceeds 64 MiB return ATTN_ERR_SCRATCH before anything is
+ * launched: with d = 128 that is B * Hq * S above about 128 Ki rows (e.g. B = 1, Hq = 16,
+ * S = 7680 fits).  Every call on one GPU uses that GPU's one array, whose contents need
+ * not be cleared (the backward overwrites what it reads): calls that overlap in time on
+ * one GPU (on different streams, or from different host threads) race on it and give
+ * wrong results; calls ordered on one stream are safe.  Arguments, checks, outputs and
+ * results are those of attn_bwd with the default options.
+ */
+int attn_bwd_noalloc(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                     const void* dO, void* dq, void* dk, void* dv,
+                     int B, int Hq, int Hkv, int S, int d, float scale, int causal, void* stream);
 
 /*
  * One phase of attn_bwd_ex, for callers that schedule or time the backward's launches

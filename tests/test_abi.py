@@ -43,7 +43,7 @@ def test_default_options():
 
 
 def test_status_strings():
-    for s in range(8):
+    for s in range(9):
         assert ea.attn_status_string(s).startswith("ATTN_")
     assert "unknown" in ea.attn_status_string(99)
 
@@ -229,3 +229,25 @@ def test_bwd_binding_checks_arguments():
         ea.attn_bwd(q, k, k, q, lse, q, workspace=torch.zeros(64, dtype=torch.uint8)[::2])
     with pytest.raises(ValueError, match="must be on a GPU device"):
         ea.attn_bwd(q, k, k, q, lse, q)
+
+
+def test_noalloc_checks_before_any_hip_call():
+    """attn_bwd_noalloc validates like attn_bwd and rejects problems whose workspace
+    exceeds its static 64 MiB scratch, all before any HIP call (no GPU here)."""
+    lib = ea.lib()
+    SCRATCH = 8
+    assert ea.ATTN_ERR_SCRATCH == SCRATCH
+
+    def call(ptrs=None, B=1, Hq=2, Hkv=1, S=8, d=64, scale=0.125):
+        p = [A] * 9 if ptrs is None else ptrs
+        return lib.attn_bwd_noalloc(*p, B, Hq, Hkv, S, d, scale, 1, None)
+
+    assert call(B=0) == OK
+    assert call(Hq=3, Hkv=2) == SHAPE
+    assert call(d=80) == UNSUP
+    assert call(scale=float("inf")) == VALUE
+    assert call(ptrs=[A] * 8 + [None]) == NULL
+    assert call(ptrs=[A] * 8 + [ctypes.c_void_p(0x10008)]) == ALIGN
+    assert ea.attn_bwd_workspace_bytes(1, 16, 16, 8192, 128) > 64 << 20
+    assert call(B=1, Hq=16, Hkv=16, S=8192, d=128) == SCRATCH
+    assert "64 MiB" in ea.attn_status_string(SCRATCH)
