@@ -1,17 +1,24 @@
 """Benchmark: exact attention forward + backward on one MI355X.
 
 One step is one pass of the whole path over one batch of seeded synthetic inputs
-already resident in device memory: attn_fwd (O, LSE) then the three backward launches
-(preprocess, dK/dV main kernel, dQ kernel) giving dQ, dK, dV.
+already resident in device memory: attn_fwd (O, LSE) then the backward's three launches
+(preprocess, dQ kernel, dK/dV kernel) giving dQ, dK, dV.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+                    [--no-configs]
 
 Prints one JSON line.  value = algorithmic TFLOP/s of the step, where a step's flop
 count is fwd + bwd with fwd = 4*B*Hq*S^2*d (halved when causal) and bwd = 2.5 * fwd.
-The roofline object is for the dominant kernel (the backward dK/dV kernel, timed with
+The roofline object is for the dominant kernel (the backward's dK/dV kernel, timed with
 HIP events on the stream it runs on, inside the timed region; its algorithmic flop is
-the four products it performs, 2.0x the forward's).  cpu_baseline is the
-fp64 oracle timed on this host on a bounded sample of the same workload.
+the four products it performs, 2.0x the forward's).  "configs" adds, after the timed
+region, event-timed median and minimum per-launch times of the other headline
+configurations (the 2k prefill forward, the 32k long-context forward and the 4k
+backward) and of this workload's own passes.  "clock" is the shader clock and board
+power (amdsmi) while the same step repeats for a few seconds right after the timed region
+(amdsmi refreshes about once a second, slower than the timed region lasts); the 32k
+forward's entry has one too.  cpu_baseline is the fp64 oracle timed on this host on a
+bounded sample of the same workload.
 """
 
 import argparse
@@ -20,7 +27,9 @@ import hashlib
 import json
 import math
 import os
+import statistics
 import sys
+import threading
 import time
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
@@ -53,6 +62,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="gqa_fwd_bwd", choices=sorted(workload_names()))
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the per-configuration timings that follow the timed region")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target oracle sample time")
     ap.add_argument("--exp-mode", type=int, default=None)
     ap.add_argument("--tau", type=float, default=None)
@@ -264,6 +275,164 @@ def main_varlen(args, w):
     print(json.dumps(line), flush=True)
 
 
+class ClockSampler:
+    """Samples the shader clock (mean over the XCDs) and board power with amdsmi in a
+    background thread.  The values amdsmi reports are refreshed about once a second, so
+    they describe a load only after it has run for over a second; stats() drops the
+    first `settle_s` seconds of samples.  None where amdsmi is absent."""
+
+    def __init__(self, period_s=0.02, settle_s=1.2):
+        self.period, self.settle = period_s, settle_s
+        self.samples = []
+        self._stop = threading.Event()
+        self._thread = None
+        try:
+            import amdsmi
+            amdsmi.amdsmi_init()
+            self._smi = amdsmi
+            self._h = amdsmi.amdsmi_get_processor_handles()[0]
+        except Exception:  # noqa: BLE001
+            self._smi = None
+
+    def _run(self):
+        t0 = time.perf_counter()
+        while not self._stop.is_set():
+            try:
+                m = self._smi.amdsmi_get_gpu_metrics_info(self._h)
+                c = [x for x in m.get("current_gfxclks", []) if isinstance(x, (int, float)) and 0 < x < 10000]
+                p = m.get("current_socket_power")
+                if c:
+                    self.samples.append((time.perf_counter() - t0, sum(c) / len(c),
+                                         p if isinstance(p, (int, float)) else None))
+            except Exception:  # noqa: BLE001
+                return
+            time.sleep(self.period)
+
+    def __enter__(self):
+        if self._smi is not None:
+            self._thread = threading.Thread(target=self._run, daemon=True)
+            self._thread.start()
+        return self
+
+    def __exit__(self, *exc):
+        if self._thread is not None:
+            self._stop.set()
+            self._thread.join(timeout=5)
+        return False
+
+    def stats(self):
+        s = [x for x in self.samples if x[0] >= self.settle]
+        if not s:
+            return None
+        clk = [x[1] for x in s]
+        pwr = [x[2] for x in s if x[2] is not None]
+        out = {"sclk_mhz_mean": round(statistics.mean(clk), 1), "sclk_mhz_min": round(min(clk), 1),
+               "sclk_mhz_max": round(max(clk), 1), "samples": len(s)}
+        if pwr:
+            out["power_w_mean"] = round(statistics.mean(pwr), 1)
+        return out
+
+
+def sustained_clock(run, seconds=2.6):
+    """The shader clock and board power while `run`'s step repeats back to back for about
+    `seconds` (amdsmi refreshes its readings about once a second, too slowly for the short
+    timed region itself): the clock the timed steps run at, measured right after them."""
+    sampler = ClockSampler()
+    if sampler._smi is None:
+        return None
+    with sampler:
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 < seconds:
+            for _ in range(8):
+                run.step()
+            run.torch.cuda.synchronize()
+    st = sampler.stats()
+    if st:
+        st["source"] = (f"amdsmi current_gfxclks (mean of the XCDs) and current_socket_power, sampled while "
+                        f"the same step repeated for {seconds:.1f} s after the timed region; first "
+                        f"{sampler.settle:.1f} s dropped (amdsmi refreshes about once a second)")
+    return st
+
+
+def pass_stats(ms_list, flop):
+    """Median / min / mean per-launch time of one pass and its algorithmic rate."""
+    med, mn = statistics.median(ms_list), min(ms_list)
+    return {"ms_median": round(med, 4), "ms_min": round(mn, 4), "ms_mean": round(statistics.mean(ms_list), 4),
+            "tflops_median": round(flop / (med * 1e-3) / 1e12, 2), "tflops_best": round(flop / (mn * 1e-3) / 1e12, 2),
+            "frac_of_peak_median": round(flop / (med * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+
+
+class DenseRun:
+    """Device-resident inputs and outputs of a dense workload, and one step of the path with
+    an event after each launch (forward, then the backward's phases in their order)."""
+
+    PHASES = (("bwd_pre", "ATTN_BWD_PREPROCESS"), ("bwd_dq", "ATTN_BWD_DQ"), ("bwd_main", "ATTN_BWD_MAIN"))
+
+    def __init__(self, w, opt, with_bwd):
+        import torch
+        import exact_attention_27_amd as ea
+        import workloads
+        self.torch, self.ea, self.w, self.opt, self.with_bwd = torch, ea, w, opt, with_bwd
+        self.host = workloads.make_inputs(w)
+        t = {n: x.to("cuda:0") for n, x in self.host.items()}
+        self.q, self.k, self.v, self.do = t["q"], t["k"], t["v"], t["do"]
+        self.o = torch.empty_like(self.q)
+        self.lse = torch.empty((w.B, w.Hq, w.S), dtype=torch.float32, device="cuda:0")
+        self.dq, self.dk, self.dv = torch.empty_like(self.q), torch.empty_like(self.k), torch.empty_like(self.v)
+        nb = ea.attn_bwd_workspace_bytes(w.B, w.Hq, w.Hkv, w.S, w.d)
+        self.ws = torch.empty(max(1, nb), dtype=torch.uint8, device="cuda:0")
+        self.stream = torch.cuda.current_stream()
+        self.names = ["fwd"] + ([n for n, _ in self.PHASES] if with_bwd else [])
+
+    def step(self, ev=None):
+        ea, w, s = self.ea, self.w, self.stream
+        if ev:
+            ev[0].record(s)
+        ea.attn_fwd_ex(self.q, self.k, self.v, w.scale, w.causal, self.o, self.lse, opt=self.opt, stream=s)
+        if ev:
+            ev[1].record(s)
+        if self.with_bwd:
+            for i, (_, ph) in enumerate(self.PHASES):
+                ea.attn_bwd_phase(getattr(ea, ph), self.q, self.k, self.v, self.o, self.lse, self.do, w.scale,
+                                  w.causal, self.dq, self.dk, self.dv, self.ws, opt=self.opt, stream=s)
+                if ev:
+                    ev[2 + i].record(s)
+
+    def timed(self, steps, warmup):
+        """Runs warmup untimed steps, then `steps` steps with events; returns (wall seconds of
+        the timed steps, {launch name: [ms per step]})."""
+        torch = self.torch
+        for _ in range(warmup):
+            self.step()
+        torch.cuda.synchronize()
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(self.names) + 1)] for _ in range(steps)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(steps):
+            self.step(evs[i])
+        torch.cuda.synchronize()
+        elapsed = time.perf_counter() - t0
+        ms = {n: [e[j].elapsed_time(e[j + 1]) for e in evs] for j, n in enumerate(self.names)}
+        return elapsed, ms
+
+
+def config_entry(w, opt, steps, warmup, clock=False):
+    """Event-timed per-launch statistics of one more dense workload (after the timed region)."""
+    with_bwd = "bwd" in w.passes
+    run = DenseRun(w, opt, with_bwd)
+    _, ms = run.timed(steps, warmup)
+    out = {"shape": {"B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "S": w.S, "d": w.d, "causal": w.causal},
+           "steps": steps, "fwd": pass_stats(ms["fwd"], w.fwd_flop())}
+    if with_bwd:
+        bwd = [sum(x) for x in zip(*(ms[n] for n, _ in DenseRun.PHASES))]
+        out["bwd"] = pass_stats(bwd, w.bwd_flop())
+        out["bwd"]["phases_ms_median"] = {n: round(statistics.median(ms[n]), 4) for n, _ in DenseRun.PHASES}
+    if clock:
+        out["clock"] = sustained_clock(run)
+    del run
+    return out
+
+
 def main():
     args = parse()
     if args.copy_calibration:
@@ -283,11 +452,7 @@ def main():
     if isinstance(w, workloads.VarlenWorkload):
         main_varlen(args, w)
         return
-    dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
-    host = workloads.make_inputs(w)
-    t = {n: x.to(dev) for n, x in host.items()}
-    q, k, v, do = t["q"], t["k"], t["v"], t["do"]
+    torch.cuda.set_device(torch.device("cuda:0"))
     opt = ea.attn_default_options()
     if args.exp_mode is not None:
         opt.exp_mode = args.exp_mode
@@ -295,54 +460,21 @@ def main():
         opt.tau = args.tau
     if args.variant is not None:
         opt.variant = args.variant
-    o = torch.empty_like(q)
-    lse = torch.empty((w.B, w.Hq, w.S), dtype=torch.float32, device=dev)
-    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
-    ws = torch.empty(max(1, ea.attn_bwd_workspace_bytes(w.B, w.Hq, w.Hkv, w.S, w.d)), dtype=torch.uint8, device=dev)
     do_bwd = "bwd" in w.passes
-    stream = torch.cuda.current_stream()
+    run = DenseRun(w, opt, do_bwd)
+    host = run.host
 
-    def step(ev=None):
-        if ev:
-            ev[0].record(stream)
-        ea.attn_fwd_ex(q, k, v, w.scale, w.causal, o, lse, opt=opt, stream=stream)
-        if ev:
-            ev[1].record(stream)
-        if do_bwd:
-            for ph, e in ((ea.ATTN_BWD_PREPROCESS, 2), (ea.ATTN_BWD_DQ, 3), (ea.ATTN_BWD_MAIN, 4)):
-                ea.attn_bwd_phase(ph, q, k, v, o, lse, do, w.scale, w.causal, dq, dk, dv, ws, opt=opt, stream=stream)
-                if ev:
-                    ev[e].record(stream)
-
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    # A forward-only step is one launch: one event pair around the whole timed loop gives
-    # its average duration back to back.  The backward's phases need events between them.
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps if do_bwd else 1)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    if do_bwd:
-        for i in range(args.steps):
-            step(evs[i])
-    else:
-        evs[0][0].record(stream)
-        for i in range(args.steps):
-            step()
-        evs[0][1].record(stream)
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
+    # The timed region: exactly args.steps steps, synchronized on both sides.
+    elapsed, ms = run.timed(args.steps, args.warmup)
+    clock = None if args.no_configs else sustained_clock(run)
 
     ms_step = elapsed * 1e3 / args.steps
-    fwd_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
-    phase_ms = {}
-    if do_bwd:
-        phase_ms["bwd_pre"] = sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps
-        phase_ms["bwd_dq"] = sum(e[2].elapsed_time(e[3]) for e in evs) / args.steps
-        phase_ms["bwd_main"] = sum(e[3].elapsed_time(e[4]) for e in evs) / args.steps
-    fwd_tf = w.fwd_flop() / (fwd_ms * 1e-3) / 1e12
     flop = w.fwd_flop() + (w.bwd_flop() if do_bwd else 0.0)
     value = flop / (ms_step * 1e-3) / 1e12
+    step_ms = [sum(x) for x in zip(*ms.values())]  # event-timed launches of each step
+    fwd_ms = statistics.mean(ms["fwd"])
+    fwd_tf = w.fwd_flop() / (fwd_ms * 1e-3) / 1e12
+    phase_ms = {n: statistics.mean(ms[n]) for n, _ in DenseRun.PHASES} if do_bwd else {}
 
     if do_bwd:
         # The dK/dV kernel performs four of the backward's five counted products (S, dP,
@@ -360,14 +492,32 @@ def main():
                 "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
                 "traffic_unit": "bytes per launch (HBM, rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
                 "avg_launch_ms": round(main_ms, 4)}
+    if clock:
+        roofline["frac_at_measured_clock"] = round(achieved / (PEAK_BF16_TFLOPS * clock["sclk_mhz_mean"] / 2400.0), 4)
     breakdown = {"fwd_ms": round(fwd_ms, 4), "fwd_tflops": round(fwd_tf, 2),
-                 "fwd_frac_of_peak": round(fwd_tf / PEAK_BF16_TFLOPS, 4)}
+                 "fwd_frac_of_peak": round(fwd_tf / PEAK_BF16_TFLOPS, 4),
+                 "step_ms_median": round(statistics.median(step_ms), 4), "step_ms_min": round(min(step_ms), 4)}
     if do_bwd:
         bwd_ms = sum(phase_ms.values())
         bwd_tf = w.bwd_flop() / (bwd_ms * 1e-3) / 1e12
         breakdown.update({k + "_ms": round(v, 4) for k, v in phase_ms.items()})
         breakdown.update({"bwd_ms": round(bwd_ms, 4), "bwd_tflops": round(bwd_tf, 2),
                           "bwd_frac_of_peak": round(bwd_tf / PEAK_BF16_TFLOPS, 4)})
+    del run
+
+    # After the timed region: the other headline configurations, and this one's passes.
+    configs = None
+    if not args.no_configs:
+        configs = {}
+        own = {"fwd": pass_stats(ms["fwd"], w.fwd_flop())}
+        if do_bwd:
+            own["bwd"] = pass_stats([sum(x) for x in zip(*(ms[n] for n, _ in DenseRun.PHASES))], w.bwd_flop())
+        configs[w.name] = own
+        extra = {"prefill_fwd": (50, 10, False), "long_context_fwd": (20, 3, True), "bwd": (20, 5, False)}
+        for name, (k, wu, clk) in extra.items():
+            if name != w.name:
+                configs[name] = config_entry(get_workload(name), opt, k, wu, clk)
+                torch.cuda.empty_cache()
 
     ceiling = mfma_ceiling()
     if ceiling:
@@ -382,9 +532,11 @@ def main():
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "S": w.S, "d": w.d,
                    "causal": w.causal, "passes": "+".join(w.passes), "exp_mode": int(opt.exp_mode),
-                   "tau": float(opt.tau), "variant": VARIANT_NAMES.get(int(opt.variant), int(opt.variant)), "step_flop": flop},
+                   "tau": float(opt.tau), "variant": VARIANT_NAMES.get(int(opt.variant), int(opt.variant)),
+                   "step_flop": flop},
         "frac_of_peak": round(value / PEAK_BF16_TFLOPS, 4),
-        "roofline": roofline, "mfma_ceiling": ceiling, "breakdown": breakdown, "cpu_baseline": cpu,
+        "roofline": roofline, "clock": clock, "mfma_ceiling": ceiling, "breakdown": breakdown,
+        "configs": configs, "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
 

@@ -1,7 +1,9 @@
 """GPU parity of the packed variable-length forward (attn_fwd_varlen) against the fp64
 oracle, sequence by sequence: every sequence of a packed batch is an independent
-attention problem on its own rows (FlashAttention-2, Sections 3.1-3.2: the forward over
-one sequence; a packed batch only changes where each sequence's rows live).
+attention problem on its own rows (the prefill batches of SGLang and vLLM that the hyper.ai
+FlashAttention-4 story names as FA4's integration target hold prompts of different
+lengths; the pages give no interface, so a packed batch only changes where each
+sequence's rows live).
 
 Small cases: the oracle on every row of every (sequence, head), with ragged lengths
 including empty and one-token sequences and lengths on both sides of the 64-key and
