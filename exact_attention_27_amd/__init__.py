@@ -194,7 +194,7 @@ def attn_fwd_ex(q, k, v, scale: Optional[float] = None, causal: bool = False,
                 ) -> Tuple[torch.Tensor, torch.Tensor]:
     """Forward pass; returns (o [B,Hq,S,d] bf16, lse [B,Hq,S] fp32).  scale defaults to 1/sqrt(d).
     variant: ATTN_VARIANT_AUTO (default), ATTN_VARIANT_PINGPONG or ATTN_VARIANT_FOURWAVE (the
-    forward schedule; all give bit-identical results)."""
+    forward schedule; they round differently, each within the stated accuracy)."""
     B, Hq, Hkv, S, d = _dims(q, k)
     _need(q, "q", torch.bfloat16, (B, Hq, S, d))
     _need(k, "k", torch.bfloat16, (B, Hkv, S, d))

@@ -60,12 +60,13 @@ void scale_setup(float scale, float* c, uint32_t* q_and, uint32_t* q_xor) {
 int hip_status(hipError_t e) { return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP; }
 
 // The forward schedule a launch runs (true: ping-pong).  ATTN_VARIANT_AUTO takes the
-// ping-pong schedule for dense launches of S >= 8192 with at least one 256-query
-// workgroup per CU, where it measured 1-3% faster; on shorter sequences, small grids
-// and packed batches the 4-wave schedule measured faster.
-bool use_pingpong(int variant, bool packed, int B, int Hq, int S) {
+// four-wave schedule (32-key tiles, three waves per SIMD), which measured 2-5% faster than
+// the ping-pong schedule on causal launches from S = 2k to 64k, GQA and packed batches,
+// except for dense non-causal launches of S >= 8192 with at least one 256-query
+// workgroup per CU, where the ping-pong schedule measured about 1% faster.
+bool use_pingpong(int variant, bool packed, bool causal, int B, int Hq, int S) {
   if (variant != ATTN_VARIANT_AUTO) return variant == ATTN_VARIANT_PINGPONG;
-  return !packed && S >= 8192 && (int64_t)B * Hq * ((S + 255) / 256) >= 256;
+  return !packed && !causal && S >= 8192 && (int64_t)B * Hq * ((S + 255) / 256) >= 256;
 }
 
 // Backward workspace, in order, each part aligned to 256 bytes (S_pad = S rounded up to
@@ -169,7 +170,7 @@ int attn_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse
   a.cu_seqlens = nullptr;
   a.total = 0;
   (void)hipGetLastError();  // a stale error from earlier work is not this call's failure
-  return hip_status(attn::launch_fwd(a, d, causal != 0, o_.exp_mode, use_pingpong(o_.variant, false, B, Hq, S),
+  return hip_status(attn::launch_fwd(a, d, causal != 0, o_.exp_mode, use_pingpong(o_.variant, false, causal != 0, B, Hq, S),
                                      static_cast<hipStream_t>(stream)));
 }
 
@@ -212,7 +213,7 @@ int attn_fwd_varlen(const void* q, const void* k, const void* v, void* o, float*
   a.total = total;
   (void)hipGetLastError();
   return hip_status(attn::launch_fwd_varlen(a, d, causal != 0, o_.exp_mode,
-                                            use_pingpong(o_.variant, true, nseq, Hq, max_seqlen),
+                                            use_pingpong(o_.variant, true, causal != 0, nseq, Hq, max_seqlen),
                                             static_cast<hipStream_t>(stream)));
 }
 

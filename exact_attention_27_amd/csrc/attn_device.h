@@ -103,6 +103,15 @@ __device__ __forceinline__ float sum_halves(float x) {
 
 __device__ __forceinline__ bool wave_any(bool p) { return __builtin_amdgcn_ballot_w64(p) != 0; }
 
+// The lane's index in the wave, computed where it is called: the asm keeps the compiler
+// from computing it once and holding it in a register across a loop (for rare paths and
+// epilogues of kernels at their register limit, recomputing costs less than the register).
+__device__ __forceinline__ int lane_id_here() {
+  int l;
+  __asm__ volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l));
+  return l;
+}
+
 // ---------------------------------------------------------------------------------
 // MFMA and LDS access.
 // ---------------------------------------------------------------------------------

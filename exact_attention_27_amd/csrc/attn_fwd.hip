@@ -1,9 +1,11 @@
 // attn_fwd.hip - forward pass of exact attention on gfx950 (CDNA4).
 //
-// One workgroup of W waves (4 by default, 8 for the ping-pong schedule) owns 32 W
-// consecutive queries of one (batch, query head); each wave owns 32 of them.  The
-// workgroup walks the key/value sequence in tiles of 64 keys that are staged through LDS
-// and shared by its waves; the S x S score matrix never leaves registers (the
+// One workgroup of W waves (4 for the four-wave schedule, 8 for the ping-pong schedule)
+// owns 32 W consecutive queries of one (batch, query head); each wave owns 32 of them.
+// The workgroup walks the key/value sequence in tiles of BN keys (32 for the four-wave
+// schedule, which then fits three workgroups, three waves per SIMD, on a CU; 64 for the
+// ping-pong schedule) that are staged through LDS and shared by its waves; the S x S
+// score matrix never leaves registers (the
 // memory-traffic argument of "NVIDIA Blackwell: FlashAttention-4 Overcomes Memory
 // Bottlenecks", body paragraph, and of the hyper.ai FlashAttention-4 story).
 //
@@ -52,7 +54,15 @@
 namespace attn {
 namespace {
 
-constexpr int kFwdBN = 64;  // keys per LDS tile
+// Keys per LDS tile and waves per SIMD of a schedule.  The four-wave schedule uses
+// 32-key tiles: half the score registers of 64-key tiles, so that three waves share
+// each SIMD (168 registers each) and hide more of each other's latency.  The cubic
+// exponential needs a few registers more than that, so its four-wave kernels keep two
+// waves per SIMD.
+template <int W>
+constexpr int fwd_bn() { return W == 4 ? 32 : 64; }
+template <int W, int EXPMODE>
+constexpr int fwd_waves_per_simd() { return W == 4 && EXPMODE == 0 ? 3 : 2; }
 // Slots between an LDS read and the product that uses it: two hide the read latency
 // behind the two products in between; three or four measured slower on both schedules.
 constexpr int kFwdPD = 2;
@@ -63,10 +73,11 @@ constexpr int kFwdPD = 2;
 // workgroups share a CU.  W = 8: the staggered two-group schedule described below, one
 // workgroup per CU.
 template <int D, bool CAUSAL, int EXPMODE, bool VARLEN, int W>
-__global__ __attribute__((amdgpu_flat_work_group_size(64 * W, 64 * W), amdgpu_waves_per_eu(2, 2)))
+__global__ __attribute__((amdgpu_flat_work_group_size(64 * W, 64 * W),
+                          amdgpu_waves_per_eu(fwd_waves_per_simd<W, EXPMODE>(), fwd_waves_per_simd<W, EXPMODE>())))
 void fwd_kernel(FwdArgs a) {
   static_assert(W == 4 || W == 8, "4 or 8 waves per workgroup");
-  constexpr int BN = kFwdBN;
+  constexpr int BN = fwd_bn<W>();
   constexpr int BM = 32 * W;            // queries per workgroup
   constexpr int KB = BN / 32;           // 32-key blocks per tile
   constexpr int KSTEPS = D / 16;        // MFMA k-steps of S^T = K Q^T
@@ -219,8 +230,12 @@ void fwd_kernel(FwdArgs a) {
   // query: the only ones with masked scores.
   auto needs_mask = [&](int k0) { return (k0 + BN > S) || (CAUSAL && k0 + BN - 1 > qw); };
   auto mask = [&](f32x16* s, int k0) {
-    const int lim_s = S - 1 - k0 - half * 4;                          // key <= S - 1
-    int lim = CAUSAL ? min(lim_s, qi - k0 - half * 4) : lim_s;        // key <= query
+    // The lane's half and column, recomputed here from the lane id: kept live across the
+    // loop for this rare path they would cost registers.
+    const int ln = lane_id_here();
+    const int hf = ln >> 5;
+    const int lim_s = S - 1 - k0 - hf * 4;                                   // key <= S - 1
+    int lim = CAUSAL ? min(lim_s, qw + (ln & 31) - k0 - hf * 4) : lim_s;     // key <= query
     __asm__ volatile("" : "+v"(lim));  // keep the comparisons inside this rare path
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb)
@@ -413,8 +428,11 @@ void fwd_kernel(FwdArgs a) {
   // Epilogue: O = O_acc / l (bf16, round to nearest even) and LSE in natural log.
   const float l = sum_halves(l_run);
   const float inv = 1.0f / l;
-  if (qi < Sq) {
-    uint16_t* orow = a.o + qbase + (size_t)qi * rs_q;
+  // The lane's query and half, recomputed from the lane id (not held across the loop).
+  const int ln = lane_id_here();
+  const int qo = qw + (ln & 31), ho = ln >> 5;
+  if (qo < Sq) {
+    uint16_t* orow = a.o + qbase + (size_t)qo * rs_q;
 #pragma unroll
     for (int db = 0; db < DBLK; ++db) {
 #pragma unroll
@@ -422,10 +440,10 @@ void fwd_kernel(FwdArgs a) {
         u32x2 w;
         w[0] = pack_bf16x2(oacc[db][g * 4 + 0] * inv, oacc[db][g * 4 + 1] * inv);
         w[1] = pack_bf16x2(oacc[db][g * 4 + 2] * inv, oacc[db][g * 4 + 3] * inv);
-        *(u32x2*)(orow + db * 32 + g * 8 + half * 4) = w;
+        *(u32x2*)(orow + db * 32 + g * 8 + ho * 4) = w;
       }
     }
-    if (half == 0) a.lse[lse0 + qi] = (m_ref + log2f(l)) * kLn2;
+    if (ho == 0) a.lse[lse0 + qo] = (m_ref + log2f(l)) * kLn2;
   }
 }
 

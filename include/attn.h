@@ -92,19 +92,22 @@ enum {
  *              Technical Edge").  The result is the same for every tau; tau only
  *              bounds the unnormalised probabilities by 2^tau.  tau <= 30.
  *   variant  : forward schedule (the backward has one schedule and ignores it).
- *              ATTN_VARIANT_FOURWAVE (2): 4-wave workgroups of 128 queries, two per
- *              CU, every wave in the same phase order.  ATTN_VARIANT_PINGPONG (1):
- *              8-wave workgroups of 256 queries, one per CU, whose two 4-wave
- *              halves run half a step apart, so that of the two waves sharing a
- *              SIMD one exponentiates while the other runs matrix products (the
- *              two-team pipelining of the gist.science summary, section 2.A, and
- *              the overlap of "NVIDIA's FlashAttention-4", section "The Technical
- *              Edge").  ATTN_VARIANT_AUTO (0, the default): the ping-pong schedule
- *              for dense launches with S >= 8192 that give every CU at least one
- *              256-query workgroup (B * Hq * ceil(S / 256) >= 256), the 4-wave
- *              schedule otherwise and for packed batches (which measured faster
- *              each way).  All schedules give bit-identical results, so the choice
- *              affects speed only.  Other values: ATTN_ERR_UNSUPPORTED.
+ *              ATTN_VARIANT_FOURWAVE (2): 4-wave workgroups of 128 queries walking
+ *              32-key tiles, three per CU (three waves per SIMD), every wave in the
+ *              same phase order.  ATTN_VARIANT_PINGPONG (1): 8-wave workgroups of 256
+ *              queries walking 64-key tiles, one per CU, whose two 4-wave halves run
+ *              half a step apart, so that of the two waves sharing a SIMD one
+ *              exponentiates while the other runs matrix products (the two-team
+ *              pipelining of the gist.science summary, section 2.A, and the overlap
+ *              of "NVIDIA's FlashAttention-4", section "The Technical Edge").
+ *              ATTN_VARIANT_AUTO (0, the default): the ping-pong schedule for dense
+ *              non-causal launches with S >= 8192 that give every CU at least one
+ *              256-query workgroup (B * Hq * ceil(S / 256) >= 256), the four-wave
+ *              schedule otherwise (which measured faster each way).  The schedules
+ *              round differently (their tiles differ, and with them the rescale
+ *              points and the order of the row sums), so their results agree to the
+ *              accuracy the library states, not bit for bit; a given schedule is
+ *              deterministic.  Other values: ATTN_ERR_UNSUPPORTED.
  */
 typedef struct attn_options {
     int exp_mode;
