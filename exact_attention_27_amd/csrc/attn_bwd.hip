@@ -585,396 +585,6 @@ void bwd_main_kernel(BwdArgs a) {
   }
 }
 
-// ------------------------------------------------------------------ main, d = 128
-
-// The d = 128 dK/dV kernel.  The workgroup, step order, staging and products are those of
-// bwd_main_kernel, but the two waves that share a 32-key block split the head dimension of
-// dK and dV between them instead of the queries.  Wave w (key block kq = w % 4, role
-// h = w / 4) computes S, dP, P and dS for query half h of each 64-query step, as there,
-// and accumulates dK and dV only for d in [64 h, 64 h + 64), over all 64 queries.  Halving
-// the dK/dV accumulators (64 registers) makes room for the wave's K and V operand fragments
-// of the S and dP products in registers (64 registers, read from LDS once), so the
-// kernel's LDS operand reads fall from 48 to 32 KB per wave and step.  The price is an
-// exchange: each wave writes its fp16 P and dS to LDS (4 KB per step, in the K tile's
-// space, which the fragments free) and reads its partner's (wave w ^ 4) after a workgroup
-// barrier in the middle of the step.  Nothing is left to add up at the end.
-//
-// Slots of one step (one product each):
-//   0-7    S = Q_h K^T                      (Q from LDS, K^T fragments in registers)
-//   8-15   dP = dO_h V^T, beside P          (P then written for the partner)
-//   16-19  dV^T += dO^T P    own queries    beside dS
-//   20-21  dK^T += Q^T dS    own queries, first 16, beside dS (then written for the partner)
-//   -- barrier: the partner's P and dS are in LDS --
-//   22-23  dK^T += Q^T dS    own queries, last 16 (while the partner's operands load)
-//   24-27  dV^T += dO^T P    partner's queries
-//   28-31  dK^T += Q^T dS    partner's queries
-// Under the causal mask a wave whose key block lies wholly above its own query half skips
-// slots 0-23 and one whose partner's does skips 24-31 (that P and dS are zero); every wave
-// meets both barriers of each step.
-template <bool CAUSAL, int EXPMODE>
-__global__ __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_per_eu(2, 2)))
-void bwd_main_dsplit_kernel(BwdArgs a) {
-  constexpr int D = 128;
-  constexpr int KSTEPS = D / 16;               // 8
-  constexpr int CG = D / 32;                   // 4-chunk groups per row
-  constexpr int ROWB = D * 2;                  // bytes per row in memory
-  constexpr int KT = kBwdBN * D;               // elements of the K (or V) tile
-  constexpr int QT = kBwdBM * D;               // elements of one Q (or dO) tile
-  constexpr int KDMAS = kBwdBN / 16 * CG / 8;  // 1024-byte blocks per wave, K or V tile
-  constexpr int QDMAS = kBwdBM / 16 * CG / 8;  // 1024-byte blocks per wave, Q or dO tile
-  constexpr int PD = 2;                        // slots between an LDS read and its product
-  constexpr int NS = 4 * KSTEPS;               // slots per step
-  static_assert(KDMAS * 8 * 16 == kBwdBN * CG && QDMAS * 8 * 16 == kBwdBM * CG, "tiling");
-  // [K | V | Q stage 0 | Q stage 1 | dO stage 0 | dO stage 1 | LSE, D]; once the K and V
-  // fragments are in registers the K tile holds the P/dS exchange, [wave][P t0, P t1,
-  // dS t0, dS t1][64 lanes x 16 bytes].
-  constexpr int K_OFF = 0, V_OFF = 2 * KT, Q_OFF = 4 * KT, DO_OFF = Q_OFF + 4 * QT, SD_OFF = DO_OFF + 4 * QT;
-  constexpr int X_OFF = K_OFF;
-  static_assert(SD_OFF - Q_OFF <= 65536 && 8 * 4 * 1024 <= 2 * KT, "LDS layout");
-  __shared__ __attribute__((aligned(1024))) unsigned char smem[SD_OFF + 2 * 2 * kBwdBM * 4];
-  uint16_t* const k_lds = (uint16_t*)(smem + K_OFF);
-  uint16_t* const v_lds = (uint16_t*)(smem + V_OFF);
-  uint16_t* const q_lds[2] = {(uint16_t*)(smem + Q_OFF), (uint16_t*)(smem + Q_OFF + 2 * QT)};
-  uint16_t* const do_lds[2] = {(uint16_t*)(smem + DO_OFF), (uint16_t*)(smem + DO_OFF + 2 * QT)};
-  float (*const sd_lds)[2 * kBwdBM] = (float (*)[2 * kBwdBM])(smem + SD_OFF);  // [stage][LSE log2e | D]
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int kq = wave & 3;   // key block of this wave
-  const int dh = wave >> 2;  // its query half for S and dP, its half of d for dK and dV
-  const int col = lane & 31;
-  const int half = lane >> 5;
-  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
-  const int dh_u = wave_u >> 2;
-  const int S = a.S;
-  const int G = a.Hq / a.Hkv;
-
-  // Lowest key tiles (most query tiles under the causal mask) first.
-  const int nbh = a.B * a.Hkv;
-  const int kt = blockIdx.x / nbh;
-  const int bh = blockIdx.x % nbh;
-  const int b = bh / a.Hkv;
-  const int hkv = bh - b * a.Hkv;
-  const int k0 = kt * kBwdBN;
-  const int kw = k0 + kq * 32;
-  const int key = kw + col;  // this lane's key (column of S)
-  const size_t kvbase = ((size_t)b * a.Hkv + hkv) * (size_t)S * D;
-
-  // DMA as in bwd_main_kernel: wave w fills blocks i * 8 + w; lane l fetches row l / 4 of a
-  // block, chunk (l % 4) ^ ((l / 16) % 4); rows past the end are clamped to a real row.
-  const int dl_r = lane >> 2, dl_c = (lane & 3) ^ ((lane >> 4) & 3);
-#pragma unroll
-  for (int i = 0; i < KDMAS; ++i) {
-    const int bl = i * 8 + wave;
-    const int r = (bl / CG) * 16 + dl_r;
-    const size_t src = kvbase + (size_t)min(k0 + r, S - 1) * D + ((bl % CG) * 4 + dl_c) * 8;
-    dma16(a.k + src, k_lds + (i * 8 + wave_u) * 512);
-    dma16(a.v + src, v_lds + (i * 8 + wave_u) * 512);
-  }
-
-  const int nqt = (S + kBwdBM - 1) / kBwdBM;
-  const int q_first = CAUSAL ? (k0 / kBwdBM) : 0;
-  const int per_head = nqt - q_first;
-  const int steps = G * per_head;
-  const int S_pad = (S + kBwdBM - 1) / kBwdBM * kBwdBM;
-
-  uint32_t qd_off[QDMAS];
-#pragma unroll
-  for (int i = 0; i < QDMAS; ++i) {
-    const int bl = i * 8 + wave;
-    qd_off[i] = (uint32_t)(((bl / CG) * 16 + dl_r) * ROWB + ((bl % CG) * 4 + dl_c) * 16);
-  }
-  // Steps: query tiles from the last one down, the group's heads innermost (counters, as in
-  // bwd_main_kernel).
-  int stage_g = 0, stage_qt = nqt - 1;
-  auto stage_in = [&](int st) {
-    const int g = stage_g;
-    const int qt = stage_qt;
-    if (++stage_g == G) {
-      stage_g = 0;
-      --stage_qt;
-    }
-    const int hq = hkv * G + g;
-    const size_t rbase = ((size_t)b * a.Hq + hq) * (size_t)S;
-    const int q0 = qt * kBwdBM;
-    const char* qb = (const char*)(a.q16 + (rbase + q0) * D);
-    const char* ob = (const char*)(a.do16 + (rbase + q0) * D);
-    if (q0 + kBwdBM <= S) {
-#pragma unroll
-      for (int i = 0; i < QDMAS; ++i) {
-        dma16_s(qb, qd_off[i], q_lds[st] + (i * 8 + wave_u) * 512);
-        dma16_s(ob, qd_off[i], do_lds[st] + (i * 8 + wave_u) * 512);
-      }
-    } else {
-      int lr = dl_r;
-      __asm__ volatile("" : "+v"(lr));  // keep this rare path's row arithmetic inside it
-#pragma unroll
-      for (int i = 0; i < QDMAS; ++i) {
-        const int row = ((i * 8 + wave) / CG) * 16 + lr;  // row within the tile
-        const int rc = min(q0 + row, S - 1) - q0;
-        const uint32_t off = qd_off[i] + (uint32_t)((rc - row) * ROWB);
-        dma16_s(qb, off, q_lds[st] + (i * 8 + wave_u) * 512);
-        dma16_s(ob, off, do_lds[st] + (i * 8 + wave_u) * 512);
-      }
-    }
-    if (wave_u < 2) {
-      const size_t pbase = ((size_t)b * a.Hq + hq) * (size_t)S_pad + q0;
-      const void* src = uniform_ptr((wave_u == 0 ? a.lse2 : a.ndx) + pbase);
-      if (lane < 16) dma16_s(src, (uint32_t)lane * 16u, &sd_lds[st][wave_u * kBwdBM]);
-    }
-  };
-
-  // Per-lane LDS byte offsets.  Q / dO rows of the wave's query half (S and dP products):
-  // chunk ks*2 + half, one register per parity of ks, the rest by (ks / 2) * 1024.
-  const int ra0 = opaque(Q_OFF + blk_chunk_inner_x<D>(dh * 32 + col, half));
-  const int ra1 = opaque(Q_OFF + blk_chunk_inner_x<D>(dh * 32 + col, 2 + half));
-  // Transpose reads of dO^T and Q^T: source lane s reads 4 d-values of query row
-  // T*16 + (s / 32) * 4 + (s % 16) / 4 (+ 8 for the second read) of query block T at
-  // column 16 * ((s / 16) % 2) + 4 * (s % 4) of d block db (in this wave's half of d).
-  // "own" bases point at the wave's own query blocks (T = 2 dh + t), "partner" bases at
-  // the other half's (T = 2 (1 - dh) + t); the rest is (t * CG + db) * 1024.
-  const int trow = (lane >> 5) * 4 + ((lane >> 2) & 3);
-  const int tcl = ((lane >> 4) & 1) * 2 + ((lane >> 1) & 1);
-  const int tb0 = Q_OFF + (trow * 4 + (tcl ^ ((trow >> 2) & 3))) * 16 + (lane & 1) * 8;
-  const int tb1 = Q_OFF + ((trow + 8) * 4 + (tcl ^ (((trow + 8) >> 2) & 3))) * 16 + (lane & 1) * 8;
-  const int t_own = (2 * dh * CG + 2 * dh) * 1024, t_par = (2 * (1 - dh) * CG + 2 * dh) * 1024;
-  const int to0 = opaque(tb0 + t_own), to1 = opaque(tb1 + t_own);
-  const int tp0 = opaque(tb0 + t_par), tp1 = opaque(tb1 + t_par);
-  // P / dS exchange: this wave's slots and its partner's.
-  const int xw = opaque(X_OFF + wave * 4096 + lane * 16);
-  const int xr = opaque(X_OFF + (wave ^ 4) * 4096 + lane * 16);
-
-  f32x16 dk_acc[2], dv_acc[2];  // d blocks 2 dh, 2 dh + 1
-#pragma unroll
-  for (int db = 0; db < 2; ++db) {
-    dk_acc[db] = f32x16{};
-    dv_acc[db] = f32x16{};
-  }
-  const GroupScales gs = group_scales(a.pmax, bh);
-  const float c = ldexpf(a.scale * kLog2e, -(gs.e_q + gs.e_k));
-  bf16x8 kvf[2 * KSTEPS];  // K^T (S) and V^T (dP) operand fragments of this wave's keys
-
-  // One step on stage ST.  own / par: this wave's / its partner's query half has visible
-  // keys of this wave's block.
-  auto compute = [&](const int q0, auto stage, auto masked, const bool own, const bool par) {
-    constexpr int ST = decltype(stage)::value;
-    constexpr bool MASKED = decltype(masked)::value;
-    constexpr int QS = ST * 2 * QT, OS = DO_OFF - Q_OFF + ST * 2 * QT;
-    const char* L = (const char*)smem;
-    const float* sd = sd_lds[ST];
-    int lim_c = -1, lim_s = 64;
-    if constexpr (MASKED) {
-      const int qb = q0 + dh * 32 + half * 4;
-      lim_s = S - qb;
-      lim_c = key >= S ? 64 : (CAUSAL ? key - qb : -1);
-    }
-
-    bf16x8 fa[2 * KSTEPS];  // Q / dO row fragments of slots 0-15
-    i16x4 tlo[NS], thi[NS];  // transpose-read halves of slots 16-31
-    f32x4 l4[4], d4[4];      // LSE log2e and -D of this lane's 16 query rows
-    auto issue = [&](const int i) {
-      if (i < 2 * KSTEPS) {
-        const int ks = i % KSTEPS;
-        fa[i] = *(const bf16x8*)(L + ((ks & 1) ? ra1 : ra0) + (i < KSTEPS ? QS : OS) + (ks >> 1) * 1024);
-      } else if (i < NS) {
-        const int p = i - 2 * KSTEPS, grp = p / 4, t = (p % 4) / 2, db = p % 2;
-        const int o = ((grp & 1) ? QS : OS) + (t * CG + db) * 1024;
-        tlo[i] = lds_read_tr16((const uint16_t*)(L + (grp < 2 ? to0 : tp0) + o));
-        thi[i] = lds_read_tr16((const uint16_t*)(L + (grp < 2 ? to1 : tp1) + o));
-      }
-      if (i < 4) l4[i] = *(const f32x4*)(&sd[dh * 32 + i * 8 + half * 4]);
-      if (i >= KSTEPS - 4 && i < KSTEPS) {
-        const int g4 = i - (KSTEPS - 4);
-        d4[g4] = *(const f32x4*)(&sd[kBwdBM + dh * 32 + g4 * 8 + half * 4]);
-      }
-    };
-
-    f32x16 sacc = f32x16{}, dpacc;
-    uint32_t pw[2][4], sw[2][4];  // P and dS packed to fp16 pairs: [t][pair], registers v = 8t ..
-    // dS for registers [v0, v1) (P in sacc, dP - D in dpacc).
-    auto ds_regs = [&](const int v0, const int v1) {
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        if (v < v0 || v >= v1) continue;
-        const float ds = sacc[v] * dpacc[v];
-        dpacc[v] = ds;
-        if (v & 1) sw[v >> 3][(v & 7) >> 1] = pack_f16x2(dpacc[v - 1], ds);
-      }
-    };
-    auto own_dk = [&](const int i) {  // slots 20-23
-      const int p = i - 20, t = p / 2, db = p % 2;
-      const u32x4 w = {sw[t][0], sw[t][1], sw[t][2], sw[t][3]};
-      dk_acc[db] = mfma32_f16(join(tlo[i], thi[i]), __builtin_bit_cast(bf16x8, w), dk_acc[db]);
-    };
-    if (own) {
-#pragma unroll
-      for (int i = 0; i < PD; ++i) issue(i);
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int i = 0; i < 22; ++i) {
-        issue(i + PD);
-        if (i < KSTEPS) {
-          sacc = mfma32_f16(fa[i], kvf[i], sacc);
-        } else if (i < 2 * KSTEPS) {
-          if (i == KSTEPS) {
-            const f32x16 nd = {d4[0][0], d4[0][1], d4[0][2], d4[0][3], d4[1][0], d4[1][1], d4[1][2], d4[1][3],
-                               d4[2][0], d4[2][1], d4[2][2], d4[2][3], d4[3][0], d4[3][1], d4[3][2], d4[3][3]};
-            dpacc = mfma32_f16(fa[i], kvf[i], nd);
-          } else {
-            dpacc = mfma32_f16(fa[i], kvf[i], dpacc);
-          }
-          // P for a share of the 16 registers, once S has had two slots to finish.
-          const int j = i - KSTEPS - 2;
-          if (j >= 0) {
-            const int n = KSTEPS - 2, e0 = j * 16 / n, e1 = (j + 1) * 16 / n;
-#pragma unroll
-            for (int v = 0; v < 16; ++v) {
-              if (v < e0 || v >= e1) continue;
-              float p = exp2_sm<EXPMODE>(fmaf(sacc[v], c, -l4[v >> 2][v & 3]));
-              if constexpr (MASKED) {
-                const int ev = (v >> 2) * 8 + (v & 3);
-                p = (ev < lim_c || ev >= lim_s) ? 0.0f : p;
-              }
-              sacc[v] = p;
-              if (v & 1) pw[v >> 3][(v & 7) >> 1] = pack_f16x2(sacc[v - 1], p);
-            }
-          }
-          if (i == 2 * KSTEPS - 1) {
-            // P for the partner.
-            *(u32x4*)((char*)smem + xw) = u32x4{pw[0][0], pw[0][1], pw[0][2], pw[0][3]};
-            *(u32x4*)((char*)smem + xw + 1024) = u32x4{pw[1][0], pw[1][1], pw[1][2], pw[1][3]};
-          }
-        } else if (i < 20) {
-          const int p = i - 2 * KSTEPS, t = p / 2, db = p % 2;
-          const u32x4 w = {pw[t][0], pw[t][1], pw[t][2], pw[t][3]};
-          dv_acc[db] = mfma32_f16(join(tlo[i], thi[i]), __builtin_bit_cast(bf16x8, w), dv_acc[db]);
-          // dS, once dP has had two slots to finish: registers 0-7 here, 8-15 in slots 20-21.
-          if (p >= 2) ds_regs((p - 2) * 4, (p - 1) * 4);
-        } else {
-          own_dk(i);
-          ds_regs(8 + (i - 20) * 4, 12 + (i - 20) * 4);
-        }
-        __builtin_amdgcn_sched_barrier(0);
-      }
-      // dS for the partner.
-      *(u32x4*)((char*)smem + xw + 2048) = u32x4{sw[0][0], sw[0][1], sw[0][2], sw[0][3]};
-      *(u32x4*)((char*)smem + xw + 3072) = u32x4{sw[1][0], sw[1][1], sw[1][2], sw[1][3]};
-    }
-    __syncthreads();  // every wave's P and dS of this step are in LDS
-    u32x4 xp[2], xs[2];
-    if (par) {
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        xp[t] = *(const u32x4*)((const char*)smem + xr + t * 1024);
-        xs[t] = *(const u32x4*)((const char*)smem + xr + 2048 + t * 1024);
-      }
-      issue(24);
-      issue(25);
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    if (own) {
-      own_dk(22);
-      __builtin_amdgcn_sched_barrier(0);
-      own_dk(23);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    if (par) {
-#pragma unroll
-      for (int i = 24; i < NS; ++i) {
-        issue(i + PD);
-        const int p = i - 24, t = (p % 4) / 2, db = p % 2;
-        if (p < 4) {
-          dv_acc[db] = mfma32_f16(join(tlo[i], thi[i]), __builtin_bit_cast(bf16x8, xp[t]), dv_acc[db]);
-        } else {
-          dk_acc[db] = mfma32_f16(join(tlo[i], thi[i]), __builtin_bit_cast(bf16x8, xs[t]), dk_acc[db]);
-        }
-        __builtin_amdgcn_sched_barrier(0);
-      }
-    }
-  };
-
-  int step_g = 0, step_qt = nqt - 1;
-  auto do_step = [&](const int step, auto stage) {
-    constexpr int ST = decltype(stage)::value;
-    wait_dma();
-    __syncthreads();  // this step's Q, dO, LSE, D are in LDS; every wave is done with the previous stage
-    if (step + 1 < steps) stage_in(ST ^ 1);
-    const int qt = step_qt;
-    if (++step_g == G) {
-      step_g = 0;
-      --step_qt;
-    }
-    const int q0 = qt * kBwdBM;
-    const int qs = q0 + dh_u * 32;        // first query of this wave's half
-    const int qp = q0 + (1 - dh_u) * 32;  // and of its partner's
-    const bool own = !CAUSAL || kw <= qs + 31;
-    const bool par = !CAUSAL || kw <= qp + 31;
-    const bool need_mask = (kw + 32 > S) || (qs + 32 > S) || (CAUSAL && kw + 31 > qs);
-    if (need_mask) {
-      compute(q0, stage, std::true_type{}, own, par);
-    } else {
-      compute(q0, stage, std::false_type{}, own, par);
-    }
-  };
-
-  if (steps > 0) stage_in(0);
-  // K and V into fp16 in place (times 2^e_k, 2^e_v, exact), then this wave's operand
-  // fragments into registers; the K tile's space then holds the P/dS exchange.
-  wait_dma();
-  __syncthreads();  // K and V are in LDS
-  {
-    const float sk = ldexpf(1.0f, gs.e_k), sv = ldexpf(1.0f, gs.e_v);
-    u32x4* kk = (u32x4*)k_lds;
-    u32x4* vv = (u32x4*)v_lds;
-#pragma unroll
-    for (int i = 0; i < KT / 8 / 512; ++i) {
-      kk[i * 512 + tid] = bf16x8_to_f16x8(kk[i * 512 + tid], sk);
-      vv[i * 512 + tid] = bf16x8_to_f16x8(vv[i * 512 + tid], sv);
-    }
-  }
-  __syncthreads();  // the converted K and V are in LDS
-  {
-    const int rb0 = K_OFF + blk_chunk_inner_x<D>(kq * 32 + col, half);
-    const int rb1 = K_OFF + blk_chunk_inner_x<D>(kq * 32 + col, 2 + half);
-#pragma unroll
-    for (int i = 0; i < 2 * KSTEPS; ++i) {
-      const int ks = i % KSTEPS;
-      const int bo = (i < KSTEPS ? 0 : V_OFF - K_OFF) + (ks >> 1) * 1024;
-      kvf[i] = *(const bf16x8*)((const char*)smem + ((ks & 1) ? rb1 : rb0) + bo);
-    }
-  }
-  // (the first step's barrier orders these reads before any write to the exchange)
-  for (int step = 0; step < steps; step += 2) {
-    do_step(step, std::integral_constant<int, 0>{});
-    if (step + 1 < steps) do_step(step + 1, std::integral_constant<int, 1>{});
-  }
-
-  if (key < S) {
-    // dK = scale 2^-(e_do + e_v) (2^-e_q acc), in two factors that each stay in range.
-    const float kqs = ldexpf(1.0f, -gs.e_q);
-    const float ks = ldexpf(a.scale, -(gs.e_do + gs.e_v));
-    const float vs = ldexpf(1.0f, -gs.e_do);
-    const int ln = lane_id_here();
-    const int hf = ln >> 5;
-    uint16_t* dkr = a.dk + kvbase + (size_t)key * D + dh * 64;
-    uint16_t* dvr = a.dv + kvbase + (size_t)key * D + dh * 64;
-#pragma unroll
-    for (int db = 0; db < 2; ++db) {
-#pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        u32x2 wk, wv;
-        wk[0] = pack_bf16x2(dk_acc[db][g4 * 4 + 0] * kqs * ks, dk_acc[db][g4 * 4 + 1] * kqs * ks);
-        wk[1] = pack_bf16x2(dk_acc[db][g4 * 4 + 2] * kqs * ks, dk_acc[db][g4 * 4 + 3] * kqs * ks);
-        wv[0] = pack_bf16x2(dv_acc[db][g4 * 4 + 0] * vs, dv_acc[db][g4 * 4 + 1] * vs);
-        wv[1] = pack_bf16x2(dv_acc[db][g4 * 4 + 2] * vs, dv_acc[db][g4 * 4 + 3] * vs);
-        *(u32x2*)(dkr + db * 32 + g4 * 8 + hf * 4) = wk;
-        *(u32x2*)(dvr + db * 32 + g4 * 8 + hf * 4) = wv;
-      }
-    }
-  }
-}
-
 // ------------------------------------------------------------------ dQ
 // dQ without atomics: one workgroup of 4 waves owns 128 queries of one (batch, query
 // head) and walks the key tiles (64 keys, staged in LDS by DMA, double-buffered) that its
@@ -1310,13 +920,8 @@ hipError_t launch_bwd_t(const BwdArgs& a, int phases, hipStream_t stream) {
   }
   if (phases & 2) {
     const int nkt = (a.S + kBwdBN - 1) / kBwdBN;
-    if constexpr (D == 128) {
-      hipLaunchKernelGGL((bwd_main_dsplit_kernel<CAUSAL, EXPMODE>), dim3((unsigned)(nkt * a.B * a.Hkv)), dim3(512), 0,
-                         stream, a);
-    } else {
-      hipLaunchKernelGGL((bwd_main_kernel<D, CAUSAL, EXPMODE>), dim3((unsigned)(nkt * a.B * a.Hkv)), dim3(512), 0,
-                         stream, a);
-    }
+    hipLaunchKernelGGL((bwd_main_kernel<D, CAUSAL, EXPMODE>), dim3((unsigned)(nkt * a.B * a.Hkv)), dim3(512), 0,
+                       stream, a);
     e = hipGetLastError();
   }
   return e;
