@@ -208,8 +208,8 @@ __device__ __forceinline__ u32x4 bf16x8_to_f16x8(u32x4 w, float sc) {
 // w + 4 accumulate partial dK and dV for the same keys over different queries, and
 // the two partials are added through LDS at the end.
 //
-// K, V (resident; with d = 64 each wave also holds its K and V operand fragments in
-// registers) and the Q, dO stages sit in LDS as XOR chunk-inner blocks (see
+// K, V (resident; each wave also holds its operand fragments of K, and with d = 64 of V,
+// in registers) and the Q, dO stages sit in LDS as XOR chunk-inner blocks (see
 // attn_device.h): MFMA-operand reads of 16 rows at one chunk and the transpose reads of
 // dO^T and Q^T are both free of bank conflicts, every lane keeps a few base addresses
 // and the rest are immediate offsets, and each 4 DMA lanes fetch one 64-byte piece of a
@@ -354,6 +354,10 @@ void bwd_main_kernel(BwdArgs a) {
   const int tq = Q_OFF + (2 * qh * CG) * 1024 + (lane & 1) * 8;
   const int tr0 = opaque(tq + (trow * 4 + (tcl ^ ((trow >> 2) & 3))) * 16);
   const int tr1 = opaque(tq + ((trow + 8) * 4 + (tcl ^ (((trow + 8) >> 2) & 3))) * 16);
+  // LSE log2e and -D of the lane's query rows: one base (the area lies past the 16-bit
+  // immediate range of the other bases), every stage and row group by an immediate offset.
+  const int sdb = opaque(SD_OFF + (qh * 32 + half * 4) * 4);
+  static_assert(2 * 2 * kBwdBM * 4 <= 65536, "immediate LDS offsets");
 
   f32x16 dk_acc[DBLK], dv_acc[DBLK];
 #pragma unroll
@@ -367,13 +371,14 @@ void bwd_main_kernel(BwdArgs a) {
   const GroupScales gs = group_scales(a.pmax, bh);
   const float c = ldexpf(a.scale * kLog2e, -(gs.e_q + gs.e_k));
 
-  // With d = 64 the wave's K and V operand fragments of the S and dP products fit in
-  // registers beside everything else (32 of them): they are read from LDS once, after the
-  // fp16 conversion, instead of once per step (a third of the kernel's LDS reads; the
-  // kernel runs 5-8% faster).  With d = 128 they would take 64 registers more than the
-  // two-waves-per-SIMD budget has.
-  constexpr bool KV_REGS = D == 64;
-  bf16x8 kvf[KV_REGS ? 2 * KSTEPS : 1];
+  // The wave's operand fragments of K (S products) and, with d = 64, of V (dP products)
+  // stay in registers for the whole run: they are read from LDS once, after the fp16
+  // conversion, instead of once per step.  With d = 64 that is 32 registers and a third of
+  // the kernel's LDS reads (the kernel runs 5-8% faster); with d = 128, K's 32 registers
+  // are what the two-waves-per-SIMD budget has left (a sixth of the LDS reads, 2.5-4.5%
+  // faster), and the cubic exponential's few extra registers leave no room for them.
+  constexpr int NKV = D == 64 ? 2 * KSTEPS : (EXPMODE == 0 ? KSTEPS : 0);  // fragments held
+  bf16x8 kvf[NKV > 0 ? NKV : 1];
   // One step on stage ST; MASKED adds the causal / end-of-sequence mask to P.
   auto compute = [&](const int q0, auto stage, auto masked) {
     constexpr int ST = decltype(stage)::value;
@@ -381,7 +386,6 @@ void bwd_main_kernel(BwdArgs a) {
     // Tile offsets from the lane bases (ra*, tr* hold Q stage 0; rb* hold K).
     constexpr int QS = ST * 2 * QT, OS = DO_OFF - Q_OFF + ST * 2 * QT, VS = V_OFF - K_OFF;
     const char* L = (const char*)smem;
-    const float* sd = sd_lds[ST];
     // Mask (MASKED only): register v holds query qb + e_v, e_v = (v/4)*8 + v%4, with
     // qb = q0 + qh*32 + half*4; P = 0 where e_v < lim_c (key > query) or e_v >= lim_s
     // (query past the end), and everywhere if the key is past the end.
@@ -395,13 +399,20 @@ void bwd_main_kernel(BwdArgs a) {
     bf16x8 fa[NS], fb[NS];  // operand fragments of phase A/B slots
     i16x4 tlo[NS], thi[NS];   // transpose-read halves of phase C/D slots
     f32x4 l4[4], d4[4];       // LSE log2e and D of this lane's 16 query rows
+    // The slot that computes P of register v: registers [j 16 / n, (j + 1) 16 / n) in slot
+    // KSTEPS + 2 + j, n = KSTEPS - 2 (two slots after the last S product).
+    auto p_slot = [](const int v) {
+      int j = 0;
+      while ((j + 1) * 16 / (KSTEPS - 2) <= v) ++j;
+      return KSTEPS + 2 + j;
+    };
     auto issue = [&](const int i) {
       if (i < 2 * KSTEPS) {
         const int ks = i % KSTEPS;
         const int o = (ks >> 1) * 1024;
         const int ao = (i < KSTEPS ? QS : OS) + o, bo = (i < KSTEPS ? 0 : VS) + o;
         fa[i] = *(const bf16x8*)(L + ((ks & 1) ? ra1 : ra0) + ao);
-        if constexpr (KV_REGS) {
+        if (i < NKV) {
           fb[i] = kvf[i];
         } else {
           fb[i] = *(const bf16x8*)(L + ((ks & 1) ? rb1 : rb0) + bo);
@@ -412,12 +423,17 @@ void bwd_main_kernel(BwdArgs a) {
         tlo[i] = lds_read_tr16((const uint16_t*)(L + tr0 + o));
         thi[i] = lds_read_tr16((const uint16_t*)(L + tr1 + o));
       }
-      if (i < 4) l4[i] = *(const f32x4*)(&sd[qh * 32 + i * 8 + half * 4]);
+      // LSE log2e of the rows of registers 4 g4 .. 4 g4 + 3, two slots before the first
+      // slot whose share of the P computation (below) needs them: loaded late, so that the
+      // 16 registers are not held through the S products.
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4)
+        if (i == p_slot(4 * g4)) l4[g4] = *(const f32x4*)(L + sdb + ST * 512 + g4 * 32);
       // -D of the lane's 16 query rows, in the accumulator's register order: the first dP
       // product takes it as its accumulator input, so the chain ends at dP - D.
       if (i >= KSTEPS - 4 && i < KSTEPS) {
         const int g4 = i - (KSTEPS - 4);
-        d4[g4] = *(const f32x4*)(&sd[kBwdBM + qh * 32 + g4 * 8 + half * 4]);
+        d4[g4] = *(const f32x4*)(L + sdb + ST * 512 + kBwdBM * 4 + g4 * 32);
       }
     };
 
@@ -520,10 +536,10 @@ void bwd_main_kernel(BwdArgs a) {
       vv[i * 512 + tid] = bf16x8_to_f16x8(vv[i * 512 + tid], sv);
     }
   }
-  if constexpr (KV_REGS) {
+  if constexpr (NKV > 0) {
     __syncthreads();  // the converted K and V are in LDS
 #pragma unroll
-    for (int i = 0; i < 2 * KSTEPS; ++i) {
+    for (int i = 0; i < NKV; ++i) {
       const int ks = i % KSTEPS;
       const int bo = (i < KSTEPS ? 0 : V_OFF - K_OFF) + (ks >> 1) * 1024;
       kvf[i] = *(const bf16x8*)((const char*)smem + ((ks & 1) ? rb1 : rb0) + bo);
