@@ -16,6 +16,10 @@
 //   hipcc --offload-arch=gfx950 -O3 -o /tmp/mfma_ceiling <repo>/exact_attention_27_amd/csrc/probes/mfma_ceiling.hip
 //   /tmp/mfma_ceiling           both operand sets, twice, as text
 //   /tmp/mfma_ceiling --json    the random set once, as one JSON line (what bench.py reads)
+//   /tmp/mfma_ceiling --chain   constant operands, one wave per SIMD, one dependent
+//                               accumulation chain per wave against four independent ones
+//                               (and two waves per SIMD with four): whether back-to-back
+//                               products on one accumulator cost issue rate
 #include <hip/hip_runtime.h>
 
 #include <cstdio>
@@ -60,6 +64,47 @@ void mfma_loop(const u32x4* src, float* out, int iters) {
   out[blockIdx.x * 256 + threadIdx.x] = s;
 }
 
+// One wave per SIMD (96 KiB of LDS: one workgroup per CU), NACC accumulators: NACC = 1
+// makes every product depend on the one before it.
+template <int NACC, int LDS_FLOATS>
+__global__ __launch_bounds__(256) void mfma_chain(float* out, int iters) {
+  __shared__ float pad[LDS_FLOATS];
+  pad[threadIdx.x] = 0.f;
+  __syncthreads();
+  bf16x8 a;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) a[e] = (__bf16)(0.01f * (float)((threadIdx.x + e) & 7));
+  f32x16 acc[NACC] = {};
+  for (int i = 0; i < iters; ++i) {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) acc[k % NACC] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, a, acc[k % NACC], 0, 0, 0);
+  }
+  float s = pad[(threadIdx.x + 1) & 255];
+#pragma unroll
+  for (int j = 0; j < NACC; ++j)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) s += acc[j][v];
+  out[blockIdx.x * 256 + threadIdx.x] = s;
+}
+
+template <int NACC, int LDS_FLOATS>
+bool run_chain(const char* name, float* out, int blocks) {
+  const int iters = 4096;
+  hipEvent_t e0, e1;
+  if (hipEventCreate(&e0) != hipSuccess || hipEventCreate(&e1) != hipSuccess) return false;
+  hipLaunchKernelGGL((mfma_chain<NACC, LDS_FLOATS>), dim3(blocks), dim3(256), 0, 0, out, iters);
+  if (hipEventRecord(e0, 0) != hipSuccess) return false;
+  for (int r = 0; r < 8; ++r) hipLaunchKernelGGL((mfma_chain<NACC, LDS_FLOATS>), dim3(blocks), dim3(256), 0, 0, out, iters);
+  if (hipEventRecord(e1, 0) != hipSuccess || hipEventSynchronize(e1) != hipSuccess) return false;
+  float ms = 0.f;
+  if (hipEventElapsedTime(&ms, e0, e1) != hipSuccess) return false;
+  const double products = 8.0 * blocks * 4 * (double)iters * 8;
+  std::printf("%-40s %8.2f ms for 8 launches, %7.1f TFLOP/s bf16 dense\n", name, ms,
+              products * 32768.0 / (ms * 1e-3) / 1e12);
+  std::fflush(stdout);
+  return true;
+}
+
 template <bool RANDOM>
 bool run(const char* name, const u32x4* src, float* out, int iters, bool json = false) {
   hipEvent_t e0, e1;
@@ -85,6 +130,19 @@ bool run(const char* name, const u32x4* src, float* out, int iters, bool json = 
 
 int main(int argc, char** argv) {
   const bool json = argc > 1 && std::strcmp(argv[1], "--json") == 0;
+  if (argc > 1 && std::strcmp(argv[1], "--chain") == 0) {
+    float* out = nullptr;
+    if (hipMalloc(&out, (size_t)kBlocks * 256 * 4) != hipSuccess) return 1;
+    // Twice, so that the second round runs at the settled clock.
+    bool ok = true;
+    for (int r = 0; r < 2 && ok; ++r) {
+      ok = run_chain<1, 24576>("1 wave/SIMD, 1 dependent chain", out, kBlocks / 2) &&
+           run_chain<4, 24576>("1 wave/SIMD, 4 independent chains", out, kBlocks / 2) &&
+           run_chain<4, 16384>("2 waves/SIMD, 4 independent chains", out, kBlocks);
+    }
+    ok = ok && hipDeviceSynchronize() == hipSuccess;
+    return ok ? 0 : 1;
+  }
   static unsigned short h[kFragWords * 8];
   unsigned st = 12345u;
   for (int i = 0; i < kFragWords * 8; ++i) {
