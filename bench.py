@@ -12,9 +12,11 @@ count is fwd + bwd with fwd = 4*B*Hq*S^2*d (halved when causal) and bwd = 2.5 * 
 The roofline object is for the dominant kernel (the backward's dK/dV kernel, timed with
 HIP events on the stream it runs on, inside the timed region; its algorithmic flop is
 the four products it performs, 2.0x the forward's).  "configs" adds, after the timed
-region, event-timed median and minimum per-launch times of the other headline
-configurations (the 2k prefill forward, the 32k long-context forward and the 4k
-backward) and of this workload's own passes.  "clock" is the shader clock and board
+region, median and minimum per-launch times of the other headline configurations (the
+2k prefill forward, the 32k long-context forward and the 4k backward), each timed over
+groups of back-to-back calls with one event pair per group (an event pair around every
+call would add the events' own cost to each 0.08 ms prefill launch), and of this
+workload's own passes (from the timed steps' per-launch events).  "clock" is the shader clock and board
 power (amdsmi) while the same step repeats for a few seconds right after the timed region
 (amdsmi refreshes about once a second, slower than the timed region lasts); the 32k
 forward's entry has one too.  cpu_baseline is the fp64 oracle timed on this host on a
@@ -415,17 +417,56 @@ class DenseRun:
         ms = {n: [e[j].elapsed_time(e[j + 1]) for e in evs] for j, n in enumerate(self.names)}
         return elapsed, ms
 
+    def grouped(self, reps, target_ms=2.0):
+        """Per-launch times of the forward, and of the whole backward, over groups of
+        back-to-back calls: one event pair around each group of g calls (g chosen so that a
+        group lasts about target_ms), `reps` groups.  An event pair around every single call
+        adds the events' own cost to each launch (several microseconds, which a 0.08 ms
+        launch feels); grouped calls measure what a stream of calls sustains.  Returns
+        {"fwd": [ms per call], "bwd": [ms per call]} (bwd only for backward workloads)."""
+        torch, ea, w, s = self.torch, self.ea, self.w, self.stream
+
+        def fwd():
+            ea.attn_fwd_ex(self.q, self.k, self.v, w.scale, w.causal, self.o, self.lse, opt=self.opt, stream=s)
+
+        def bwd():
+            for _, ph in self.PHASES:
+                ea.attn_bwd_phase(getattr(ea, ph), self.q, self.k, self.v, self.o, self.lse, self.do, w.scale,
+                                  w.causal, self.dq, self.dk, self.dv, self.ws, opt=self.opt, stream=s)
+
+        out = {}
+        for name, fn in (("fwd", fwd),) + ((("bwd", bwd),) if self.with_bwd else ()):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(s)
+            fn()
+            e1.record(s)
+            torch.cuda.synchronize()
+            g = max(1, min(200, int(target_ms / max(e0.elapsed_time(e1), 1e-3))))
+            ms = []
+            for _ in range(reps):
+                e0.record(s)
+                for _ in range(g):
+                    fn()
+                e1.record(s)
+                torch.cuda.synchronize()
+                ms.append(e0.elapsed_time(e1) / g)
+            out[name] = ms
+        return out
+
 
 def config_entry(w, opt, steps, warmup, clock=False):
-    """Event-timed per-launch statistics of one more dense workload (after the timed region)."""
+    """Per-launch statistics of one more dense workload (after the timed region): median and
+    minimum over `steps` groups of back-to-back calls (DenseRun.grouped), and the backward's
+    phases from an event pair around each launch."""
     with_bwd = "bwd" in w.passes
     run = DenseRun(w, opt, with_bwd)
     _, ms = run.timed(steps, warmup)
+    gr = run.grouped(steps)
     out = {"shape": {"B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "S": w.S, "d": w.d, "causal": w.causal},
-           "steps": steps, "fwd": pass_stats(ms["fwd"], w.fwd_flop())}
+           "groups": steps, "timing": "per call, over groups of back-to-back calls of about 2 ms",
+           "fwd": pass_stats(gr["fwd"], w.fwd_flop())}
     if with_bwd:
-        bwd = [sum(x) for x in zip(*(ms[n] for n, _ in DenseRun.PHASES))]
-        out["bwd"] = pass_stats(bwd, w.bwd_flop())
+        out["bwd"] = pass_stats(gr["bwd"], w.bwd_flop())
         out["bwd"]["phases_ms_median"] = {n: round(statistics.median(ms[n]), 4) for n, _ in DenseRun.PHASES}
     if clock:
         out["clock"] = sustained_clock(run)
