@@ -12,7 +12,9 @@
 //               tiles (64 queries) that can see its keys (causal: only tiles at or below
 //               the diagonal), from the last one down, for every query head of the GQA
 //               group.  Per step, with Q, dO, LSE and D staged in LDS:
-//                   S   = Q K^T,  dP = dO V^T     (MFMA; K and V stay in LDS for the run)
+//                   S   = Q K^T,  dP = dO V^T     (MFMA; K and V stay on chip for the run:
+//                                                 K's operand fragments in registers, V in
+//                                                 LDS, and with d = 64 V's in registers too)
 //                   P   = 2^(S c - LSE log2 e), 0 where masked  (c = scale log2 e)
 //                   dS  = P (dP - D)
 //                   dV^T += dO^T P,  dK^T += Q^T dS   (dO^T and Q^T by LDS transpose reads)
@@ -20,9 +22,10 @@
 //               summed over the group without atomics.
 //  3. bwd_dq:   dQ, per query tile, recomputing S and dP (see below); no atomics.
 //
-// In the S accumulator layout of bwd_main (v_mfma_f32_32x32x16_bf16, A = Q rows, B = K^T)
-// a lane holds one key column and 16 query rows; P and dS are packed to bf16 in registers
-// and used directly as the B operand of the dV^T and dK^T products.
+// In the S accumulator layout of bwd_main (v_mfma_f32_32x32x16_f16, A = Q rows, B = K^T,
+// all four products on fp16 operands scaled by powers of two, see below) a lane holds one
+// key column and 16 query rows; P and dS are packed to fp16 in registers and used directly
+// as the B operand of the dV^T and dK^T products.
 #include <type_traits>
 
 #include "attn_device.h"
@@ -438,7 +441,7 @@ void bwd_main_kernel(BwdArgs a) {
     };
 
     f32x16 sacc = f32x16{}, dpacc;
-    uint32_t pw[2][4], sw[2][4];  // P and dS packed to bf16 pairs: [t][pair], registers v = 8t ..
+    uint32_t pw[2][4], sw[2][4];  // P and dS packed to fp16 pairs: [t][pair], registers v = 8t ..
 #pragma unroll
     for (int i = 0; i < PD; ++i) issue(i);
     __builtin_amdgcn_sched_barrier(0);
