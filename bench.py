@@ -71,6 +71,10 @@ def parse():
     ap.add_argument("--tau", type=float, default=None)
     ap.add_argument("--variant", type=int, default=None,
                     help="forward schedule: 0 auto (default), 1 ping-pong, 2 four-wave")
+    ap.add_argument("--sweep", action="store_true",
+                    help="instead of the benchmark, print one JSON line per sequence length S = 2k..32k "
+                         "(H=16, d=128, causal, B*S = 32768 tokens): forward and backward per-call times "
+                         "over groups of back-to-back calls")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="instead of the benchmark, run a plain device copy of MIB MiB (3 times): the "
                          "reference kernel that scales rocprofv3 FETCH_SIZE/WRITE_SIZE into bytes")
@@ -474,6 +478,25 @@ def config_entry(w, opt, steps, warmup, clock=False):
     return out
 
 
+def sweep(opt):
+    """Forward and backward rates against the sequence length at a fixed token count
+    (B * S = 32768, H = 16, d = 128, causal, bf16 N(0,1) inputs seeded by S), one JSON line
+    per length."""
+    import torch
+    import workloads
+    for S in (2048, 4096, 8192, 16384, 32768):
+        B = 32768 // S
+        w = workloads.Workload(100 + S // 1024, f"sweep_S{S}", B, 16, 16, S, 128, True, ("fwd", "bwd"))
+        run = DenseRun(w, opt, True)
+        run.timed(3, 3)  # warm-up
+        gr = run.grouped(10)
+        print(json.dumps({"S": S, "B": B, "H": 16, "d": 128, "causal": True,
+                          "fwd": pass_stats(gr["fwd"], w.fwd_flop()), "bwd": pass_stats(gr["bwd"], w.bwd_flop())}),
+              flush=True)
+        del run
+        torch.cuda.empty_cache()
+
+
 def main():
     args = parse()
     if args.copy_calibration:
@@ -489,6 +512,10 @@ def main():
     import exact_attention_27_amd as ea
     import workloads
 
+    if args.sweep:
+        torch.cuda.set_device(torch.device("cuda:0"))
+        sweep(ea.attn_default_options())
+        return
     w = get_workload(args.workload)
     if isinstance(w, workloads.VarlenWorkload):
         main_varlen(args, w)
