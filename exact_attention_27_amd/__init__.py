@@ -270,17 +270,19 @@ ATTN_BWD_ALL, ATTN_BWD_PREPROCESS, ATTN_BWD_MAIN, ATTN_BWD_DQ = 0, 1, 2, 3
 def attn_bwd_ex(q, k, v, o, lse, do, scale: Optional[float] = None, causal: bool = False,
                 dq=None, dk=None, dv=None, workspace: Optional[torch.Tensor] = None,
                 opt: Optional[attn_options] = None, exp_mode: Optional[int] = None,
-                tau: Optional[float] = None, stream=None):
+                tau: Optional[float] = None, stream=None, variant: Optional[int] = None):
     """Backward pass; returns (dq, dk, dv).  workspace (uint8, >= attn_bwd_workspace_bytes)
-    is allocated with torch when not given."""
+    is allocated with torch when not given.  variant: the dK/dV kernel's schedule
+    (ATTN_VARIANT_AUTO, ATTN_VARIANT_PINGPONG for eight-wave workgroups, ATTN_VARIANT_FOURWAVE
+    for four-wave ones)."""
     return attn_bwd_phase(ATTN_BWD_ALL, q, k, v, o, lse, do, scale, causal, dq, dk, dv, workspace,
-                          opt, exp_mode, tau, stream)
+                          opt, exp_mode, tau, stream, variant)
 
 
 def attn_bwd_phase(phase: int, q, k, v, o, lse, do, scale: Optional[float] = None, causal: bool = False,
                    dq=None, dk=None, dv=None, workspace: Optional[torch.Tensor] = None,
                    opt: Optional[attn_options] = None, exp_mode: Optional[int] = None,
-                   tau: Optional[float] = None, stream=None):
+                   tau: Optional[float] = None, stream=None, variant: Optional[int] = None):
     """One phase of the backward (ATTN_BWD_*); the phases share ``workspace``."""
     B, Hq, Hkv, S, d = _dims(q, k)
     _need(q, "q", torch.bfloat16, (B, Hq, S, d))
@@ -303,7 +305,7 @@ def attn_bwd_phase(phase: int, q, k, v, o, lse, do, scale: Optional[float] = Non
     if workspace is None:
         workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
-    op = _options(opt, exp_mode, tau)
+    op = _options(opt, exp_mode, tau, variant)
     with _on(q.device):
         st = lib().attn_bwd_phase(int(phase), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(do),
                                _ptr(dq), _ptr(dk), _ptr(dv), B, Hq, Hkv, S, d, scale,

@@ -64,6 +64,18 @@ int hip_status(hipError_t e) { return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP; 
 // the ping-pong schedule on causal launches from S = 2k to 64k, GQA and packed batches,
 // except for dense non-causal launches of S >= 8192 with at least one 256-query
 // workgroup per CU, where the ping-pong schedule measured about 1% faster.
+// The dK/dV kernel's workgroup shape (where both exist: d = 128 with the hardware
+// exponential).  Each workgroup walks G * ceil(S / 64) query blocks at most.  Four-wave
+// workgroups, two per CU, overlap one workgroup's K/V load and closing stores with the other's
+// steps, and win while the walks are short; eight-wave workgroups, one per CU, take half the
+// barriers per product and win on long walks.  Measured: four waves 5-15% faster up to
+// G * ceil(S / 64) = 256 (S = 2k-16k at G = 1, S = 2k-4k at G = 4), 1-4% slower at 512.
+bool bwd_four_wave(int variant, int G, int S) {
+  if (variant == ATTN_VARIANT_PINGPONG) return false;
+  if (variant == ATTN_VARIANT_FOURWAVE) return true;
+  return (long)G * ((S + 63) / 64) <= 256;
+}
+
 bool use_pingpong(int variant, bool packed, bool causal, int B, int Hq, int S) {
   if (variant != ATTN_VARIANT_AUTO) return variant == ATTN_VARIANT_PINGPONG;
   return !packed && !causal && S >= 8192 && (int64_t)B * Hq * ((S + 255) / 256) >= 256;
@@ -273,7 +285,8 @@ int attn_bwd_phase(int phase, const void* q, const void* k, const void* v, const
   a.scale = scale;
   scale_setup(scale, &a.c, &a.q_and, &a.q_xor);
   (void)hipGetLastError();
-  return hip_status(attn::launch_bwd(a, d, causal != 0, o_.exp_mode, phases, static_cast<hipStream_t>(stream)));
+  return hip_status(attn::launch_bwd(a, d, causal != 0, o_.exp_mode, bwd_four_wave(o_.variant, Hq / Hkv, S), phases,
+                                     static_cast<hipStream_t>(stream)));
 }
 
 int attn_bwd_noalloc(const void* q, const void* k, const void* v, const void* o, const float* lse,

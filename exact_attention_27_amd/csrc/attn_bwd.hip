@@ -223,37 +223,54 @@ __device__ __forceinline__ u32x4 bf16x8_to_f16x8(u32x4 w, float sc) {
 //   dK^T += Q^T dS
 // so the vector work of each phase runs next to matrix products that do not need it;
 // LDS reads run two slots ahead of their products.
-template <int D, bool CAUSAL, int EXPMODE>
-__global__ __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_per_eu(2, 2)))
+template <int D, bool CAUSAL, int EXPMODE, int NW>
+__global__ __attribute__((amdgpu_flat_work_group_size(64 * NW, 64 * NW), amdgpu_waves_per_eu(2, 2)))
 void bwd_main_kernel(BwdArgs a) {
+  static_assert(NW == 4 || NW == 8, "4 or 8 waves per workgroup");
   constexpr int KSTEPS = D / 16;
   constexpr int DBLK = D / 32;
   constexpr int CG = D / 32;                   // 4-chunk groups per row
   constexpr int ROWB = D * 2;                  // bytes per row in memory
+  constexpr int BM = 32 * (NW / 4);            // queries per step
+  constexpr int NT = 64 * NW;                  // threads
   constexpr int KT = kBwdBN * D;               // elements of the K (or V) tile
-  constexpr int QT = kBwdBM * D;               // elements of one Q (or dO) tile
-  constexpr int KDMAS = kBwdBN / 16 * CG / 8;  // 1024-byte blocks per wave, K or V tile
-  constexpr int QDMAS = kBwdBM / 16 * CG / 8;  // 1024-byte blocks per wave, Q or dO tile
+  constexpr int QT = BM * D;                   // elements of one Q (or dO) tile
+  constexpr int KDMAS = kBwdBN / 16 * CG / NW; // 1024-byte blocks per wave, K or V tile
+  constexpr int QDMAS = BM / 16 * CG / NW;     // 1024-byte blocks per wave, Q or dO tile
   constexpr int PD = 2;                        // slots between an LDS read and its product
   constexpr int NS = 4 * KSTEPS;               // slots per step (== 4 * 2 * DBLK)
-  static_assert(KSTEPS == 2 * DBLK && KDMAS * 8 * 16 == kBwdBN * CG && QDMAS * 8 * 16 == kBwdBM * CG, "tiling");
-  // One LDS buffer, [K | V | Q stage 0 | Q stage 1 | dO stage 0 | dO stage 1 | LSE, D]: every
-  // operand read reaches its tile from a lane's base register by an immediate offset
-  // below 64 KiB (K and V from the K base; the four stages from the Q base).
-  constexpr int K_OFF = 0, V_OFF = 2 * KT, Q_OFF = 4 * KT, DO_OFF = Q_OFF + 4 * QT, SD_OFF = DO_OFF + 4 * QT;
+  static_assert(KSTEPS == 2 * DBLK && KDMAS * NW * 16 == kBwdBN * CG && QDMAS * NW * 16 == BM * CG, "tiling");
+  // The wave's operand fragments of K (S products) and, with d = 64, of V (dP products)
+  // stay in registers for the whole run: they are read from LDS once, after the fp16
+  // conversion, instead of once per step.  With d = 64 that is 32 registers and a third of
+  // the kernel's LDS reads (the kernel runs 5-8% faster); with d = 128, K's 32 registers
+  // are what the two-waves-per-SIMD budget has left (a sixth of the LDS reads, 2.5-4.5%
+  // faster), and the cubic exponential's few extra registers leave no room for them.
+  constexpr int NKV = D == 64 ? 2 * KSTEPS : (EXPMODE == 0 ? KSTEPS : 0);  // fragments held
+  // With K in registers, K's LDS tile is only needed until its fragments are loaded, and V
+  // then takes its place: the four-wave workgroup's LDS (one K/V tile, two Q/dO stages of
+  // 32 queries, LSE and D: 64.5 KiB at d = 128) lets two workgroups share a CU.
+  constexpr bool SHARED_KV = NW == 4;
+  static_assert(!SHARED_KV || NKV >= KSTEPS, "V can only replace K when K's fragments are in registers");
+  // One LDS buffer, [K | V | Q stage 0 | Q stage 1 | dO stage 0 | dO stage 1 | LSE, D]
+  // (K and V in one tile when SHARED_KV): every operand read reaches its tile from a
+  // lane's base register by an immediate offset below 64 KiB (K and V from the K base; the
+  // four stages from the Q base).
+  constexpr int K_OFF = 0, V_OFF = SHARED_KV ? 0 : 2 * KT, Q_OFF = V_OFF + 2 * KT, DO_OFF = Q_OFF + 4 * QT,
+                SD_OFF = DO_OFF + 4 * QT;
   static_assert(V_OFF + 2 * KT - K_OFF <= 65536 && SD_OFF - Q_OFF <= 65536, "immediate LDS offsets");
-  __shared__ __attribute__((aligned(1024))) unsigned char smem[SD_OFF + 2 * 2 * kBwdBM * 4];
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[SD_OFF + 2 * 2 * BM * 4];
   uint16_t* const k_lds = (uint16_t*)(smem + K_OFF);
   uint16_t* const v_lds = (uint16_t*)(smem + V_OFF);
   uint16_t* const q_lds[2] = {(uint16_t*)(smem + Q_OFF), (uint16_t*)(smem + Q_OFF + 2 * QT)};
   uint16_t* const do_lds[2] = {(uint16_t*)(smem + DO_OFF), (uint16_t*)(smem + DO_OFF + 2 * QT)};
-  float (*const sd_lds)[2 * kBwdBM] = (float (*)[2 * kBwdBM])(smem + SD_OFF);  // [stage][LSE log2e | D]
+  float (*const sd_lds)[2 * BM] = (float (*)[2 * BM])(smem + SD_OFF);  // [stage][LSE log2e | D]
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int kq = wave & 3;   // key block of this wave
-  const int qh = wave >> 2;  // query half of each step
+  const int kq = wave & 3;                  // key block of this wave
+  const int qh = NW == 8 ? wave >> 2 : 0;   // query half of each step (NW = 8)
   const int col = lane & 31;
   const int half = lane >> 5;
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
@@ -272,22 +289,26 @@ void bwd_main_kernel(BwdArgs a) {
   const int key = kw + col;  // this lane's key (column of S)
   const size_t kvbase = ((size_t)b * a.Hkv + hkv) * (size_t)S * D;
 
-  // DMA: wave w fills blocks i * 8 + w of a tile; block bl holds rows 16 (bl / CG) ..,
+  // DMA: wave w fills blocks i * NW + w of a tile; block bl holds rows 16 (bl / CG) ..,
   // chunks 4 (bl % CG) ..; lane l fetches row l / 4 of it, chunk (l % 4) ^ ((l / 16) % 4).
   const int dl_r = lane >> 2, dl_c = (lane & 3) ^ ((lane >> 4) & 3);
-  // K and V tiles -> LDS for the whole run (rows past the end are clamped to a real
-  // row; their probabilities are masked to 0).
+  // K and V tiles -> LDS (rows past the end are clamped to a real row; their
+  // probabilities are masked to 0).  With SHARED_KV, V follows once K's fragments are in
+  // registers.
+  auto dma_kv = [&](const uint16_t* __restrict__ src_t, uint16_t* dst) {
 #pragma unroll
-  for (int i = 0; i < KDMAS; ++i) {
-    const int bl = i * 8 + wave;
-    const int r = (bl / CG) * 16 + dl_r;
-    const size_t src = kvbase + (size_t)min(k0 + r, S - 1) * D + ((bl % CG) * 4 + dl_c) * 8;
-    dma16(a.k + src, k_lds + (i * 8 + wave_u) * 512);
-    dma16(a.v + src, v_lds + (i * 8 + wave_u) * 512);
-  }
+    for (int i = 0; i < KDMAS; ++i) {
+      const int bl = i * NW + wave;
+      const int r = (bl / CG) * 16 + dl_r;
+      const size_t src = kvbase + (size_t)min(k0 + r, S - 1) * D + ((bl % CG) * 4 + dl_c) * 8;
+      dma16(src_t + src, dst + (i * NW + wave_u) * 512);
+    }
+  };
+  dma_kv(a.k, k_lds);
+  if constexpr (!SHARED_KV) dma_kv(a.v, v_lds);
 
-  const int nqt = (S + kBwdBM - 1) / kBwdBM;
-  const int q_first = CAUSAL ? (k0 / kBwdBM) : 0;
+  const int nqt = (S + BM - 1) / BM;
+  const int q_first = CAUSAL ? (k0 / BM) : 0;
   const int per_head = nqt - q_first;
   const int steps = G * per_head;
   const int S_pad = (S + kBwdBM - 1) / kBwdBM * kBwdBM;
@@ -296,7 +317,7 @@ void bwd_main_kernel(BwdArgs a) {
   uint32_t qd_off[QDMAS];
 #pragma unroll
   for (int i = 0; i < QDMAS; ++i) {
-    const int bl = i * 8 + wave;
+    const int bl = i * NW + wave;
     qd_off[i] = (uint32_t)(((bl / CG) * 16 + dl_r) * ROWB + ((bl % CG) * 4 + dl_c) * 16);
   }
   // Step order: query tiles from the last one down, the group's heads innermost, so the
@@ -314,32 +335,32 @@ void bwd_main_kernel(BwdArgs a) {
     }
     const int hq = hkv * G + g;
     const size_t rbase = ((size_t)b * a.Hq + hq) * (size_t)S;
-    const int q0 = qt * kBwdBM;
+    const int q0 = qt * BM;
     const char* qb = (const char*)(a.q16 + (rbase + q0) * D);
     const char* ob = (const char*)(a.do16 + (rbase + q0) * D);
-    if (q0 + kBwdBM <= S) {
+    if (q0 + BM <= S) {
 #pragma unroll
       for (int i = 0; i < QDMAS; ++i) {
-        dma16_s(qb, qd_off[i], q_lds[st] + (i * 8 + wave_u) * 512);
-        dma16_s(ob, qd_off[i], do_lds[st] + (i * 8 + wave_u) * 512);
+        dma16_s(qb, qd_off[i], q_lds[st] + (i * NW + wave_u) * 512);
+        dma16_s(ob, qd_off[i], do_lds[st] + (i * NW + wave_u) * 512);
       }
     } else {
       int lr = dl_r;
       __asm__ volatile("" : "+v"(lr));  // keep this rare path's row arithmetic inside it
 #pragma unroll
       for (int i = 0; i < QDMAS; ++i) {
-        const int row = ((i * 8 + wave) / CG) * 16 + lr;  // row within the tile
+        const int row = ((i * NW + wave) / CG) * 16 + lr;  // row within the tile
         const int rc = min(q0 + row, S - 1) - q0;
         const uint32_t off = qd_off[i] + (uint32_t)((rc - row) * ROWB);
-        dma16_s(qb, off, q_lds[st] + (i * 8 + wave_u) * 512);
-        dma16_s(ob, off, do_lds[st] + (i * 8 + wave_u) * 512);
+        dma16_s(qb, off, q_lds[st] + (i * NW + wave_u) * 512);
+        dma16_s(ob, off, do_lds[st] + (i * NW + wave_u) * 512);
       }
     }
-    // LSE log2e (wave 0) and D (wave 1) of the 64 queries: 16 lanes x 16 bytes each.
+    // LSE log2e (wave 0) and D (wave 1) of the BM queries: BM / 4 lanes x 16 bytes each.
     if (wave_u < 2) {
       const size_t pbase = ((size_t)b * a.Hq + hq) * (size_t)S_pad + q0;
       const void* src = uniform_ptr((wave_u == 0 ? a.lse2 : a.ndx) + pbase);
-      if (lane < 16) dma16_s(src, (uint32_t)lane * 16u, &sd_lds[st][wave_u * kBwdBM]);
+      if (lane < BM / 4) dma16_s(src, (uint32_t)lane * 16u, &sd_lds[st][wave_u * BM]);
     }
   };
 
@@ -360,7 +381,6 @@ void bwd_main_kernel(BwdArgs a) {
   // LSE log2e and -D of the lane's query rows: one base (the area lies past the 16-bit
   // immediate range of the other bases), every stage and row group by an immediate offset.
   const int sdb = opaque(SD_OFF + (qh * 32 + half * 4) * 4);
-  static_assert(2 * 2 * kBwdBM * 4 <= 65536, "immediate LDS offsets");
 
   f32x16 dk_acc[DBLK], dv_acc[DBLK];
 #pragma unroll
@@ -374,13 +394,6 @@ void bwd_main_kernel(BwdArgs a) {
   const GroupScales gs = group_scales(a.pmax, bh);
   const float c = ldexpf(a.scale * kLog2e, -(gs.e_q + gs.e_k));
 
-  // The wave's operand fragments of K (S products) and, with d = 64, of V (dP products)
-  // stay in registers for the whole run: they are read from LDS once, after the fp16
-  // conversion, instead of once per step.  With d = 64 that is 32 registers and a third of
-  // the kernel's LDS reads (the kernel runs 5-8% faster); with d = 128, K's 32 registers
-  // are what the two-waves-per-SIMD budget has left (a sixth of the LDS reads, 2.5-4.5%
-  // faster), and the cubic exponential's few extra registers leave no room for them.
-  constexpr int NKV = D == 64 ? 2 * KSTEPS : (EXPMODE == 0 ? KSTEPS : 0);  // fragments held
   bf16x8 kvf[NKV > 0 ? NKV : 1];
   // One step on stage ST; MASKED adds the causal / end-of-sequence mask to P.
   auto compute = [&](const int q0, auto stage, auto masked) {
@@ -431,12 +444,12 @@ void bwd_main_kernel(BwdArgs a) {
       // 16 registers are not held through the S products.
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4)
-        if (i == p_slot(4 * g4)) l4[g4] = *(const f32x4*)(L + sdb + ST * 512 + g4 * 32);
+        if (i == p_slot(4 * g4)) l4[g4] = *(const f32x4*)(L + sdb + ST * BM * 8 + g4 * 32);
       // -D of the lane's 16 query rows, in the accumulator's register order: the first dP
       // product takes it as its accumulator input, so the chain ends at dP - D.
       if (i >= KSTEPS - 4 && i < KSTEPS) {
         const int g4 = i - (KSTEPS - 4);
-        d4[g4] = *(const f32x4*)(L + sdb + ST * 512 + kBwdBM * 4 + g4 * 32);
+        d4[g4] = *(const f32x4*)(L + sdb + ST * BM * 8 + BM * 4 + g4 * 32);
       }
     };
 
@@ -510,7 +523,7 @@ void bwd_main_kernel(BwdArgs a) {
       step_g = 0;
       --step_qt;
     }
-    const int q0 = qt * kBwdBM;
+    const int q0 = qt * BM;
     const int qs = q0 + qh * 32;  // first query of this wave's half
     if (!CAUSAL || kw <= qs + 31) {
       const bool need_mask = (kw + 32 > S) || (qs + 32 > S) || (CAUSAL && kw + 31 > qs);
@@ -527,25 +540,42 @@ void bwd_main_kernel(BwdArgs a) {
   // product runs in fp16, on Q 2^e_q and dO 2^e_do staged from the dQ kernel's copies: S
   // carries 2^(e_q + e_k) (taken out through c), dP, -D and dS 2^(e_do + e_v), dV 2^e_do
   // and dK 2^(e_q + e_do + e_v); the last two are taken out at the end.
-  wait_dma();
-  __syncthreads();  // K and V are in LDS
-  {
-    const float sk = ldexpf(1.0f, gs.e_k), sv = ldexpf(1.0f, gs.e_v);
-    u32x4* kk = (u32x4*)k_lds;
-    u32x4* vv = (u32x4*)v_lds;
+  // A tile of bf16 into fp16 in place, times 2^e.
+  auto to_f16 = [&](uint16_t* t, int e) {
+    const float sc = ldexpf(1.0f, e);
+    u32x4* tt = (u32x4*)t;
 #pragma unroll
-    for (int i = 0; i < KT / 8 / 512; ++i) {
-      kk[i * 512 + tid] = bf16x8_to_f16x8(kk[i * 512 + tid], sk);
-      vv[i * 512 + tid] = bf16x8_to_f16x8(vv[i * 512 + tid], sv);
-    }
-  }
-  if constexpr (NKV > 0) {
-    __syncthreads();  // the converted K and V are in LDS
+    for (int i = 0; i < KT / 8 / NT; ++i) tt[i * NT + tid] = bf16x8_to_f16x8(tt[i * NT + tid], sc);
+  };
+  // Fragments i0 .. i1 - 1 of kvf (K's, then V's) from the converted tiles.
+  auto load_frags = [&](const int i0, const int i1) {
 #pragma unroll
-    for (int i = 0; i < NKV; ++i) {
+    for (int i = i0; i < i1; ++i) {
       const int ks = i % KSTEPS;
       const int bo = (i < KSTEPS ? 0 : V_OFF - K_OFF) + (ks >> 1) * 1024;
       kvf[i] = *(const bf16x8*)((const char*)smem + ((ks & 1) ? rb1 : rb0) + bo);
+    }
+  };
+  wait_dma();
+  __syncthreads();  // K (and V) are in LDS
+  to_f16(k_lds, gs.e_k);
+  if constexpr (SHARED_KV) {
+    __syncthreads();  // the converted K is in LDS
+    load_frags(0, KSTEPS);
+    __syncthreads();  // every wave holds its K fragments: V takes K's place
+    dma_kv(a.v, v_lds);
+    wait_dma();
+    __syncthreads();  // V is in LDS
+    to_f16(v_lds, gs.e_v);
+    if constexpr (NKV > KSTEPS) {
+      __syncthreads();  // the converted V is in LDS
+      load_frags(KSTEPS, NKV);
+    }
+  } else {
+    to_f16(v_lds, gs.e_v);
+    if constexpr (NKV > 0) {
+      __syncthreads();  // the converted K and V are in LDS
+      load_frags(0, NKV);
     }
   }
   // (the first step's barrier orders the conversion's writes before any other read of V)
@@ -554,10 +584,11 @@ void bwd_main_kernel(BwdArgs a) {
     if (step + 1 < steps) do_step(step + 1, std::integral_constant<int, 1>{});
   }
 
-  // Add the two query halves' partial dK, dV through LDS (the Q/dO stages are free now),
-  // then dK = scale dK_acc, dV = dV_acc.
+  // With NW = 8, add the two query halves' partial dK, dV through LDS (the Q/dO stages
+  // are free now); then dK = scale dK_acc, dV = dV_acc.
+  if constexpr (NW == 8) {
   float* red = reinterpret_cast<float*>(smem + Q_OFF);  // 4 waves x DBLK x 16 x 64 floats
-  static_assert(SD_OFF - Q_OFF >= 4 * DBLK * 16 * 64 * (int)sizeof(float), "reduction space");
+  static_assert(NW != 8 || SD_OFF - Q_OFF >= 4 * DBLK * 16 * 64 * (int)sizeof(float), "reduction space");
   __syncthreads();
 #pragma unroll
   for (int pass = 0; pass < 2; ++pass) {
@@ -578,6 +609,7 @@ void bwd_main_kernel(BwdArgs a) {
       }
     }
     __syncthreads();
+  }
   }
   if (qh == 0 && key < S) {
     // dK = scale 2^-(e_do + e_v) (2^-e_q acc), in two factors that each stay in range.
@@ -922,7 +954,7 @@ void bwd_dq_kernel(BwdArgs a) {
 }
 
 template <int D, bool CAUSAL, int EXPMODE>
-hipError_t launch_bwd_t(const BwdArgs& a, int phases, hipStream_t stream) {
+hipError_t launch_bwd_t(const BwdArgs& a, bool four_wave, int phases, hipStream_t stream) {
   hipError_t e = hipSuccess;
   // Order: preprocess, dQ (which also writes the exact -D and the fp16 dO that the dK/dV
   // kernel reads), dK/dV.
@@ -939,26 +971,41 @@ hipError_t launch_bwd_t(const BwdArgs& a, int phases, hipStream_t stream) {
   }
   if (phases & 2) {
     const int nkt = (a.S + kBwdBN - 1) / kBwdBN;
-    hipLaunchKernelGGL((bwd_main_kernel<D, CAUSAL, EXPMODE>), dim3((unsigned)(nkt * a.B * a.Hkv)), dim3(512), 0,
-                       stream, a);
+    const dim3 grid((unsigned)(nkt * a.B * a.Hkv));
+    // Four-wave workgroups (two per CU) need K's fragments in registers: always at d = 64,
+    // at d = 128 with the hardware exponential only.
+    if constexpr (D == 64) {
+      hipLaunchKernelGGL((bwd_main_kernel<D, CAUSAL, EXPMODE, 4>), grid, dim3(256), 0, stream, a);
+    } else if constexpr (EXPMODE == 0) {
+      if (four_wave) {
+        hipLaunchKernelGGL((bwd_main_kernel<D, CAUSAL, EXPMODE, 4>), grid, dim3(256), 0, stream, a);
+      } else {
+        hipLaunchKernelGGL((bwd_main_kernel<D, CAUSAL, EXPMODE, 8>), grid, dim3(512), 0, stream, a);
+      }
+    } else {
+      hipLaunchKernelGGL((bwd_main_kernel<D, CAUSAL, EXPMODE, 8>), grid, dim3(512), 0, stream, a);
+    }
     e = hipGetLastError();
   }
   return e;
 }
 
 template <int D>
-hipError_t launch_bwd_d(const BwdArgs& a, bool causal, int exp_mode, int phases, hipStream_t stream) {
+hipError_t launch_bwd_d(const BwdArgs& a, bool causal, int exp_mode, bool four_wave, int phases, hipStream_t stream) {
   if (causal) {
-    return exp_mode == 0 ? launch_bwd_t<D, true, 0>(a, phases, stream) : launch_bwd_t<D, true, 1>(a, phases, stream);
+    return exp_mode == 0 ? launch_bwd_t<D, true, 0>(a, four_wave, phases, stream)
+                         : launch_bwd_t<D, true, 1>(a, four_wave, phases, stream);
   }
-  return exp_mode == 0 ? launch_bwd_t<D, false, 0>(a, phases, stream) : launch_bwd_t<D, false, 1>(a, phases, stream);
+  return exp_mode == 0 ? launch_bwd_t<D, false, 0>(a, four_wave, phases, stream)
+                       : launch_bwd_t<D, false, 1>(a, four_wave, phases, stream);
 }
 
 }  // namespace
 
-hipError_t launch_bwd(const BwdArgs& a, int d, bool causal, int exp_mode, int phases, hipStream_t stream) {
-  return d == 64 ? launch_bwd_d<64>(a, causal, exp_mode, phases, stream)
-                 : launch_bwd_d<128>(a, causal, exp_mode, phases, stream);
+hipError_t launch_bwd(const BwdArgs& a, int d, bool causal, int exp_mode, bool four_wave, int phases,
+                      hipStream_t stream) {
+  return d == 64 ? launch_bwd_d<64>(a, causal, exp_mode, four_wave, phases, stream)
+                 : launch_bwd_d<128>(a, causal, exp_mode, four_wave, phases, stream);
 }
 
 }  // namespace attn

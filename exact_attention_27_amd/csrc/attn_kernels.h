@@ -61,7 +61,10 @@ hipError_t launch_fwd(const FwdArgs& a, int d, bool causal, int exp_mode, bool p
 hipError_t launch_fwd_varlen(const FwdArgs& a, int d, bool causal, int exp_mode, bool pingpong, hipStream_t stream);
 // phases: bit 0 = preprocess (D, LSE log2 e), bit 1 = dK/dV kernel, bit 2 = dQ kernel.
 // 7 runs the whole backward.
-hipError_t launch_bwd(const BwdArgs& a, int d, bool causal, int exp_mode, int phases, hipStream_t stream);
+// four_wave: the dK/dV kernel in four-wave workgroups, two per CU (d = 64 always; at
+// d = 128 only with the hardware exponential); otherwise eight-wave workgroups, one per CU.
+hipError_t launch_bwd(const BwdArgs& a, int d, bool causal, int exp_mode, bool four_wave, int phases,
+                      hipStream_t stream);
 hipError_t launch_exp2_eval(const float* x, float* y, long n, int exp_mode, hipStream_t stream);
 
 }  // namespace attn

@@ -74,11 +74,13 @@ enum {
                           summary (section 2.B)                                    */
 };
 
-/* Forward schedules (attn_options.variant). */
+/* Schedules (attn_options.variant), for the forward and the backward's dK/dV kernel. */
 enum {
     ATTN_VARIANT_AUTO = 0,     /* the library picks per launch (the default)          */
-    ATTN_VARIANT_PINGPONG = 1, /* 8-wave workgroups in two half-step-staggered groups */
-    ATTN_VARIANT_FOURWAVE = 2  /* 4-wave workgroups, two per CU                      */
+    ATTN_VARIANT_PINGPONG = 1, /* 8-wave workgroups (forward: two half-step-staggered
+                                  groups; dK/dV: the query halves of each step split
+                                  between wave pairs), one per CU                    */
+    ATTN_VARIANT_FOURWAVE = 2  /* 4-wave workgroups, several per CU                  */
 };
 
 /*
@@ -91,7 +93,7 @@ enum {
  *              softmax rescaling" of "NVIDIA's FlashAttention-4", section "The
  *              Technical Edge").  The result is the same for every tau; tau only
  *              bounds the unnormalised probabilities by 2^tau.  tau <= 30.
- *   variant  : forward schedule (the backward has one schedule and ignores it).
+ *   variant  : schedule.  Forward:
  *              ATTN_VARIANT_FOURWAVE (2): 4-wave workgroups of 128 queries walking
  *              32-key tiles, three per CU (three waves per SIMD), every wave in the
  *              same phase order.  ATTN_VARIANT_PINGPONG (1): 8-wave workgroups of 256
@@ -107,7 +109,20 @@ enum {
  *              round differently (their tiles differ, and with them the rescale
  *              points and the order of the row sums), so their results agree to the
  *              accuracy the library states, not bit for bit; a given schedule is
- *              deterministic.  Other values: ATTN_ERR_UNSUPPORTED.
+ *              deterministic.
+ *              Backward (the dK/dV kernel; the other two launches have one schedule):
+ *              ATTN_VARIANT_FOURWAVE (2): 4-wave workgroups of 128 keys stepping 32
+ *              queries at a time, two per CU, so that one workgroup's K/V load and
+ *              closing stores overlap the other's steps.  ATTN_VARIANT_PINGPONG (1):
+ *              8-wave workgroups of 128 keys stepping 64 queries, one per CU, whose
+ *              wave pairs split each step's queries and add their partial dK/dV at the
+ *              end.  ATTN_VARIANT_AUTO (0): four-wave when G * ceil(S / 64) <= 256
+ *              (G = Hq / Hkv), eight-wave otherwise.  With d = 64 the four-wave
+ *              schedule is always used, and with d = 128 and ATTN_EXP_POLY3 the
+ *              eight-wave one (its kernel cannot hold K in registers, which four-wave
+ *              workgroups need).  The schedules add dK and dV in different orders, so
+ *              they agree to the stated accuracy, not bit for bit.
+ *              Other values: ATTN_ERR_UNSUPPORTED.
  */
 typedef struct attn_options {
     int exp_mode;

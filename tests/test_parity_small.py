@@ -173,6 +173,31 @@ def test_bwd_edge_shapes(case, causal):
     assert_bf16_close("dv", dv, rdv)
 
 
+SCHEDULE_CASES = [(1, 2, 1, 17, 128), (1, 4, 2, 257, 128), (1, 8, 1, 200, 128), (2, 2, 2, 700, 128)]
+
+
+@pytest.mark.parametrize("variant", [ea.ATTN_VARIANT_PINGPONG, ea.ATTN_VARIANT_FOURWAVE], ids=["eight_wave", "four_wave"])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("case", SCHEDULE_CASES, ids=lambda c: "B%dHq%dHkv%dS%dd%d" % c)
+def test_bwd_dkdv_schedules(case, causal, variant):
+    """Both workgroup shapes of the dK/dV kernel (eight waves stepping 64 queries, four
+    waves stepping 32), forced through the options on ragged, grouped and causal shapes,
+    against the oracle at the plain bar, and each bitwise deterministic."""
+    B, Hq, Hkv, S, d = case
+    print(f"\n[bwd schedule] {case} causal={causal} variant={variant}", flush=True)
+    t = inputs(B, Hq, Hkv, S, d, seed=300 + sum(case))
+    scale = d ** -0.5
+    o, lse = ea.attn_fwd(t["q"], t["k"], t["v"], scale, causal)
+    g1 = ea.attn_bwd_ex(t["q"], t["k"], t["v"], o, lse, t["do"], scale, causal, variant=variant)
+    g2 = ea.attn_bwd_ex(t["q"], t["k"], t["v"], o, lse, t["do"], scale, causal, variant=variant)
+    torch.cuda.synchronize()
+    assert all(torch.equal(x, y) for x, y in zip(g1, g2))
+    rdq, rdk, rdv = oracle_bwd(t, scale, causal)
+    assert_bf16_close("dq", g1[0], rdq)
+    assert_bf16_close("dk", g1[1], rdk)
+    assert_bf16_close("dv", g1[2], rdv)
+
+
 @pytest.mark.parametrize("exp_mode", [ea.ATTN_EXP_HW, ea.ATTN_EXP_POLY3])
 @pytest.mark.parametrize("causal", [False, True])
 def test_bwd_from_oracle_forward(exp_mode, causal):
