@@ -9,9 +9,9 @@
 //               into the workspace.  Bound by HBM bandwidth.
 //  2. bwd_main: dK and dV.  One workgroup per (batch, KV head, tile of 128 keys) keeps dK
 //               and dV for its keys in registers for the whole run and walks the query
-//               tiles (64 queries) that can see its keys (causal: only tiles at or below
-//               the diagonal), from the last one down, for every query head of the GQA
-//               group.  Per step, with Q, dO, LSE and D staged in LDS:
+//               tiles (64 or 32 queries, by workgroup shape) that can see its keys (causal:
+//               only tiles at or below the diagonal), from the last one down, for every
+//               query head of the GQA group.  Per step, with Q, dO, LSE and D staged in LDS:
 //                   S   = Q K^T,  dP = dO V^T     (MFMA; K and V stay on chip for the run:
 //                                                 K's operand fragments in registers, V in
 //                                                 LDS, and with d = 64 V's in registers too)
@@ -206,10 +206,17 @@ __device__ __forceinline__ u32x4 bf16x8_to_f16x8(u32x4 w, float sc) {
 
 // ------------------------------------------------------------------ main
 
-// Workgroup of 8 waves (two per SIMD) on a tile of 128 keys.  Wave w owns key block
-// kq = w % 4 (32 keys) for query half qh = w / 4 of every 64-query step: waves w and
-// w + 4 accumulate partial dK and dV for the same keys over different queries, and
-// the two partials are added through LDS at the end.
+// A workgroup owns a tile of 128 keys; wave w owns key block kq = w % 4 (32 keys).  Two
+// shapes (NW waves, two waves per SIMD either way):
+//  * NW = 8, one workgroup per CU: each step covers 64 queries, and wave w takes query half
+//    qh = w / 4 of it, so waves w and w + 4 accumulate partial dK and dV for the same keys
+//    over different queries; the two partials are added through LDS at the end.
+//  * NW = 4, two workgroups per CU: each step covers 32 queries, every wave all of them, and
+//    no partials need adding.  V's tile takes K's place in LDS once each wave holds its K
+//    fragments, so the workgroup needs 64.5 KiB (d = 128) and two fit on a CU: one's K/V
+//    load and closing stores overlap the other's steps.  That pays on short walks (each
+//    workgroup's fixed cost is spread over few steps); on long ones the eight-wave shape,
+//    with half the barriers per product, is faster (the launcher chooses).
 //
 // K, V (resident; each wave also holds its operand fragments of K, and with d = 64 of V,
 // in registers) and the Q, dO stages sit in LDS as XOR chunk-inner blocks (see
