@@ -733,6 +733,41 @@ void bwd_dq_kernel(BwdArgs a) {
   const uint16_t* __restrict__ Kg = a.k + kvbase;
   const uint16_t* __restrict__ Vg = a.v + kvbase;
 
+  // DMA of a tile: wave w fills blocks 4 i + w; lane l fetches row l / 4 of the block,
+  // chunk (l % 4) ^ ((l / 16) % 4).  Fixed per-lane offsets from a scalar tile base; the
+  // last tile, if it runs past the end of the sequence, clamps its rows (their scores
+  // are masked).
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  const int dl_r = lane >> 2, dl_c = (lane & 3) ^ ((lane >> 4) & 3);
+  uint32_t dma_off[DMAS];
+#pragma unroll
+  for (int i = 0; i < DMAS; ++i) {
+    const int bl = i * 4 + wave;
+    dma_off[i] = (uint32_t)(((bl / CG) * 16 + dl_r) * ROWB + ((bl % CG) * 4 + dl_c) * 16);
+  }
+  auto dma_tile = [&](const uint16_t* __restrict__ src, int j, uint16_t* slot) {
+    const char* base = (const char*)(src + (size_t)j * BN * D);
+    if (j * BN + BN <= S) {
+#pragma unroll
+      for (int i = 0; i < DMAS; ++i) dma16_s(base, dma_off[i], slot + (i * 4 + wave_u) * 512);
+    } else {
+      int lr = dl_r;
+      __asm__ volatile("" : "+v"(lr));  // keep this rare path's row arithmetic inside it
+#pragma unroll
+      for (int i = 0; i < DMAS; ++i) {
+        const int row = ((i * 4 + wave) / CG) * 16 + lr;  // row within the tile
+        const int rc = min(j * BN + row, S - 1) - j * BN;
+        dma16_s(base, dma_off[i] + (uint32_t)((rc - row) * ROWB), slot + (i * 4 + wave_u) * 512);
+      }
+    }
+  };
+  uint16_t* const Kring = smem;
+  uint16_t* const Vring = smem + 2 * TILE;
+
+  // The first K and V tiles are on their way while the Q and dO rows load.
+  dma_tile(Kg, 0, Kring);
+  dma_tile(Vg, 0, Vring);
+
   // Q^T and dO^T fragments (B operands): query qc, d = ks*16 + half*8 .. +7.
   bf16x8 qf[KSTEPS], of[KSTEPS];
   {
@@ -769,37 +804,6 @@ void bwd_dq_kernel(BwdArgs a) {
 
   const int kv_end = CAUSAL ? min(S, q0 + kDqBM) : S;
   const int nkv = (kv_end + BN - 1) / BN;
-
-  // DMA of a tile: wave w fills blocks 4 i + w; lane l fetches row l / 4 of the block,
-  // chunk (l % 4) ^ ((l / 16) % 4).  Fixed per-lane offsets from a scalar tile base; the
-  // last tile, if it runs past the end of the sequence, clamps its rows (their scores
-  // are masked).
-  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
-  const int dl_r = lane >> 2, dl_c = (lane & 3) ^ ((lane >> 4) & 3);
-  uint32_t dma_off[DMAS];
-#pragma unroll
-  for (int i = 0; i < DMAS; ++i) {
-    const int bl = i * 4 + wave;
-    dma_off[i] = (uint32_t)(((bl / CG) * 16 + dl_r) * ROWB + ((bl % CG) * 4 + dl_c) * 16);
-  }
-  auto dma_tile = [&](const uint16_t* __restrict__ src, int j, uint16_t* slot) {
-    const char* base = (const char*)(src + (size_t)j * BN * D);
-    if (j * BN + BN <= S) {
-#pragma unroll
-      for (int i = 0; i < DMAS; ++i) dma16_s(base, dma_off[i], slot + (i * 4 + wave_u) * 512);
-    } else {
-      int lr = dl_r;
-      __asm__ volatile("" : "+v"(lr));  // keep this rare path's row arithmetic inside it
-#pragma unroll
-      for (int i = 0; i < DMAS; ++i) {
-        const int row = ((i * 4 + wave) / CG) * 16 + lr;  // row within the tile
-        const int rc = min(j * BN + row, S - 1) - j * BN;
-        dma16_s(base, dma_off[i] + (uint32_t)((rc - row) * ROWB), slot + (i * 4 + wave_u) * 512);
-      }
-    }
-  };
-  uint16_t* const Kring = smem;
-  uint16_t* const Vring = smem + 2 * TILE;
 
   // Per-lane LDS byte offsets.  K and V operand reads: key row kb*32 + col, chunk
   // ks*2 + half (one register per parity of ks).  K^T transpose reads: source lane s
@@ -928,8 +932,6 @@ void bwd_dq_kernel(BwdArgs a) {
     __syncthreads();
   };
 
-  dma_tile(Kg, 0, Kring);
-  dma_tile(Vg, 0, Vring);
   wait_dma();
   __syncthreads();
   for (int j = 0; j < nkv; j += 2) {
