@@ -284,11 +284,19 @@ void bwd_main_kernel(BwdArgs a) {
   const int S = a.S;
   const int G = a.Hq / a.Hkv;
 
-  // Tiles with the lowest key index have the most query tiles under the causal mask:
-  // launch them first.
-  const int nbh = a.B * a.Hkv;
-  const int kt = blockIdx.x / nbh;
-  const int bh = blockIdx.x % nbh;
+  // Dispatch order: chunks of kv_chunk KV groups one after the other (dispatch_chunk);
+  // within a chunk, key tile by key tile, the lowest key index first (it has the most
+  // query tiles under the causal mask).  With the chunk's group count a multiple of 8,
+  // all key tiles of one group run on one XCD (XCD = block index % 8) and share its L2
+  // for the group's Q and dO.
+  const int ngrp = a.B * a.Hkv;
+  const int nkt = (S + kBwdBN - 1) / kBwdBN;
+  const int per_chunk = a.kv_chunk * nkt;
+  const int chunk = (int)blockIdx.x / per_chunk;
+  const int pos = (int)blockIdx.x - chunk * per_chunk;
+  const int ncg = min(a.kv_chunk, ngrp - chunk * a.kv_chunk);  // groups in this chunk
+  const int kt = pos / ncg;
+  const int bh = chunk * a.kv_chunk + (pos - kt * ncg);
   const int b = bh / a.Hkv;
   const int hkv = bh - b * a.Hkv;
   const int k0 = kt * kBwdBN;
@@ -699,23 +707,31 @@ void bwd_dq_kernel(BwdArgs a) {
   const int S = a.S;
   const int S_pad = (S + kBwdBM - 1) / kBwdBM * kBwdBM;
 
-  const int nbh = a.B * a.Hq;
   const int nqt = (S + kDqBM - 1) / kDqBM;
   const int bid = blockIdx.x;
-  const int qt = CAUSAL ? (nqt - 1 - bid / nbh) : (bid / nbh);
-  // Head of this workgroup, as in the forward: with B * Hkv a multiple of 8, every query
-  // head and query tile of one KV group lands on one XCD (XCD = bid % 8) and reads K and
-  // V through one L2.
+  // Dispatch order and head of this workgroup, as in the forward: chunks of dq_chunk KV
+  // groups (dispatch_chunk), within a chunk the longest query tiles first; with the
+  // chunk's group count a multiple of 8, every query head and query tile of one KV group
+  // lands on one XCD (XCD = bid % 8) and reads K and V through one L2.
   const int G = a.Hq / a.Hkv;
-  const int u = bid % nbh;
+  const int ngrp = a.B * a.Hkv;
+  const int per_chunk = a.dq_chunk * G * nqt;
+  const int chunk = bid / per_chunk;
+  const int pos = bid - chunk * per_chunk;
+  const int g0 = chunk * a.dq_chunk;
+  const int ncg = min(a.dq_chunk, ngrp - g0);  // KV groups in this chunk
+  const int nbh = ncg * G;
+  const int level = pos / nbh;
+  const int qt = CAUSAL ? (nqt - 1 - level) : level;
+  const int u = pos - level * nbh;
   int kvg, g;
-  if (((a.B * a.Hkv) & 7) == 0) {
+  if ((ncg & 7) == 0) {
     const int jj = u >> 3;
-    kvg = (jj / G) * 8 + (u & 7);
+    kvg = g0 + (jj / G) * 8 + (u & 7);
     g = jj - (jj / G) * G;
   } else {
-    kvg = u / G;
-    g = u - kvg * G;
+    kvg = g0 + u / G;
+    g = u - (u / G) * G;
   }
   const int b = kvg / a.Hkv;
   const int hkv = kvg - b * a.Hkv;
@@ -963,8 +979,13 @@ void bwd_dq_kernel(BwdArgs a) {
 }
 
 template <int D, bool CAUSAL, int EXPMODE>
-hipError_t launch_bwd_t(const BwdArgs& a, bool four_wave, int phases, hipStream_t stream) {
+hipError_t launch_bwd_t(const BwdArgs& a0, bool four_wave, int phases, hipStream_t stream) {
   hipError_t e = hipSuccess;
+  // Dispatch chunks: the dQ kernel's groups re-read K and V (4 S d bytes), the dK/dV
+  // kernel's the fp16 Q and dO of G query heads (4 G S d bytes).
+  BwdArgs a = a0;
+  a.dq_chunk = dispatch_chunk(a.B * a.Hkv, a.S, 4L * a.S * D);
+  a.kv_chunk = dispatch_chunk(a.B * a.Hkv, a.S, 4L * (a.Hq / a.Hkv) * a.S * D);
   // Order: preprocess, dQ (which also writes the exact -D and the fp16 dO that the dK/dV
   // kernel reads), dK/dV.
   if (phases & 1) {

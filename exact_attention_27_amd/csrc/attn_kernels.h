@@ -27,6 +27,8 @@ struct FwdArgs {
   // rows cu_seqlens[b] .. cu_seqlens[b + 1] - 1 (clamped to [0, total]).
   const int* cu_seqlens;
   int total;
+  // KV groups per dispatch chunk (set by the launcher, dispatch_chunk below).
+  int grp_chunk;
 };
 
 // Workgroups of the backward preprocess per (batch, KV head); each leaves one set of
@@ -54,7 +56,27 @@ struct BwdArgs {
   float c;        // |scale| * log2(e) (1 for a zero scale)
   float scale;    // the caller's scale (dQ and dK carry it)
   uint32_t q_and, q_xor;
+  // KV groups per dispatch chunk of the dQ and the dK/dV kernels (set by the launcher).
+  int dq_chunk, kv_chunk;
 };
+
+// Dispatch chunks.  A launch whose workgroups of one (batch, KV head) group all re-read
+// that group's group_bytes of operands (K and V; Q and dO) runs its grid in chunks of
+// groups, one chunk after the other, so that the resident workgroups share a few groups'
+// operands in L2 and the memory-side cache instead of streaming every group's from HBM.
+// Chunks are used when the operands of all groups exceed 160 MiB (the 256 MiB
+// memory-side cache holds less beside the other streams) and sequences have at most 4096
+// keys: the fewest equal chunks of at most about 96 MiB each, rounded up to a multiple of
+// 8 groups.  Longer sequences keep one chunk: there a causal launch's longest workgroups
+// are a large share of its run and must start first.  Returns groups per chunk.
+inline int dispatch_chunk(int ngrp, int S, long group_bytes) {
+  const long budget = 96L << 20;
+  const long total = (long)ngrp * group_bytes;
+  if (S > 4096 || S < 1 || group_bytes < 1 || total <= (160L << 20)) return ngrp;
+  const long nch = (total + budget - 1) / budget;
+  const long c = ((ngrp + nch - 1) / nch + 7) & ~7L;
+  return c >= ngrp ? ngrp : (int)c;
+}
 
 hipError_t launch_fwd(const FwdArgs& a, int d, bool causal, int exp_mode, bool pingpong, hipStream_t stream);
 // The same forward over a variable-length packed batch (a.cu_seqlens != nullptr).
