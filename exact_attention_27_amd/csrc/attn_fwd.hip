@@ -186,10 +186,12 @@ void fwd_kernel(FwdArgs a) {
 
   // Q^T fragments (B operand): query qi, d = ks*16 + half*8 .. +7.  Rows past the end
   // of the sequence load the last row instead (their outputs are never stored); no
-  // branch, so all the loads are in flight together.
+  // branch, so all the loads are in flight together.  With d = 128 they are issued after
+  // the first K and V tiles' DMA, so that the two overlap (2k prefill 1.5-2% faster); with
+  // d = 64 before it (1.5% faster that way).
   bf16x8 qf[KSTEPS];
-  {
-    const u32x4* qrow = (const u32x4*)(a.q + qbase + (size_t)min(qi, S - 1) * rs_q + half * 8);
+  const u32x4* qrow = (const u32x4*)(a.q + qbase + (size_t)min(qi, S - 1) * rs_q + half * 8);
+  if constexpr (D == 64) {
 #pragma unroll
     for (int ks = 0; ks < KSTEPS; ++ks) qf[ks] = __builtin_bit_cast(bf16x8, (qrow[ks * 2] & a.q_and) ^ a.q_xor);
   }
@@ -301,6 +303,10 @@ void fwd_kernel(FwdArgs a) {
   dma_k(0, Kring);
   if (nkv > 1) dma_k(1, Kring + TILE);
   dma_v(0, Vring);
+  if constexpr (D != 64) {
+#pragma unroll
+    for (int ks = 0; ks < KSTEPS; ++ks) qf[ks] = __builtin_bit_cast(bf16x8, (qrow[ks * 2] & a.q_and) ^ a.q_xor);
+  }
   wait_dma();
   __syncthreads();
   f32x16 sc[KB];
