@@ -22,6 +22,11 @@
 //               summed over the group without atomics.
 //  3. bwd_dq:   dQ, per query tile, recomputing S and dP (see below); no atomics.
 //
+// Both bwd_dq and bwd_main keep every tile of one (batch, KV head) group on one XCD when
+// the group count allows, and large launches of short sequences run in chunks of groups
+// (dispatch_chunk in attn_kernels.h) so that the re-read K/V (dQ) and Q/dO (dK/dV) of the
+// resident workgroups fit the memory-side cache.
+//
 // In the S accumulator layout of bwd_main (v_mfma_f32_32x32x16_f16, A = Q rows, B = K^T,
 // all four products on fp16 operands scaled by powers of two, see below) a lane holds one
 // key column and 16 query rows; P and dS are packed to fp16 in registers and used directly

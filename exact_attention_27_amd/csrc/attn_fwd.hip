@@ -46,7 +46,9 @@
 // Workgroups are dispatched longest-first (largest query tile index first; under the causal
 // mask the longer ones also run at a higher wave priority), and when the number of KV
 // groups is a multiple of 8 all query heads and query tiles of one KV group run on one XCD
-// and share its L2 for K and V.
+// and share its L2 for K and V.  Large launches of short sequences run in chunks of KV
+// groups (dispatch_chunk in attn_kernels.h) so that the resident workgroups' K and V fit
+// the memory-side cache.
 #include <type_traits>
 
 #include "attn_device.h"
