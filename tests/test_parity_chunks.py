@@ -41,6 +41,9 @@ CASES = [
     # 96 groups of 4 query heads: the dK/dV kernel's fp16 Q and dO are 2,048,000 bytes per
     # group (188 MiB): two chunks of 48; the forward and dQ kernels run one chunk.
     (24, 16, 4, 1000, 128, (0, 12, 24)),
+    # d = 64: 660 groups of 256,000 bytes (161 MiB): chunks of 336 and 324 groups in all
+    # three kernels.
+    (132, 5, 5, 1000, 64, (0, 66, 132)),
 ]
 
 
