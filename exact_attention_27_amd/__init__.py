@@ -56,6 +56,11 @@ _I = ctypes.c_int
 _F = ctypes.c_float
 
 
+class attn_plan(ctypes.Structure):
+    _fields_ = [("fwd_schedule", ctypes.c_int), ("fwd_chunk", ctypes.c_int), ("dq_chunk", ctypes.c_int),
+                ("dkdv_chunk", ctypes.c_int), ("dkdv_schedule", ctypes.c_int)]
+
+
 def lib() -> ctypes.CDLL:
     """The loaded libattn.so (raises if it is not built)."""
     global _lib
@@ -92,6 +97,8 @@ def lib() -> ctypes.CDLL:
         L.attn_bwd_noalloc.argtypes = [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _P]
         L.attn_exp2_eval.restype = _I
         L.attn_exp2_eval.argtypes = [_P, _P, ctypes.c_long, _I, _P]
+        L.attn_launch_plan.restype = _I
+        L.attn_launch_plan.argtypes = [_I, _I, _I, _I, _I, _I, ctypes.POINTER(attn_options), ctypes.POINTER(attn_plan)]
         L.attn_exp2_poly_host.restype = None
         L.attn_exp2_poly_host.argtypes = [_P, _P, ctypes.c_long]
         _lib = L
@@ -258,6 +265,17 @@ def attn_fwd(q, k, v, scale: Optional[float] = None, causal: bool = False,
              o: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None, stream=None):
     """Forward pass with the default options (see attn_fwd_ex)."""
     return attn_fwd_ex(q, k, v, scale, causal, o, lse, stream=stream)
+
+
+def attn_launch_plan(B: int, Hq: int, Hkv: int, S: int, d: int, causal: bool = False,
+                     opt: Optional[attn_options] = None, *, exp_mode: Optional[int] = None,
+                     tau: Optional[float] = None, variant: Optional[int] = None) -> dict:
+    """The launch plan (schedules and dispatch chunks) of attn_launch_plan, as a dict."""
+    op = _options(opt, exp_mode, tau, variant)
+    out = attn_plan()
+    _check(lib().attn_launch_plan(B, Hq, Hkv, S, d, int(bool(causal)), ctypes.byref(op) if op is not None else None,
+                                  ctypes.byref(out)))
+    return {n: getattr(out, n) for n, _ in attn_plan._fields_}
 
 
 def attn_bwd_workspace_bytes(B: int, Hq: int, Hkv: int, S: int, d: int) -> int:

@@ -157,6 +157,28 @@ const char* attn_status_string(int status) {
   }
 }
 
+int attn_launch_plan(int B, int Hq, int Hkv, int S, int d, int causal, const attn_options* opt,
+                     attn_plan* out) {
+  if (!out) return ATTN_ERR_NULL;
+  bool empty = false;
+  int st = check_sizes(B, Hq, Hkv, S, d, &empty);
+  if (st != ATTN_OK) return st;
+  const attn_options o_ = opt ? *opt : attn_default_options();
+  if ((st = check_options(o_)) != ATTN_OK) return st;
+  attn_plan p;
+  p.fwd_schedule = use_pingpong(o_.variant, false, causal != 0, B, Hq, S) ? ATTN_VARIANT_PINGPONG
+                                                                          : ATTN_VARIANT_FOURWAVE;
+  p.fwd_chunk = attn::fwd_chunk_groups(B, Hkv, S, d);
+  p.dq_chunk = attn::dq_chunk_groups(B, Hkv, S, d);
+  p.dkdv_chunk = attn::dkdv_chunk_groups(B, Hq, Hkv, S, d);
+  // The launcher's rule: four waves always at d = 64; at d = 128 with the hardware
+  // exponential only, by bwd_four_wave; eight waves for the cubic exponential at d = 128.
+  const bool four = d == 64 || (o_.exp_mode == ATTN_EXP_HW && bwd_four_wave(o_.variant, Hq / Hkv, S));
+  p.dkdv_schedule = four ? ATTN_VARIANT_FOURWAVE : ATTN_VARIANT_PINGPONG;
+  *out = p;
+  return ATTN_OK;
+}
+
 int attn_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse,
                 int B, int Hq, int Hkv, int S, int d, float scale, int causal,
                 const attn_options* opt, void* stream) {

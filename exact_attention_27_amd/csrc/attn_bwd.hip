@@ -986,11 +986,9 @@ void bwd_dq_kernel(BwdArgs a) {
 template <int D, bool CAUSAL, int EXPMODE>
 hipError_t launch_bwd_t(const BwdArgs& a0, bool four_wave, int phases, hipStream_t stream) {
   hipError_t e = hipSuccess;
-  // Dispatch chunks: the dQ kernel's groups re-read K and V (4 S d bytes), the dK/dV
-  // kernel's the fp16 Q and dO of G query heads (4 G S d bytes).
   BwdArgs a = a0;
-  a.dq_chunk = dispatch_chunk(a.B * a.Hkv, a.S, 4L * a.S * D);
-  a.kv_chunk = dispatch_chunk(a.B * a.Hkv, a.S, 4L * (a.Hq / a.Hkv) * a.S * D);
+  a.dq_chunk = dq_chunk_groups(a.B, a.Hkv, a.S, D);
+  a.kv_chunk = dkdv_chunk_groups(a.B, a.Hq, a.Hkv, a.S, D);
   // Order: preprocess, dQ (which also writes the exact -D and the fp16 dO that the dK/dV
   // kernel reads), dK/dV.
   if (phases & 1) {

@@ -489,9 +489,9 @@ hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t stream) {
   const int nqt = (a.S + 32 * W - 1) / (32 * W);
   const dim3 grid((unsigned)(nqt * a.B * a.Hq));
   FwdArgs c = a;
-  // K and V of a group: 4 S d bytes.  (Measured with 256-512 heads at S = 2048: 15-25%
-  // faster than one chunk; at S = 8192, chunks of 24-48 groups were 1-4% slower.)
-  c.grp_chunk = dispatch_chunk(a.B * a.Hkv, a.S, 4L * a.S * D);
+  // (Measured with 256-512 heads at S = 2048: 15-25% faster than one chunk; at S = 8192,
+  // chunks of 24-48 groups were 1-4% slower.)
+  c.grp_chunk = fwd_chunk_groups(a.B, a.Hkv, a.S, D);
   hipLaunchKernelGGL((fwd_kernel<D, CAUSAL, EXPMODE, VARLEN, W>), grid, dim3(64 * W), 0, stream, c);
   return hipGetLastError();
 }

@@ -78,6 +78,15 @@ inline int dispatch_chunk(int ngrp, int S, long group_bytes) {
   return c >= ngrp ? ngrp : (int)c;
 }
 
+// Groups per dispatch chunk of each chunked kernel: the forward and the dQ kernel re-read
+// a group's K and V (4 S d bytes), the dK/dV kernel its G query heads' fp16 Q and dO
+// (4 G S d bytes).
+inline int fwd_chunk_groups(int B, int Hkv, int S, int d) { return dispatch_chunk(B * Hkv, S, 4L * S * d); }
+inline int dq_chunk_groups(int B, int Hkv, int S, int d) { return dispatch_chunk(B * Hkv, S, 4L * S * d); }
+inline int dkdv_chunk_groups(int B, int Hq, int Hkv, int S, int d) {
+  return dispatch_chunk(B * Hkv, S, 4L * (Hq / Hkv) * S * d);
+}
+
 hipError_t launch_fwd(const FwdArgs& a, int d, bool causal, int exp_mode, bool pingpong, hipStream_t stream);
 // The same forward over a variable-length packed batch (a.cu_seqlens != nullptr).
 hipError_t launch_fwd_varlen(const FwdArgs& a, int d, bool causal, int exp_mode, bool pingpong, hipStream_t stream);

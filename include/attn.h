@@ -259,6 +259,32 @@ int attn_bwd_phase(int phase, const void* q, const void* k, const void* v, const
                    int B, int Hq, int Hkv, int S, int d, float scale, int causal,
                    void* workspace, size_t workspace_bytes, const attn_options* opt, void* stream);
 
+/*
+ * The launch plan that attn_fwd_ex and attn_bwd_ex follow for these sizes and options,
+ * computed on the host (no device is touched); for inspection and tests.  Arguments as
+ * for attn_fwd_ex (opt may be NULL for the defaults); out receives:
+ *   fwd_schedule  : ATTN_VARIANT_PINGPONG or ATTN_VARIANT_FOURWAVE, the dense forward's
+ *                   workgroup schedule;
+ *   fwd_chunk, dq_chunk, dkdv_chunk : (batch, KV head) groups per dispatch chunk of the
+ *                   forward, the dQ kernel and the dK/dV kernel (B * Hkv: one chunk).
+ *                   Large launches of sequences of at most 4096 keys run their grid in
+ *                   chunks of groups, one after the other, so that the operands the
+ *                   resident workgroups re-read stay in the memory-side cache;
+ *   dkdv_schedule : ATTN_VARIANT_PINGPONG (eight-wave) or ATTN_VARIANT_FOURWAVE, the
+ *                   dK/dV kernel's workgroup shape.
+ * Returns ATTN_OK, ATTN_ERR_NULL if out is NULL, or the size / option error that the
+ * entry points would return (out is then left unchanged).
+ */
+typedef struct attn_plan {
+    int fwd_schedule;
+    int fwd_chunk;
+    int dq_chunk;
+    int dkdv_chunk;
+    int dkdv_schedule;
+} attn_plan;
+int attn_launch_plan(int B, int Hq, int Hkv, int S, int d, int causal, const attn_options* opt,
+                     attn_plan* out);
+
 /* Human-readable name of a status code (never NULL). */
 const char* attn_status_string(int status);
 

@@ -21,18 +21,6 @@ from helpers import assert_bf16_close, assert_lse_close, f64
 pytestmark = pytest.mark.gpu
 
 DEV = "cuda:0"
-MIB = 1 << 20
-
-
-def chunk_groups(ngrp, S, group_bytes):
-    """Groups per dispatch chunk (the launchers' rule, restated to size these cases)."""
-    total = ngrp * group_bytes
-    if S > 4096 or total <= 160 * MIB:
-        return ngrp
-    nch = -(-total // (96 * MIB))
-    return min(ngrp, (-(-ngrp // nch) + 7) // 8 * 8)
-
-
 CASES = [
     # (B, Hq, Hkv, S, d, slices): 355 groups of 512,000 bytes of K and V (173 MiB): the
     # forward, dQ and dK/dV kernels run chunks of 184 and 171 groups (the last not a
@@ -53,13 +41,13 @@ def test_chunked_launch_equals_slices(case, causal):
     B, Hq, Hkv, S, d, cuts = case
     G = Hq // Hkv
     ngrp = B * Hkv
-    kv_chunk = chunk_groups(ngrp, S, 4 * G * S * d)
-    assert kv_chunk < ngrp  # the dK/dV kernel runs in chunks
+    plan = ea.attn_launch_plan(B, Hq, Hkv, S, d, causal)
+    assert plan["dkdv_chunk"] < ngrp  # the dK/dV kernel runs in chunks
     for lo, hi in zip(cuts[:-1], cuts[1:]):  # every slice is one chunk
+        ps = ea.attn_launch_plan(hi - lo, Hq, Hkv, S, d, causal)
         n = (hi - lo) * Hkv
-        assert chunk_groups(n, S, 4 * S * d) == n and chunk_groups(n, S, 4 * G * S * d) == n
-    print(f"\n[chunks] {case[:5]} causal={causal} chunks fwd/dQ {chunk_groups(ngrp, S, 4 * S * d)} "
-          f"dK/dV {kv_chunk} of {ngrp} groups", flush=True)
+        assert ps["fwd_chunk"] == ps["dq_chunk"] == ps["dkdv_chunk"] == n
+    print(f"\n[chunks] {case[:5]} causal={causal} plan {plan} of {ngrp} groups", flush=True)
     t = {n: x.to(DEV) for n, x in workloads.make_tensors(B, Hq, Hkv, S, d, seed=500 + B).items()}
     scale = d ** -0.5
     o, lse = ea.attn_fwd(t["q"], t["k"], t["v"], scale, causal)
