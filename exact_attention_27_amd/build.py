@@ -36,19 +36,26 @@ def command(out: str = LIB):
 
 PROBE_SRC = os.path.join(CSRC, "probes", "mfma_ceiling.hip")
 PROBE_BIN = os.path.join(PKG, "probes", "mfma_ceiling")
+# Further stand-alone probes: (source, binary).
+PROBES = [
+    (PROBE_SRC, PROBE_BIN),
+    (os.path.join(CSRC, "probes", "dq_atomics.hip"), os.path.join(PKG, "probes", "dq_atomics")),
+]
 
 
 def build_probe(verbose: bool = True) -> str:
-    """Compile the stand-alone MFMA ceiling probe (not part of the library) next to the
-    package, as a check that it builds; run it on a GPU to measure the ceiling."""
+    """Compile the stand-alone probes (not part of the library: the MFMA ceiling and the
+    fused-dQ atomic traffic) next to the package, as a check that they build; run them on
+    a GPU to measure.  Returns the MFMA ceiling probe's path."""
     os.makedirs(os.path.dirname(PROBE_BIN), exist_ok=True)
-    cmd = [hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17",
-           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-o", PROBE_BIN, PROBE_SRC]
-    if verbose:
-        print(" ".join(cmd), flush=True)
-    r = subprocess.run(cmd, capture_output=True, text=True)
-    if r.returncode != 0:
-        raise RuntimeError(f"hipcc failed ({r.returncode}):\n{r.stderr}")
+    for src, out in PROBES:
+        cmd = [hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17",
+               "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-o", out, src]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError(f"hipcc failed ({r.returncode}):\n{r.stderr}")
     return PROBE_BIN
 
 
