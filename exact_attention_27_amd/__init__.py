@@ -6,7 +6,9 @@ if libattn.so is missing or fails to load, every call raises.
 
 The functions carry the C names:
     attn_fwd, attn_fwd_ex, attn_fwd_varlen, attn_bwd, attn_bwd_ex, attn_bwd_phase, attn_bwd_workspace_bytes,
-    attn_bwd_noalloc, attn_default_options, attn_status_string, attn_exp2_eval, attn_exp2_poly_host
+    attn_bwd_noalloc, attn_launch_plan, attn_default_options, attn_status_string, attn_exp2_eval,
+    attn_exp2_poly_host
+and `attention` joins attn_fwd and attn_bwd under torch autograd.
 """
 
 from __future__ import annotations
@@ -21,7 +23,7 @@ import torch
 __all__ = [
     "AttnError", "attn_options", "library_path", "lib",
     "attn_fwd", "attn_fwd_ex", "attn_fwd_varlen", "attn_bwd", "attn_bwd_ex", "attn_bwd_phase", "attn_bwd_workspace_bytes",
-    "attn_bwd_noalloc", "ATTN_ERR_SCRATCH",
+    "attn_bwd_noalloc", "ATTN_ERR_SCRATCH", "attn_launch_plan", "attn_plan", "attention",
     "attn_default_options", "attn_status_string", "attn_exp2_eval", "attn_exp2_poly_host",
     "ATTN_EXP_HW", "ATTN_EXP_POLY3", "ATTN_VARIANT_AUTO", "ATTN_VARIANT_PINGPONG", "ATTN_VARIANT_FOURWAVE",
 ]
@@ -389,3 +391,32 @@ def attn_exp2_poly_host(x) -> "numpy.ndarray":  # noqa: F821
     y = np.empty_like(xa)
     lib().attn_exp2_poly_host(xa.ctypes.data_as(ctypes.c_void_p), y.ctypes.data_as(ctypes.c_void_p), xa.size)
     return y
+
+
+class _Attention(torch.autograd.Function):
+    """attn_fwd in the forward, attn_bwd in the backward (O and LSE kept for it)."""
+
+    @staticmethod
+    def forward(ctx, q, k, v, scale, causal):
+        o, lse = attn_fwd(q, k, v, scale, causal)
+        ctx.save_for_backward(q, k, v, o, lse)
+        ctx.scale, ctx.causal = scale, causal
+        ctx.mark_non_differentiable(lse)
+        return o, lse
+
+    @staticmethod
+    def backward(ctx, do, _dlse):
+        q, k, v, o, lse = ctx.saved_tensors
+        dq, dk, dv = attn_bwd(q, k, v, o, lse, do.contiguous(), ctx.scale, ctx.causal)
+        return dq, dk, dv, None, None
+
+
+def attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, scale: Optional[float] = None,
+              causal: bool = False, return_lse: bool = False):
+    """Exact attention with autograd: O = softmax(scale Q K^T [causal mask]) V on bf16
+    [B, Hq, S, d] Q and [B, Hkv, S, d] K, V (contiguous, one GPU), computed by attn_fwd;
+    the gradients of Q, K and V come from attn_bwd (so the incoming gradient of O is taken
+    as bf16, contiguous).  Returns O, or (O, LSE) with return_lse (LSE [B, Hq, S] fp32,
+    natural log, not differentiable)."""
+    o, lse = _Attention.apply(q, k, v, scale, causal)
+    return (o, lse) if return_lse else o
