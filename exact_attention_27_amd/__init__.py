@@ -23,6 +23,7 @@ import torch
 __all__ = [
     "AttnError", "attn_options", "library_path", "lib",
     "attn_fwd", "attn_fwd_ex", "attn_fwd_varlen", "attn_bwd", "attn_bwd_ex", "attn_bwd_phase", "attn_bwd_workspace_bytes",
+    "attn_bwd_varlen",
     "attn_bwd_noalloc", "ATTN_ERR_SCRATCH", "attn_launch_plan", "attn_plan", "attention",
     "attn_default_options", "attn_status_string", "attn_exp2_eval", "attn_exp2_poly_host",
     "ATTN_EXP_HW", "ATTN_EXP_POLY3", "ATTN_VARIANT_AUTO", "ATTN_VARIANT_PINGPONG", "ATTN_VARIANT_FOURWAVE",
@@ -95,6 +96,9 @@ def lib() -> ctypes.CDLL:
         L.attn_bwd_phase.restype = _I
         L.attn_bwd_phase.argtypes = [_I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I,
                                      _P, ctypes.c_size_t, ctypes.POINTER(attn_options), _P]
+        L.attn_bwd_varlen.restype = _I
+        L.attn_bwd_varlen.argtypes = [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _I,
+                                      _P, ctypes.c_size_t, ctypes.POINTER(attn_options), _P]
         L.attn_bwd_noalloc.restype = _I
         L.attn_bwd_noalloc.argtypes = [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _P]
         L.attn_exp2_eval.restype = _I
@@ -261,6 +265,56 @@ def attn_fwd_varlen(q, k, v, cu_seqlens, max_seqlen: int, scale: Optional[float]
                                    None if op is None else ctypes.byref(op), _stream(stream))
     _check(st)
     return o, lse
+
+
+def attn_bwd_varlen(q, k, v, o, lse, do, cu_seqlens, max_seqlen: int, scale: Optional[float] = None,
+                    causal: bool = False, dq=None, dk=None, dv=None, workspace: Optional[torch.Tensor] = None,
+                    opt: Optional[attn_options] = None, exp_mode: Optional[int] = None,
+                    tau: Optional[float] = None, stream=None, variant: Optional[int] = None):
+    """Backward pass over a packed batch (the gradients of attn_fwd_varlen).
+
+    q, o, do: [total, Hq, d], k and v: [total, Hkv, d] bf16; lse: [Hq, total] fp32 (as
+    attn_fwd_varlen returns it); cu_seqlens: [nseq + 1] int32 device tensor of token
+    offsets; max_seqlen must be >= every length.  Returns (dq, dk, dv) in the layouts of
+    q, k and v; rows outside every sequence are left as allocated (torch.empty).
+    workspace (uint8, >= attn_bwd_workspace_bytes(nseq, Hq, Hkv, max_seqlen, d)) is
+    allocated with torch when not given.  scale defaults to 1/sqrt(d)."""
+    if q.dim() != 3 or k.dim() != 3:
+        raise ValueError("q and k must be [total, H, d]")
+    total, Hq, d = (int(x) for x in q.shape)
+    Hkv = int(k.shape[1])
+    _need(q, "q", torch.bfloat16, (total, Hq, d))
+    _need(k, "k", torch.bfloat16, (total, Hkv, d))
+    _need(v, "v", torch.bfloat16, (total, Hkv, d))
+    _need(o, "o", torch.bfloat16, (total, Hq, d))
+    _need(lse, "lse", torch.float32, (Hq, total))
+    _need(do, "do", torch.bfloat16, (total, Hq, d))
+    if cu_seqlens.dtype != torch.int32 or cu_seqlens.dim() != 1 or not cu_seqlens.is_contiguous():
+        raise ValueError("cu_seqlens must be a contiguous 1-D int32 tensor")
+    nseq = max(int(cu_seqlens.numel()) - 1, 0)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    _need(dq, "dq", torch.bfloat16, (total, Hq, d))
+    _need(dk, "dk", torch.bfloat16, (total, Hkv, d))
+    _need(dv, "dv", torch.bfloat16, (total, Hkv, d))
+    if workspace is not None and (not isinstance(workspace, torch.Tensor) or not workspace.is_contiguous()):
+        raise ValueError("workspace must be a contiguous tensor")
+    _same_gpu(q=q, k=k, v=v, o=o, lse=lse, do=do, cu_seqlens=cu_seqlens, dq=dq, dk=dk, dv=dv,
+              **({} if workspace is None else {"workspace": workspace}))
+    nbytes = attn_bwd_workspace_bytes(nseq, Hq, Hkv, int(max_seqlen), d)
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    op = _options(opt, exp_mode, tau, variant)
+    with _on(q.device):
+        st = lib().attn_bwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(do),
+                                   _ptr(dq), _ptr(dk), _ptr(dv), _ptr(cu_seqlens), nseq, total, int(max_seqlen),
+                                   Hq, Hkv, d, scale, int(bool(causal)), _ptr(workspace),
+                                   workspace.numel() * workspace.element_size(),
+                                   None if op is None else ctypes.byref(op), _stream(stream))
+    _check(st)
+    return dq, dk, dv
 
 
 def attn_fwd(q, k, v, scale: Optional[float] = None, causal: bool = False,

@@ -306,9 +306,65 @@ int attn_bwd_phase(int phase, const void* q, const void* k, const void* v, const
   a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.S = S;
   a.scale = scale;
   scale_setup(scale, &a.c, &a.q_and, &a.q_xor);
+  a.cu_seqlens = nullptr;
+  a.total = 0;
   (void)hipGetLastError();
   return hip_status(attn::launch_bwd(a, d, causal != 0, o_.exp_mode, bwd_four_wave(o_.variant, Hq / Hkv, S), phases,
                                      static_cast<hipStream_t>(stream)));
+}
+
+int attn_bwd_varlen(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                    const void* dO, void* dq, void* dk, void* dv,
+                    const int* cu_seqlens, int nseq, int total, int max_seqlen,
+                    int Hq, int Hkv, int d, float scale, int causal,
+                    void* workspace, size_t workspace_bytes, const attn_options* opt, void* stream) {
+  if (nseq < 0 || total < 0 || max_seqlen < 0 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0) return ATTN_ERR_SHAPE;
+  if (d != 64 && d != 128) return ATTN_ERR_UNSUPPORTED;
+  // The grids and the workspace are those of a dense batch of nseq sequences of
+  // max_seqlen rows; per-lane offsets within a tile of token-major rows are 32-bit.
+  bool empty = false;
+  int st = check_sizes(nseq, Hq, Hkv, max_seqlen, d, &empty);
+  if (st != ATTN_OK) return st;
+  if ((int64_t)Hq * d * 64 * 2 >= (int64_t)1 << 31) return ATTN_ERR_SHAPE;
+  const attn_options o_ = opt ? *opt : attn_default_options();
+  if ((st = check_options(o_)) != ATTN_OK) return st;
+  if (!std::isfinite(scale)) return ATTN_ERR_VALUE;
+  if (empty || total == 0) return ATTN_OK;
+  if (!q || !k || !v || !o || !lse || !dO || !dq || !dk || !dv || !cu_seqlens) return ATTN_ERR_NULL;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse) ||
+      !aligned16(dO) || !aligned16(dq) || !aligned16(dk) || !aligned16(dv) ||
+      (reinterpret_cast<uintptr_t>(cu_seqlens) & 3u) != 0)
+    return ATTN_ERR_ALIGN;
+  const size_t need = attn_bwd_workspace_bytes(nseq, Hq, Hkv, max_seqlen, d);
+  if (!workspace || workspace_bytes < need || (reinterpret_cast<uintptr_t>(workspace) % kAlign) != 0)
+    return ATTN_ERR_WORKSPACE;
+
+  attn::BwdArgs a;
+  a.q = static_cast<const uint16_t*>(q);
+  a.k = static_cast<const uint16_t*>(k);
+  a.v = static_cast<const uint16_t*>(v);
+  a.o = static_cast<const uint16_t*>(o);
+  a.lse = lse;
+  a.dO = static_cast<const uint16_t*>(dO);
+  a.dq = static_cast<uint16_t*>(dq);
+  a.dk = static_cast<uint16_t*>(dk);
+  a.dv = static_cast<uint16_t*>(dv);
+  const BwdWorkspace wl = bwd_workspace(nseq, Hq, Hkv, max_seqlen, d);
+  char* ws = static_cast<char*>(workspace);
+  a.delta = reinterpret_cast<float*>(ws + wl.delta);
+  a.lse2 = reinterpret_cast<float*>(ws + wl.lse2);
+  a.ndx = reinterpret_cast<float*>(ws + wl.ndx);
+  a.pmax = reinterpret_cast<float*>(ws + wl.pmax);
+  a.do16 = reinterpret_cast<uint16_t*>(ws + wl.do16);
+  a.q16 = reinterpret_cast<uint16_t*>(ws + wl.q16);
+  a.B = nseq; a.Hq = Hq; a.Hkv = Hkv; a.S = max_seqlen;
+  a.scale = scale;
+  scale_setup(scale, &a.c, &a.q_and, &a.q_xor);
+  a.cu_seqlens = cu_seqlens;
+  a.total = total;
+  (void)hipGetLastError();
+  return hip_status(attn::launch_bwd(a, d, causal != 0, o_.exp_mode, bwd_four_wave(o_.variant, Hq / Hkv, max_seqlen),
+                                     7, static_cast<hipStream_t>(stream)));
 }
 
 int attn_bwd_noalloc(const void* q, const void* k, const void* v, const void* o, const float* lse,

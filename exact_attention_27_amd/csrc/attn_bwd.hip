@@ -62,7 +62,7 @@ __device__ __forceinline__ float absmax8(float m, const u32x4& w) {
   return m;
 }
 
-template <int D>
+template <int D, bool VARLEN>
 __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdArgs a, int S_pad) {
   constexpr int LPR = D / 8;     // lanes per row, 8 bf16 each
   constexpr int RPI = 256 / LPR;  // rows per pass of the workgroup
@@ -73,7 +73,29 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdArgs a, int S_pad) {
   const int nb = blockIdx.x - grp * kPreBlocks;
   const int b = grp / a.Hkv;
   const int hkv = grp - b * a.Hkv;
-  const int S = a.S;
+  // This sequence's rows: S of them; row i of query head h of O, dO, Q at element
+  // qbase + i rs_q + h D, of LSE at lse[lbase + h ls_h + i], row i of K and V at
+  // kvb + i rs_kv.  (a.S is the rows of a (batch, head) in the workspace's layout.)
+  int S;
+  size_t qbase, kvb, lbase, ls_h;
+  int rs_q = D, rs_kv = D;
+  if constexpr (VARLEN) {
+    const int start = min(max(a.cu_seqlens[b], 0), a.total);
+    const int end = min(max(a.cu_seqlens[b + 1], start), a.total);
+    S = min(end - start, a.S);
+    rs_q = a.Hq * D;
+    rs_kv = a.Hkv * D;
+    qbase = (size_t)start * rs_q;
+    kvb = (size_t)start * rs_kv + (size_t)hkv * D;
+    lbase = start;
+    ls_h = a.total;
+  } else {
+    S = a.S;
+    qbase = (size_t)b * a.Hq * S * D;
+    kvb = (size_t)grp * S * D;
+    lbase = (size_t)b * a.Hq * S;
+    ls_h = S;
+  }
 
   // O, dO, Q: the group's padded rows [row0, row0 + G * S_pad), this workgroup's share.
   const long row0 = ((long)b * a.Hq + (long)hkv * G) * S_pad;
@@ -92,11 +114,13 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdArgs a, int S_pad) {
       const int hl = (int)(r / S_pad);
       const int srow = (int)(r - (long)hl * S_pad);
       real[u] = r < r_end && srow < S;
-      row[u] = ((long)b * a.Hq + (long)hkv * G + hl) * S + srow;  // unpadded [B*Hq][S] row
+      const int h = hkv * G + hl;  // query head
+      row[u] = real[u] ? (long)(lbase + (size_t)h * ls_h) + srow : 0;  // LSE index of the row
+      const size_t e = VARLEN ? qbase + (size_t)srow * rs_q + (size_t)h * D : (size_t)row[u] * D;
       if (real[u]) {
-        ov[u] = *(const u32x4*)(a.o + row[u] * D + part * 8);
-        dv[u] = *(const u32x4*)(a.dO + row[u] * D + part * 8);
-        qv[u] = *(const u32x4*)(a.q + row[u] * D + part * 8);
+        ov[u] = *(const u32x4*)(a.o + e + part * 8);
+        dv[u] = *(const u32x4*)(a.dO + e + part * 8);
+        qv[u] = *(const u32x4*)(a.q + e + part * 8);
       } else {
         ov[u] = dv[u] = qv[u] = u32x4{0u, 0u, 0u, 0u};
       }
@@ -125,11 +149,10 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdArgs a, int S_pad) {
   // K, V: the group's S rows, this workgroup's share.
   const long vper = (((long)S + kPreBlocks - 1) / kPreBlocks + RPI - 1) / RPI * RPI;
   const long v_end = min((long)S, (nb + 1) * vper);
-  const size_t kvb = (size_t)grp * S * D;
   float mv = 0.0f, mk = 0.0f;
   for (long r = nb * vper + tid / LPR; r < v_end; r += RPI) {
-    mv = absmax8(mv, *(const u32x4*)(a.v + kvb + r * D + part * 8));
-    mk = absmax8(mk, *(const u32x4*)(a.k + kvb + r * D + part * 8));
+    mv = absmax8(mv, *(const u32x4*)(a.v + kvb + r * rs_kv + part * 8));
+    mk = absmax8(mk, *(const u32x4*)(a.k + kvb + r * rs_kv + part * 8));
   }
   // Workgroup maxima: within each wave, then across the 4 waves through LDS.
   float m[kMaxes];
@@ -235,14 +258,14 @@ __device__ __forceinline__ u32x4 bf16x8_to_f16x8(u32x4 w, float sc) {
 //   dK^T += Q^T dS
 // so the vector work of each phase runs next to matrix products that do not need it;
 // LDS reads run two slots ahead of their products.
-template <int D, bool CAUSAL, int EXPMODE, int NW>
+template <int D, bool CAUSAL, int EXPMODE, int NW, bool VARLEN>
 __global__ __attribute__((amdgpu_flat_work_group_size(64 * NW, 64 * NW), amdgpu_waves_per_eu(2, 2)))
 void bwd_main_kernel(BwdArgs a) {
   static_assert(NW == 4 || NW == 8, "4 or 8 waves per workgroup");
   constexpr int KSTEPS = D / 16;
   constexpr int DBLK = D / 32;
   constexpr int CG = D / 32;                   // 4-chunk groups per row
-  constexpr int ROWB = D * 2;                  // bytes per row in memory
+  constexpr int ROWB = D * 2;                  // bytes per row of the fp16 Q and dO copies
   constexpr int BM = 32 * (NW / 4);            // queries per step
   constexpr int NT = 64 * NW;                  // threads
   constexpr int KT = kBwdBN * D;               // elements of the K (or V) tile
@@ -286,7 +309,6 @@ void bwd_main_kernel(BwdArgs a) {
   const int col = lane & 31;
   const int half = lane >> 5;
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
-  const int S = a.S;
   const int G = a.Hq / a.Hkv;
 
   // Dispatch order: chunks of kv_chunk KV groups one after the other (dispatch_chunk);
@@ -295,7 +317,7 @@ void bwd_main_kernel(BwdArgs a) {
   // all key tiles of one group run on one XCD (XCD = block index % 8) and share its L2
   // for the group's Q and dO.
   const int ngrp = a.B * a.Hkv;
-  const int nkt = (S + kBwdBN - 1) / kBwdBN;
+  const int nkt = (a.S + kBwdBN - 1) / kBwdBN;
   const int per_chunk = a.kv_chunk * nkt;
   const int chunk = (int)blockIdx.x / per_chunk;
   const int pos = (int)blockIdx.x - chunk * per_chunk;
@@ -307,7 +329,23 @@ void bwd_main_kernel(BwdArgs a) {
   const int k0 = kt * kBwdBN;
   const int kw = k0 + kq * 32;
   const int key = kw + col;  // this lane's key (column of S)
-  const size_t kvbase = ((size_t)b * a.Hkv + hkv) * (size_t)S * D;
+  // This sequence's rows: S of them; row i of K, V, dK, dV at element kvbase + i rs_kv
+  // (kvbase includes the head).  a.S is the rows of a (batch, head) in the workspace's
+  // dense layout (the fp16 Q and dO copies, LSE and D): with VARLEN the longest sequence.
+  int S;
+  size_t kvbase;
+  int rs_kv = D;
+  if constexpr (VARLEN) {
+    const int start = min(max(a.cu_seqlens[b], 0), a.total);
+    const int end = min(max(a.cu_seqlens[b + 1], start), a.total);
+    S = min(end - start, a.S);
+    if (k0 >= S) return;  // the whole workgroup: this key tile lies past its sequence
+    rs_kv = a.Hkv * D;
+    kvbase = (size_t)start * rs_kv + (size_t)hkv * D;
+  } else {
+    S = a.S;
+    kvbase = ((size_t)b * a.Hkv + hkv) * (size_t)S * D;
+  }
 
   // DMA: wave w fills blocks i * NW + w of a tile; block bl holds rows 16 (bl / CG) ..,
   // chunks 4 (bl % CG) ..; lane l fetches row l / 4 of it, chunk (l % 4) ^ ((l / 16) % 4).
@@ -320,7 +358,7 @@ void bwd_main_kernel(BwdArgs a) {
     for (int i = 0; i < KDMAS; ++i) {
       const int bl = i * NW + wave;
       const int r = (bl / CG) * 16 + dl_r;
-      const size_t src = kvbase + (size_t)min(k0 + r, S - 1) * D + ((bl % CG) * 4 + dl_c) * 8;
+      const size_t src = kvbase + (size_t)min(k0 + r, S - 1) * rs_kv + ((bl % CG) * 4 + dl_c) * 8;
       dma16(src_t + src, dst + (i * NW + wave_u) * 512);
     }
   };
@@ -331,7 +369,7 @@ void bwd_main_kernel(BwdArgs a) {
   const int q_first = CAUSAL ? (k0 / BM) : 0;
   const int per_head = nqt - q_first;
   const int steps = G * per_head;
-  const int S_pad = (S + kBwdBM - 1) / kBwdBM * kBwdBM;
+  const int S_pad = (a.S + kBwdBM - 1) / kBwdBM * kBwdBM;
 
   // Per-lane byte offsets of the Q / dO DMA within a tile.
   uint32_t qd_off[QDMAS];
@@ -354,7 +392,7 @@ void bwd_main_kernel(BwdArgs a) {
       --stage_qt;
     }
     const int hq = hkv * G + g;
-    const size_t rbase = ((size_t)b * a.Hq + hq) * (size_t)S;
+    const size_t rbase = ((size_t)b * a.Hq + hq) * (size_t)a.S;
     const int q0 = qt * BM;
     const char* qb = (const char*)(a.q16 + (rbase + q0) * D);
     const char* ob = (const char*)(a.do16 + (rbase + q0) * D);
@@ -638,8 +676,8 @@ void bwd_main_kernel(BwdArgs a) {
     const float vs = ldexpf(1.0f, -gs.e_do);
     // The lane's half, recomputed here rather than kept live across the loop.
     const int half = __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u)) >> 5;
-    uint16_t* dkr = a.dk + kvbase + (size_t)key * D;
-    uint16_t* dvr = a.dv + kvbase + (size_t)key * D;
+    uint16_t* dkr = a.dk + kvbase + (size_t)key * rs_kv;
+    uint16_t* dvr = a.dv + kvbase + (size_t)key * rs_kv;
 #pragma unroll
     for (int db = 0; db < DBLK; ++db) {
 #pragma unroll
@@ -686,7 +724,7 @@ void bwd_main_kernel(BwdArgs a) {
 constexpr int kDqBM = 128;  // queries per workgroup
 constexpr int kDqBN = 64;   // keys per tile
 
-template <int D, bool CAUSAL, int EXPMODE>
+template <int D, bool CAUSAL, int EXPMODE, bool VARLEN>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(2, 2)))
 void bwd_dq_kernel(BwdArgs a) {
   constexpr int BN = kDqBN;
@@ -694,7 +732,6 @@ void bwd_dq_kernel(BwdArgs a) {
   constexpr int KSTEPS = D / 16;
   constexpr int DBLK = D / 32;
   constexpr int CG = D / 32;            // 4-chunk groups per row
-  constexpr int ROWB = D * 2;           // bytes per row in memory
   constexpr int TILE = BN * D;          // elements of one K or V tile
   constexpr int DMAS = BN / 16 * CG / 4;  // 1024-byte blocks per wave per tile
   constexpr int NA = KSTEPS * KB;       // S^T slots
@@ -709,10 +746,11 @@ void bwd_dq_kernel(BwdArgs a) {
   const int wave = tid >> 6;
   const int col = lane & 31;
   const int half = lane >> 5;
-  const int S = a.S;
-  const int S_pad = (S + kBwdBM - 1) / kBwdBM * kBwdBM;
+  // a.S: rows of a (batch, head) in the workspace's dense layout, and the grid's; with
+  // VARLEN the longest sequence, otherwise every sequence's length.
+  const int S_pad = (a.S + kBwdBM - 1) / kBwdBM * kBwdBM;
 
-  const int nqt = (S + kDqBM - 1) / kDqBM;
+  const int nqt = (a.S + kDqBM - 1) / kDqBM;
   const int bid = blockIdx.x;
   // Dispatch order and head of this workgroup, as in the forward: chunks of dq_chunk KV
   // groups (dispatch_chunk), within a chunk the longest query tiles first; with the
@@ -742,6 +780,28 @@ void bwd_dq_kernel(BwdArgs a) {
   const int hkv = kvg - b * a.Hkv;
   const int hq = hkv * G + g;
   const int q0 = qt * kDqBM;
+  // This sequence's rows: S of them; row i of head h of Q, dO, dQ (K, V) at element
+  // qbase + i rs_q (kvbase + i rs_kv), where qbase and kvbase include the head.
+  int S;
+  size_t qbase, kvbase;
+  int rs_q = D, rs_kv = D;
+  if constexpr (VARLEN) {
+    const int start = min(max(a.cu_seqlens[b], 0), a.total);
+    const int end = min(max(a.cu_seqlens[b + 1], start), a.total);
+    S = min(end - start, a.S);
+    if (q0 >= S) return;  // the whole workgroup: this tile lies past its sequence
+    rs_q = a.Hq * D;
+    rs_kv = a.Hkv * D;
+    qbase = (size_t)start * rs_q + (size_t)hq * D;
+    kvbase = (size_t)start * rs_kv + (size_t)hkv * D;
+  } else {
+    S = a.S;
+    qbase = ((size_t)b * a.Hq + hq) * (size_t)S * D;
+    kvbase = ((size_t)b * a.Hkv + hkv) * (size_t)S * D;
+  }
+  const int ROWB = rs_kv * 2;  // bytes between K/V rows in memory
+  // This (batch or sequence, head)'s rows of the workspace's fp16 Q and dO copies.
+  const size_t wbase = ((size_t)b * a.Hq + hq) * (size_t)a.S * D;
   const int qw = q0 + wave * 32;
   const int qi = qw + col;  // this lane's query
   const int qc = min(qi, S - 1);  // rows past the end read the last row; never stored
@@ -749,8 +809,6 @@ void bwd_dq_kernel(BwdArgs a) {
   // against a bound past any sequence (kept opaque): with the tests folded away at compile
   // time the compiler's allocation for them exceeds the 256 registers and spills.
   const int qhi = CAUSAL ? qw : opaque(0x3fffffff);
-  const size_t qbase = ((size_t)b * a.Hq + hq) * (size_t)S * D;
-  const size_t kvbase = ((size_t)b * a.Hkv + hkv) * (size_t)S * D;
   const uint16_t* __restrict__ Kg = a.k + kvbase;
   const uint16_t* __restrict__ Vg = a.v + kvbase;
 
@@ -767,7 +825,7 @@ void bwd_dq_kernel(BwdArgs a) {
     dma_off[i] = (uint32_t)(((bl / CG) * 16 + dl_r) * ROWB + ((bl % CG) * 4 + dl_c) * 16);
   }
   auto dma_tile = [&](const uint16_t* __restrict__ src, int j, uint16_t* slot) {
-    const char* base = (const char*)(src + (size_t)j * BN * D);
+    const char* base = (const char*)(src + (size_t)j * BN * rs_kv);
     if (j * BN + BN <= S) {
 #pragma unroll
       for (int i = 0; i < DMAS; ++i) dma16_s(base, dma_off[i], slot + (i * 4 + wave_u) * 512);
@@ -792,8 +850,8 @@ void bwd_dq_kernel(BwdArgs a) {
   // Q^T and dO^T fragments (B operands): query qc, d = ks*16 + half*8 .. +7.
   bf16x8 qf[KSTEPS], of[KSTEPS];
   {
-    const u32x4* qrow = (const u32x4*)(a.q + qbase + (size_t)qc * D + half * 8);
-    const u32x4* orow = (const u32x4*)(a.dO + qbase + (size_t)qc * D + half * 8);
+    const u32x4* qrow = (const u32x4*)(a.q + qbase + (size_t)qc * rs_q + half * 8);
+    const u32x4* orow = (const u32x4*)(a.dO + qbase + (size_t)qc * rs_q + half * 8);
 #pragma unroll
     for (int ks = 0; ks < KSTEPS; ++ks) {
       qf[ks] = __builtin_bit_cast(bf16x8, qrow[ks * 2]);
@@ -805,8 +863,8 @@ void bwd_dq_kernel(BwdArgs a) {
   const GroupScales gs = group_scales(a.pmax, kvg);
   if (qi < S) {
     const float so = ldexpf(1.0f, gs.e_do), sq = ldexpf(1.0f, gs.e_q);
-    u32x4* dst_o = (u32x4*)(a.do16 + qbase + (size_t)qi * D + half * 8);
-    u32x4* dst_q = (u32x4*)(a.q16 + qbase + (size_t)qi * D + half * 8);
+    u32x4* dst_o = (u32x4*)(a.do16 + wbase + (size_t)qi * D + half * 8);
+    u32x4* dst_q = (u32x4*)(a.q16 + wbase + (size_t)qi * D + half * 8);
 #pragma unroll
     for (int ks = 0; ks < KSTEPS; ++ks) {
       dst_o[ks * 2] = bf16x8_to_f16x8(__builtin_bit_cast(u32x4, of[ks]), so);
@@ -968,7 +1026,7 @@ void bwd_dq_kernel(BwdArgs a) {
     a.ndx[pr] = qi < S ? (nd0 - dtot) * ldexpf(1.0f, gs.e_do + gs.e_v) : 0.0f;
   }
   if (qi < S) {
-    uint16_t* dqr = a.dq + qbase + (size_t)qi * D;
+    uint16_t* dqr = a.dq + qbase + (size_t)qi * rs_q;
     const float sc = a.scale;
 #pragma unroll
     for (int db = 0; db < DBLK; ++db) {
@@ -983,7 +1041,7 @@ void bwd_dq_kernel(BwdArgs a) {
   }
 }
 
-template <int D, bool CAUSAL, int EXPMODE>
+template <int D, bool CAUSAL, int EXPMODE, bool VARLEN>
 hipError_t launch_bwd_t(const BwdArgs& a0, bool four_wave, int phases, hipStream_t stream) {
   hipError_t e = hipSuccess;
   BwdArgs a = a0;
@@ -993,12 +1051,13 @@ hipError_t launch_bwd_t(const BwdArgs& a0, bool four_wave, int phases, hipStream
   // kernel reads), dK/dV.
   if (phases & 1) {
     const int S_pad = (a.S + kBwdBM - 1) / kBwdBM * kBwdBM;
-    hipLaunchKernelGGL(bwd_pre_kernel<D>, dim3((unsigned)(a.B * a.Hkv * kPreBlocks)), dim3(256), 0, stream, a, S_pad);
+    hipLaunchKernelGGL((bwd_pre_kernel<D, VARLEN>), dim3((unsigned)(a.B * a.Hkv * kPreBlocks)), dim3(256), 0, stream, a,
+                       S_pad);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   if (phases & 4) {
     const int nqt = (a.S + kDqBM - 1) / kDqBM;
-    hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL, EXPMODE>), dim3((unsigned)(nqt * a.B * a.Hq)), dim3(256), 0,
+    hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL, EXPMODE, VARLEN>), dim3((unsigned)(nqt * a.B * a.Hq)), dim3(256), 0,
                        stream, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
@@ -1008,37 +1067,41 @@ hipError_t launch_bwd_t(const BwdArgs& a0, bool four_wave, int phases, hipStream
     // Four-wave workgroups (two per CU) need K's fragments in registers: always at d = 64,
     // at d = 128 with the hardware exponential only.
     if constexpr (D == 64) {
-      hipLaunchKernelGGL((bwd_main_kernel<D, CAUSAL, EXPMODE, 4>), grid, dim3(256), 0, stream, a);
+      hipLaunchKernelGGL((bwd_main_kernel<D, CAUSAL, EXPMODE, 4, VARLEN>), grid, dim3(256), 0, stream, a);
     } else if constexpr (EXPMODE == 0) {
       if (four_wave) {
-        hipLaunchKernelGGL((bwd_main_kernel<D, CAUSAL, EXPMODE, 4>), grid, dim3(256), 0, stream, a);
+        hipLaunchKernelGGL((bwd_main_kernel<D, CAUSAL, EXPMODE, 4, VARLEN>), grid, dim3(256), 0, stream, a);
       } else {
-        hipLaunchKernelGGL((bwd_main_kernel<D, CAUSAL, EXPMODE, 8>), grid, dim3(512), 0, stream, a);
+        hipLaunchKernelGGL((bwd_main_kernel<D, CAUSAL, EXPMODE, 8, VARLEN>), grid, dim3(512), 0, stream, a);
       }
     } else {
-      hipLaunchKernelGGL((bwd_main_kernel<D, CAUSAL, EXPMODE, 8>), grid, dim3(512), 0, stream, a);
+      hipLaunchKernelGGL((bwd_main_kernel<D, CAUSAL, EXPMODE, 8, VARLEN>), grid, dim3(512), 0, stream, a);
     }
     e = hipGetLastError();
   }
   return e;
 }
 
-template <int D>
+template <int D, bool VARLEN>
 hipError_t launch_bwd_d(const BwdArgs& a, bool causal, int exp_mode, bool four_wave, int phases, hipStream_t stream) {
   if (causal) {
-    return exp_mode == 0 ? launch_bwd_t<D, true, 0>(a, four_wave, phases, stream)
-                         : launch_bwd_t<D, true, 1>(a, four_wave, phases, stream);
+    return exp_mode == 0 ? launch_bwd_t<D, true, 0, VARLEN>(a, four_wave, phases, stream)
+                         : launch_bwd_t<D, true, 1, VARLEN>(a, four_wave, phases, stream);
   }
-  return exp_mode == 0 ? launch_bwd_t<D, false, 0>(a, four_wave, phases, stream)
-                       : launch_bwd_t<D, false, 1>(a, four_wave, phases, stream);
+  return exp_mode == 0 ? launch_bwd_t<D, false, 0, VARLEN>(a, four_wave, phases, stream)
+                       : launch_bwd_t<D, false, 1, VARLEN>(a, four_wave, phases, stream);
 }
 
 }  // namespace
 
 hipError_t launch_bwd(const BwdArgs& a, int d, bool causal, int exp_mode, bool four_wave, int phases,
                       hipStream_t stream) {
-  return d == 64 ? launch_bwd_d<64>(a, causal, exp_mode, four_wave, phases, stream)
-                 : launch_bwd_d<128>(a, causal, exp_mode, four_wave, phases, stream);
+  if (a.cu_seqlens != nullptr) {
+    return d == 64 ? launch_bwd_d<64, true>(a, causal, exp_mode, four_wave, phases, stream)
+                   : launch_bwd_d<128, true>(a, causal, exp_mode, four_wave, phases, stream);
+  }
+  return d == 64 ? launch_bwd_d<64, false>(a, causal, exp_mode, four_wave, phases, stream)
+                 : launch_bwd_d<128, false>(a, causal, exp_mode, four_wave, phases, stream);
 }
 
 }  // namespace attn

@@ -58,6 +58,13 @@ struct BwdArgs {
   uint32_t q_and, q_xor;
   // KV groups per dispatch chunk of the dQ and the dK/dV kernels (set by the launcher).
   int dq_chunk, kv_chunk;
+  // Variable-length (packed) batches; nullptr for the dense [B, H, S, d] layout.  With
+  // cu_seqlens set, B is the number of sequences and S the longest sequence (it sizes the
+  // grids and the workspace's dense layout above); q, o, dO, dq are [total, Hq, d], k, v,
+  // dk, dv [total, Hkv, d] and lse [Hq, total]; sequence b is the rows cu_seqlens[b] ..
+  // cu_seqlens[b + 1] - 1 (clamped to [0, total]), of which the first S are used.
+  const int* cu_seqlens;
+  int total;
 };
 
 // Dispatch chunks.  A launch whose workgroups of one (batch, KV head) group all re-read
@@ -91,6 +98,7 @@ hipError_t launch_fwd(const FwdArgs& a, int d, bool causal, int exp_mode, bool p
 // The same forward over a variable-length packed batch (a.cu_seqlens != nullptr).
 hipError_t launch_fwd_varlen(const FwdArgs& a, int d, bool causal, int exp_mode, bool pingpong, hipStream_t stream);
 // phases: bit 0 = preprocess (D, LSE log2 e), bit 1 = dK/dV kernel, bit 2 = dQ kernel.
+// A packed batch when a.cu_seqlens is set.
 // 7 runs the whole backward.
 // four_wave: the dK/dV kernel in four-wave workgroups, two per CU (d = 64 always; at
 // d = 128 only with the hardware exponential); otherwise eight-wave workgroups, one per CU.

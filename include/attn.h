@@ -216,6 +216,33 @@ int attn_bwd_ex(const void* q, const void* k, const void* v, const void* o, cons
                 void* workspace, size_t workspace_bytes, const attn_options* opt, void* stream);
 
 /*
+ * Backward pass over a variable-length (packed) batch: the gradients of attn_fwd_varlen,
+ * for training on sequences of different lengths laid end to end (the packed batches of
+ * the pages' integration targets, hyper.ai FlashAttention-4 story; the backward itself:
+ * "NVIDIA Blackwell: FlashAttention-4 Overcomes Memory Bottlenecks", body paragraph).
+ * Each sequence is its own attention problem, exactly as attn_bwd computes it.  Layout,
+ * token-major, as attn_fwd_varlen:
+ *     q, o, dO, dq : [total, Hq,  d] bf16     k, v, dk, dv : [total, Hkv, d] bf16
+ *     lse          : [Hq, total]     fp32 (as attn_fwd_varlen writes it)
+ *     cu_seqlens   : [nseq + 1] int32 DEVICE array, as for attn_fwd_varlen.
+ * max_seqlen must be >= every sequence's length: a longer sequence is taken as its first
+ * max_seqlen rows (keys and queries), and its later rows of dq, dk and dv are not
+ * written.  Rows not covered by any sequence are not written; overlapping sequences (offsets
+ * that are not non-decreasing) leave the rows they share unspecified.  Offsets outside
+ * [0, total] are clamped, so no access leaves the tensors.  workspace: at least
+ * attn_bwd_workspace_bytes(nseq, Hq, Hkv, max_seqlen, d) bytes, 256-byte aligned, owned
+ * by the caller (the dense layout of nseq sequences of max_seqlen rows; contents on
+ * entry do not matter).  nseq == 0, total == 0 or max_seqlen == 0 is an empty problem
+ * (ATTN_OK, nothing launched).  Rounding, determinism, checks and the other conventions
+ * are those of attn_bwd_ex; opt == NULL means the defaults.
+ */
+int attn_bwd_varlen(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                    const void* dO, void* dq, void* dk, void* dv,
+                    const int* cu_seqlens, int nseq, int total, int max_seqlen,
+                    int Hq, int Hkv, int d, float scale, int causal,
+                    void* workspace, size_t workspace_bytes, const attn_options* opt, void* stream);
+
+/*
  * attn_bwd for callers that cannot allocate device memory or pass a workspace: code
  * under HIP graph capture, tight serving loops, harnesses that forbid allocation.  It
  * calls no allocating routine.  Its scratch is a static device array of 64 MiB that the

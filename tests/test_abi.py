@@ -251,3 +251,49 @@ def test_noalloc_checks_before_any_hip_call():
     assert ea.attn_bwd_workspace_bytes(1, 16, 16, 8192, 128) > 64 << 20
     assert call(B=1, Hq=16, Hkv=16, S=8192, d=128) == SCRATCH
     assert "64 MiB" in ea.attn_status_string(SCRATCH)
+
+
+def bwd_varlen(q=A, k=A, v=A, o=A, lse=A, do=A, dq=A, dk=A, dv=A, cu=ctypes.c_void_p(0x30000), nseq=2, total=16,
+               max_seqlen=8, Hq=2, Hkv=1, d=64, scale=0.125, causal=0, ws=A2, wsb=None, opt=None):
+    lib = ea.lib()
+    if wsb is None:
+        wsb = max(ea.attn_bwd_workspace_bytes(max(nseq, 0), Hq, Hkv, max(max_seqlen, 0), d), 1) if Hq >= 1 and Hkv >= 1 else 1
+    return lib.attn_bwd_varlen(q, k, v, o, lse, do, dq, dk, dv, cu, nseq, total, max_seqlen, Hq, Hkv, d, scale,
+                               causal, ws, wsb, None if opt is None else ctypes.byref(opt), None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), NULL), (dict(k=None), NULL), (dict(v=None), NULL), (dict(o=None), NULL), (dict(lse=None), NULL),
+    (dict(do=None), NULL), (dict(dq=None), NULL), (dict(dk=None), NULL), (dict(dv=None), NULL), (dict(cu=None), NULL),
+    (dict(nseq=-1), SHAPE), (dict(total=-1), SHAPE), (dict(max_seqlen=-1), SHAPE), (dict(Hq=3, Hkv=2), SHAPE),
+    (dict(Hkv=0), SHAPE), (dict(nseq=1 << 30, max_seqlen=1 << 30, Hq=64, Hkv=64), SHAPE),
+    (dict(d=96), UNSUP), (dict(opt=ea.attn_options(4, 8.0, 0)), UNSUP),
+    (dict(dk=ctypes.c_void_p(0x10008)), ALIGN), (dict(cu=ctypes.c_void_p(0x30002)), ALIGN),
+    (dict(scale=float("inf")), VALUE),
+    (dict(ws=None), WS), (dict(wsb=64), WS), (dict(ws=ctypes.c_void_p(0x20010)), WS),
+])
+def test_bwd_varlen_rejects(kw, status):
+    assert bwd_varlen(**kw) == status
+
+
+@pytest.mark.parametrize("kw", [dict(nseq=0), dict(total=0), dict(max_seqlen=0),
+                                dict(total=0, q=None, dq=None, cu=None, ws=None)])
+def test_bwd_varlen_empty_is_ok_without_launch(kw):
+    assert bwd_varlen(**kw) == OK
+
+
+def test_bwd_varlen_binding_checks_arguments():
+    """Operand checks run before the device check, so CPU tensors reach each of them."""
+    import torch
+    q = torch.zeros(10, 2, 64, dtype=torch.bfloat16)
+    k = torch.zeros(10, 1, 64, dtype=torch.bfloat16)
+    lse = torch.zeros(2, 10, dtype=torch.float32)
+    cu = torch.tensor([0, 10], dtype=torch.int32)
+    with pytest.raises(ValueError, match="cu_seqlens must be"):
+        ea.attn_bwd_varlen(q, k, k, q, lse, q, torch.tensor([0, 10], dtype=torch.int64), 10)
+    with pytest.raises(ValueError, match="has shape"):
+        ea.attn_bwd_varlen(q, k, k, q, lse[:, :9], q, cu, 10)
+    with pytest.raises(TypeError, match="must be torch.bfloat16"):
+        ea.attn_bwd_varlen(q, k, k, q, lse, q.float(), cu, 10)
+    with pytest.raises(ValueError, match="must be on a GPU device"):
+        ea.attn_bwd_varlen(q, k, k, q, lse, q, cu, 10)

@@ -120,10 +120,12 @@ VARLEN_WORKLOADS: Dict[int, VarlenWorkload] = {
 }
 
 
-def make_varlen_tensors(lengths, Hq: int, Hkv: int, d: int, seed: int) -> Dict[str, torch.Tensor]:
+def make_varlen_tensors(lengths, Hq: int, Hkv: int, d: int, seed: int,
+                        with_do: bool = False) -> Dict[str, torch.Tensor]:
     """Seeded packed bf16 CPU tensors: q [T,Hq,d], k, v [T,Hkv,d] (T = sum of lengths), drawn
-    in that order as fp32 N(0,1) after ``seed`` and rounded to bf16, and the int32 offsets
-    cu_seqlens [n+1]."""
+    in that order as fp32 N(0,1) after ``seed`` and rounded to bf16 (with_do: then the
+    upstream gradient do [T,Hq,d], drawn last, so q, k and v do not depend on it), and the
+    int32 offsets cu_seqlens [n+1]."""
     g = torch.Generator("cpu").manual_seed(seed)
     T = int(sum(lengths))
     q = torch.randn((T, Hq, d), generator=g, dtype=torch.float32)
@@ -132,13 +134,17 @@ def make_varlen_tensors(lengths, Hq: int, Hkv: int, d: int, seed: int) -> Dict[s
     cu = torch.zeros(len(lengths) + 1, dtype=torch.int32)
     if lengths:
         cu[1:] = torch.cumsum(torch.tensor(lengths, dtype=torch.int64), 0).to(torch.int32)
-    return {"q": q.to(torch.bfloat16), "k": k.to(torch.bfloat16), "v": v.to(torch.bfloat16), "cu_seqlens": cu}
+    out = {"q": q.to(torch.bfloat16), "k": k.to(torch.bfloat16), "v": v.to(torch.bfloat16), "cu_seqlens": cu}
+    if with_do:
+        out["do"] = torch.randn((T, Hq, d), generator=g, dtype=torch.float32).to(torch.bfloat16)
+    return out
 
 
-def make_varlen_inputs(w: VarlenWorkload, seed: int | None = None) -> Dict[str, torch.Tensor]:
+def make_varlen_inputs(w: VarlenWorkload, seed: int | None = None, with_do: bool = False) -> Dict[str, torch.Tensor]:
     """Inputs of the packed workload ``w`` (seed defaults to its number + 100, so that the
     tensor draws do not repeat the draws of its lengths)."""
-    return make_varlen_tensors(w.lengths(), w.Hq, w.Hkv, w.d, w.number + 100 if seed is None else seed)
+    return make_varlen_tensors(w.lengths(), w.Hq, w.Hkv, w.d, w.number + 100 if seed is None else seed,
+                               with_do=with_do)
 
 
 def make_tensors(B: int, Hq: int, Hkv: int, S: int, d: int, seed: int,
