@@ -198,6 +198,10 @@ def cpu_baseline_varlen(w, inputs, target_s):
             f = lambda x, hh: x[a:a + n, hh].float().numpy().astype(np.float64)
             oracle.head_forward(f(inputs["q"], h), f(inputs["k"], hk), f(inputs["v"], hk), w.scale, w.causal)
             flop += 4.0 * n * n * w.d / (2 if w.causal else 1)
+            if "bwd" in w.passes:
+                oracle.head_backward(f(inputs["q"], h), f(inputs["k"], hk), f(inputs["v"], hk), f(inputs["do"], h),
+                                     w.scale, w.causal)
+                flop += 2.5 * 4.0 * n * n * w.d / (2 if w.causal else 1)
             pairs += 1
             toks += n
             if time.perf_counter() - t0 >= target_s:
@@ -208,21 +212,95 @@ def cpu_baseline_varlen(w, inputs, target_s):
     dt = time.perf_counter() - t0
     return {
         "value": flop / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "blas": blas, "kind": "oracle",
-        "sample": f"fp64 numpy oracle, fwd of {pairs} of {w.n * w.Hq} (sequence, query head) pairs "
+        "sample": f"fp64 numpy oracle, {'+'.join(w.passes)} of {pairs} of {w.n * w.Hq} (sequence, query head) pairs "
                   f"({toks} query rows) of the packed batch, d={w.d}, {dt:.1f} s; algorithmic flop",
     }
 
 
+class VarlenRun:
+    """A packed workload's tensors on the GPU and its passes: attn_fwd_varlen and, for
+    backward workloads, attn_bwd_varlen (workspace allocated once, outside any timing)."""
+
+    def __init__(self, w, opt):
+        import torch
+        import exact_attention_27_amd as ea
+        import workloads
+        self.torch, self.ea, self.w, self.opt = torch, ea, w, opt
+        self.with_bwd = "bwd" in w.passes
+        dev = torch.device("cuda:0")
+        host = workloads.make_varlen_inputs(w, with_do=self.with_bwd)
+        self.host = host
+        self.t = {n: x.to(dev) for n, x in host.items()}
+        self.lens = w.lengths()
+        self.total = sum(self.lens)
+        self.ms = max(self.lens)
+        self.o = torch.empty_like(self.t["q"])
+        self.lse = torch.empty((w.Hq, self.total), dtype=torch.float32, device=dev)
+        self.stream = torch.cuda.current_stream()
+        if self.with_bwd:
+            self.dq = torch.empty_like(self.t["q"])
+            self.dk = torch.empty_like(self.t["k"])
+            self.dv = torch.empty_like(self.t["v"])
+            nb = ea.attn_bwd_workspace_bytes(w.n, w.Hq, w.Hkv, self.ms, w.d)
+            self.ws = torch.empty(max(nb, 1), dtype=torch.uint8, device=dev)
+
+    def fwd(self):
+        t, w = self.t, self.w
+        self.ea.attn_fwd_varlen(t["q"], t["k"], t["v"], t["cu_seqlens"], self.ms, w.scale, w.causal, o=self.o,
+                                lse=self.lse, opt=self.opt, stream=self.stream)
+
+    def bwd(self):
+        t, w = self.t, self.w
+        self.ea.attn_bwd_varlen(t["q"], t["k"], t["v"], self.o, self.lse, t["do"], t["cu_seqlens"], self.ms, w.scale,
+                                w.causal, dq=self.dq, dk=self.dk, dv=self.dv, workspace=self.ws, opt=self.opt,
+                                stream=self.stream)
+
+    def grouped(self, reps, target_ms=2.0):
+        """Per-call times of each pass over groups of back-to-back calls (as DenseRun.grouped)."""
+        torch, s = self.torch, self.stream
+        out = {}
+        self.fwd()
+        for name, fn in (("fwd", self.fwd),) + ((("bwd", self.bwd),) if self.with_bwd else ()):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(s)
+            fn()
+            e1.record(s)
+            torch.cuda.synchronize()
+            g = max(1, min(200, int(target_ms / max(e0.elapsed_time(e1), 1e-3))))
+            ms = []
+            for _ in range(reps):
+                e0.record(s)
+                for _ in range(g):
+                    fn()
+                e1.record(s)
+                torch.cuda.synchronize()
+                ms.append(e0.elapsed_time(e1) / g)
+            out[name] = ms
+        return out
+
+
+def varlen_config_entry(w, opt, reps):
+    """Per-call statistics of a packed workload's passes (after the timed region)."""
+    run = VarlenRun(w, opt)
+    gr = run.grouped(reps)
+    out = {"shape": {"sequences": w.n, "lengths": f"{min(run.lens)}..{max(run.lens)}", "total_tokens": run.total,
+                     "Hq": w.Hq, "Hkv": w.Hkv, "d": w.d, "causal": w.causal},
+           "groups": reps, "timing": "per call, over groups of back-to-back calls of about 2 ms",
+           "fwd": pass_stats(gr["fwd"], w.fwd_flop())}
+    if run.with_bwd:
+        out["bwd"] = pass_stats(gr["bwd"], w.bwd_flop())
+    del run
+    return out
+
+
 def main_varlen(args, w):
-    """Time the packed forward (attn_fwd_varlen) on a variable-length workload."""
+    """Time a packed workload: attn_fwd_varlen, and attn_bwd_varlen for backward workloads."""
     import torch
     import exact_attention_27_amd as ea
     import workloads
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    host = workloads.make_varlen_inputs(w)
-    t = {n: x.to(dev) for n, x in host.items()}
     lens = w.lengths()
     total = sum(lens)
     opt = ea.attn_default_options()
@@ -232,31 +310,36 @@ def main_varlen(args, w):
         opt.tau = args.tau
     if args.variant is not None:
         opt.variant = args.variant
-    o = torch.empty_like(t["q"])
-    lse = torch.empty((w.Hq, total), dtype=torch.float32, device=dev)
-    stream = torch.cuda.current_stream()
+    run = VarlenRun(w, opt)
+    host = run.host
+    stream = run.stream
 
-    def step():
-        ea.attn_fwd_varlen(t["q"], t["k"], t["v"], t["cu_seqlens"], max(lens), w.scale, w.causal, o=o, lse=lse,
-                           opt=opt, stream=stream)
+    def step(ev=None):
+        run.fwd()
+        if ev:
+            ev[1].record(stream)
+        if run.with_bwd:
+            run.bwd()
+            if ev:
+                ev[2].record(stream)
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    ev[0].record(stream)
-    for _ in range(args.steps):
-        step()
-    ev[1].record(stream)
+    for i in range(args.steps):
+        evs[i][0].record(stream)
+        step(evs[i])
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     ms_step = elapsed * 1e3 / args.steps
-    fwd_ms = ev[0].elapsed_time(ev[1]) / args.steps
-    flop = w.fwd_flop()
+    fwd_ms = statistics.mean(e[0].elapsed_time(e[1]) for e in evs)
+    bwd_ms = statistics.mean(e[1].elapsed_time(e[2]) for e in evs) if run.with_bwd else None
+    flop = w.fwd_flop() + (w.bwd_flop() if run.with_bwd else 0.0)
     value = flop / (ms_step * 1e-3) / 1e12
-    fwd_tf = flop / (fwd_ms * 1e-3) / 1e12
+    fwd_tf = w.fwd_flop() / (fwd_ms * 1e-3) / 1e12
     roofline = {"kernel": "fwd_kernel", "bound": "mfma", "achieved": round(fwd_tf, 2), "peak": PEAK_BF16_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(fwd_tf / PEAK_BF16_TFLOPS, 4),
                 "traffic": traffic_record("fwd_kernel", w.name),
@@ -272,10 +355,13 @@ def main_varlen(args, w):
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": w.name, "sequences": w.n, "lengths": f"{min(lens)}..{max(lens)} log-uniform",
                    "total_tokens": total, "Hq": w.Hq, "Hkv": w.Hkv, "d": w.d, "causal": w.causal,
-                   "passes": "fwd", "exp_mode": int(opt.exp_mode), "tau": float(opt.tau),
+                   "passes": "+".join(w.passes), "exp_mode": int(opt.exp_mode), "tau": float(opt.tau),
                    "variant": VARIANT_NAMES.get(int(opt.variant), int(opt.variant)), "step_flop": flop},
         "frac_of_peak": round(value / PEAK_BF16_TFLOPS, 4),
-        "roofline": roofline, "mfma_ceiling": ceiling, "breakdown": {"fwd_ms": round(fwd_ms, 4), "fwd_tflops": round(fwd_tf, 2)},
+        "roofline": roofline, "mfma_ceiling": ceiling,
+        "breakdown": {"fwd_ms": round(fwd_ms, 4), "fwd_tflops": round(fwd_tf, 2),
+                      **({"bwd_ms": round(bwd_ms, 4), "bwd_tflops": round(w.bwd_flop() / (bwd_ms * 1e-3) / 1e12, 2)}
+                         if run.with_bwd else {})},
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
@@ -586,6 +672,8 @@ def main():
             if name != w.name:
                 configs[name] = config_entry(get_workload(name), opt, k, wu, clk)
                 torch.cuda.empty_cache()
+        configs["varlen_train_fwd_bwd"] = varlen_config_entry(get_workload("varlen_train_fwd_bwd"), opt, 10)
+        torch.cuda.empty_cache()
 
     ceiling = mfma_ceiling()
     if ceiling:

@@ -24,7 +24,7 @@ __all__ = [
     "AttnError", "attn_options", "library_path", "lib",
     "attn_fwd", "attn_fwd_ex", "attn_fwd_varlen", "attn_bwd", "attn_bwd_ex", "attn_bwd_phase", "attn_bwd_workspace_bytes",
     "attn_bwd_varlen",
-    "attn_bwd_noalloc", "ATTN_ERR_SCRATCH", "attn_launch_plan", "attn_plan", "attention",
+    "attn_bwd_noalloc", "ATTN_ERR_SCRATCH", "attn_launch_plan", "attn_plan", "attention", "attention_varlen",
     "attn_default_options", "attn_status_string", "attn_exp2_eval", "attn_exp2_poly_host",
     "ATTN_EXP_HW", "ATTN_EXP_POLY3", "ATTN_VARIANT_AUTO", "ATTN_VARIANT_PINGPONG", "ATTN_VARIANT_FOURWAVE",
 ]
@@ -473,4 +473,36 @@ def attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, scale: Optional
     as bf16, contiguous).  Returns O, or (O, LSE) with return_lse (LSE [B, Hq, S] fp32,
     natural log, not differentiable)."""
     o, lse = _Attention.apply(q, k, v, scale, causal)
+    return (o, lse) if return_lse else o
+
+
+class _AttentionVarlen(torch.autograd.Function):
+    """attn_fwd_varlen in the forward, attn_bwd_varlen in the backward (O and LSE kept)."""
+
+    @staticmethod
+    def forward(ctx, q, k, v, cu_seqlens, max_seqlen, scale, causal):
+        o, lse = attn_fwd_varlen(q, k, v, cu_seqlens, max_seqlen, scale, causal)
+        ctx.save_for_backward(q, k, v, o, lse, cu_seqlens)
+        ctx.max_seqlen, ctx.scale, ctx.causal = max_seqlen, scale, causal
+        ctx.mark_non_differentiable(lse)
+        return o, lse
+
+    @staticmethod
+    def backward(ctx, do, _dlse):
+        q, k, v, o, lse, cu = ctx.saved_tensors
+        # Rows outside every sequence get no gradient from the library: zero them first.
+        dq, dk, dv = torch.zeros_like(q), torch.zeros_like(k), torch.zeros_like(v)
+        attn_bwd_varlen(q, k, v, o, lse, do.contiguous(), cu, ctx.max_seqlen, ctx.scale, ctx.causal,
+                        dq=dq, dk=dk, dv=dv)
+        return dq, dk, dv, None, None, None, None
+
+
+def attention_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens: torch.Tensor,
+                     max_seqlen: int, scale: Optional[float] = None, causal: bool = False,
+                     return_lse: bool = False):
+    """Exact attention with autograd over a packed batch: attn_fwd_varlen's layouts
+    (q [total, Hq, d], k and v [total, Hkv, d] bf16, cu_seqlens [nseq + 1] int32 on the
+    same GPU, max_seqlen >= every length); gradients from attn_bwd_varlen (zero for rows
+    outside every sequence).  Returns O, or (O, LSE [Hq, total]) with return_lse."""
+    o, lse = _AttentionVarlen.apply(q, k, v, cu_seqlens, int(max_seqlen), scale, causal)
     return (o, lse) if return_lse else o

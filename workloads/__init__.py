@@ -107,6 +107,10 @@ class VarlenWorkload:
         f = sum(4.0 * self.Hq * n * n * self.d for n in self.lengths())
         return f / 2 if self.causal else f
 
+    def bwd_flop(self) -> float:
+        """Algorithmic backward flop: 2.5 x the forward's (its five products)."""
+        return 2.5 * self.fwd_flop()
+
     def describe(self) -> str:
         ls = self.lengths()
         return (f"{self.n} sequences, lengths {min(ls)}..{max(ls)} (total {sum(ls)} tokens), Hq={self.Hq} "
@@ -117,6 +121,8 @@ VARLEN_WORKLOADS: Dict[int, VarlenWorkload] = {
     # A prefill batch of prompts of mixed lengths (the pages' integration target: prefill
     # in SGLang/vLLM).
     9: VarlenWorkload(9, "varlen_prefill_fwd", 32, 256, 8192, 32, 8, 128, True),
+    # A packed training batch of the same kind of mix: forward and backward.
+    10: VarlenWorkload(10, "varlen_train_fwd_bwd", 32, 256, 8192, 32, 8, 128, True, ("fwd", "bwd")),
 }
 
 
