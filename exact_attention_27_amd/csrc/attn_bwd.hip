@@ -27,6 +27,12 @@
 // (dispatch_chunk in attn_kernels.h) so that the re-read K/V (dQ) and Q/dO (dK/dV) of the
 // resident workgroups fit the memory-side cache.
 //
+// Packed batches (VARLEN, attn_bwd_varlen): the same kernels with per-sequence lengths
+// from cu_seqlens and token-major rows for the caller's tensors; the workspace keeps the
+// dense layout of B sequences of S rows (S the longest), and the grids run in chunks of 8
+// (sequence, KV head) groups, one per XCD (varlen_chunk_groups).  Workgroups whose tile
+// lies past their sequence's end return at once.
+//
 // In the S accumulator layout of bwd_main (v_mfma_f32_32x32x16_f16, A = Q rows, B = K^T,
 // all four products on fp16 operands scaled by powers of two, see below) a lane holds one
 // key column and 16 query rows; P and dS are packed to fp16 in registers and used directly
@@ -1045,8 +1051,8 @@ template <int D, bool CAUSAL, int EXPMODE, bool VARLEN>
 hipError_t launch_bwd_t(const BwdArgs& a0, bool four_wave, int phases, hipStream_t stream) {
   hipError_t e = hipSuccess;
   BwdArgs a = a0;
-  a.dq_chunk = dq_chunk_groups(a.B, a.Hkv, a.S, D);
-  a.kv_chunk = dkdv_chunk_groups(a.B, a.Hq, a.Hkv, a.S, D);
+  a.dq_chunk = VARLEN ? varlen_chunk_groups(a.B, a.Hkv) : dq_chunk_groups(a.B, a.Hkv, a.S, D);
+  a.kv_chunk = VARLEN ? varlen_chunk_groups(a.B, a.Hkv) : dkdv_chunk_groups(a.B, a.Hq, a.Hkv, a.S, D);
   // Order: preprocess, dQ (which also writes the exact -D and the fp16 dO that the dK/dV
   // kernel reads), dK/dV.
   if (phases & 1) {

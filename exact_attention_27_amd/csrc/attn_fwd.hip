@@ -48,7 +48,8 @@
 // groups is a multiple of 8 all query heads and query tiles of one KV group run on one XCD
 // and share its L2 for K and V.  Large launches of short sequences run in chunks of KV
 // groups (dispatch_chunk in attn_kernels.h) so that the resident workgroups' K and V fit
-// the memory-side cache.
+// the memory-side cache; packed batches run in chunks of 8 (sequence, KV head) groups,
+// one per XCD (varlen_chunk_groups).
 #include <type_traits>
 
 #include "attn_device.h"
@@ -491,7 +492,7 @@ hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t stream) {
   FwdArgs c = a;
   // (Measured with 256-512 heads at S = 2048: 15-25% faster than one chunk; at S = 8192,
   // chunks of 24-48 groups were 1-4% slower.)
-  c.grp_chunk = fwd_chunk_groups(a.B, a.Hkv, a.S, D);
+  c.grp_chunk = VARLEN ? varlen_chunk_groups(a.B, a.Hkv) : fwd_chunk_groups(a.B, a.Hkv, a.S, D);
   hipLaunchKernelGGL((fwd_kernel<D, CAUSAL, EXPMODE, VARLEN, W>), grid, dim3(64 * W), 0, stream, c);
   return hipGetLastError();
 }

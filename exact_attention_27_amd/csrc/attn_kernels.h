@@ -93,6 +93,13 @@ inline int dq_chunk_groups(int B, int Hkv, int S, int d) { return dispatch_chunk
 inline int dkdv_chunk_groups(int B, int Hq, int Hkv, int S, int d) {
   return dispatch_chunk(B * Hkv, S, 4L * (Hq / Hkv) * S * d);
 }
+// Packed batches (every chunked kernel): chunks of 8 groups, one (sequence, KV head) per
+// XCD at a time, so that the resident workgroups of an XCD walk one sequence's operands
+// together.  In the unchunked order each XCD runs tiles of about 32 sequences at once, each
+// streaming its own rows past the shared L2.  (Measured on 32 sequences of 268-7377
+// tokens, GQA 32:8: backward 13.7 -> 9.75 ms, forward -0.9%; chunks of 16 or 32 groups
+// gained less or lost.)
+inline int varlen_chunk_groups(int nseq, int Hkv) { return nseq * Hkv < 8 ? nseq * Hkv : 8; }
 
 hipError_t launch_fwd(const FwdArgs& a, int d, bool causal, int exp_mode, bool pingpong, hipStream_t stream);
 // The same forward over a variable-length packed batch (a.cu_seqlens != nullptr).
