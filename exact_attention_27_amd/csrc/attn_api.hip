@@ -3,6 +3,7 @@
 // Host side only: argument validation, status codes, workspace layout, and the choice
 // of kernel.  Every check runs before any HIP call, so invalid arguments never launch
 // anything and never touch the caller's memory.
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 #include <cstring>
@@ -363,8 +364,14 @@ int attn_bwd_varlen(const void* q, const void* k, const void* v, const void* o, 
   a.cu_seqlens = cu_seqlens;
   a.total = total;
   (void)hipGetLastError();
-  return hip_status(attn::launch_bwd(a, d, causal != 0, o_.exp_mode, bwd_four_wave(o_.variant, Hq / Hkv, max_seqlen),
-                                     7, static_cast<hipStream_t>(stream)));
+  // The dK/dV workgroup shape by the walk of a sequence of the mean length (total / nseq)
+  // rather than the longest: in a mix of lengths most walks are much shorter than the
+  // longest one (packed training batch of 32 sequences, 268-7377 tokens: four waves 1.4%
+  // faster, where the longest length alone chooses eight).
+  const int mean_len = (int)(((int64_t)total + nseq - 1) / nseq);
+  return hip_status(attn::launch_bwd(a, d, causal != 0, o_.exp_mode,
+                                     bwd_four_wave(o_.variant, Hq / Hkv, std::min(mean_len, max_seqlen)), 7,
+                                     static_cast<hipStream_t>(stream)));
 }
 
 int attn_bwd_noalloc(const void* q, const void* k, const void* v, const void* o, const float* lse,

@@ -104,21 +104,31 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdArgs a, int S_pad) {
   }
 
   // O, dO, Q: the group's padded rows [row0, row0 + G * S_pad), this workgroup's share.
+  // Packed batches take only the sequence's own rows rounded up to 64 (what the later
+  // kernels read), token by token with the G heads of a token adjacent as they are in
+  // memory, so that the group's workgroups share real rows; dense batches head by head.
   const long row0 = ((long)b * a.Hq + (long)hkv * G) * S_pad;
-  const long nrows = (long)G * S_pad;
+  const long nrows = (long)G * (VARLEN ? (S + kBwdBM - 1) / kBwdBM * kBwdBM : S_pad);
   const long per = ((nrows + kPreBlocks - 1) / kPreBlocks + RPI - 1) / RPI * RPI;
   const long r_end = min(nrows, (nb + 1) * per);
   float mdo = 0.0f, mq = 0.0f;
   // Two rows per thread and pass, their loads issued together.
   for (long r0 = nb * per; r0 < r_end; r0 += 2 * RPI) {
-    long row[2];
+    long row[2], wi[2];
     bool real[2];
     u32x4 ov[2], dv[2], qv[2];
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       const long r = r0 + u * RPI + tid / LPR;  // group-relative padded row
-      const int hl = (int)(r / S_pad);
-      const int srow = (int)(r - (long)hl * S_pad);
+      int hl, srow;
+      if constexpr (VARLEN) {
+        srow = (int)(r / G);
+        hl = (int)(r - (long)srow * G);
+      } else {
+        hl = (int)(r / S_pad);
+        srow = (int)(r - (long)hl * S_pad);
+      }
+      wi[u] = VARLEN ? row0 + (long)hl * S_pad + srow : row0 + r;  // workspace row
       real[u] = r < r_end && srow < S;
       const int h = hkv * G + hl;  // query head
       row[u] = real[u] ? (long)(lbase + (size_t)h * ls_h) + srow : 0;  // LSE index of the row
@@ -147,8 +157,8 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdArgs a, int S_pad) {
 #pragma unroll
       for (int off = LPR / 2; off >= 1; off >>= 1) acc += __shfl_xor(acc, off);
       if (r < r_end && part == 0) {
-        a.delta[row0 + r] = -acc;  // -D: the dQ kernel's dP products start from it
-        a.lse2[row0 + r] = real[u] ? a.lse[row[u]] * kLog2e : 0.0f;
+        a.delta[wi[u]] = -acc;  // -D: the dQ kernel's dP products start from it
+        a.lse2[wi[u]] = real[u] ? a.lse[row[u]] * kLog2e : 0.0f;
       }
     }
   }
