@@ -53,6 +53,46 @@ def test_graph_capture_and_replay():
             assert torch.equal(x, r), f"replay {rep}: {name} differs from the eager result"
 
 
+def test_packed_graph_capture_and_replay():
+    """The packed forward and backward captured once, replayed three times with eager work
+    between replays; every replay equals the eager result bit for bit (the library
+    allocates nothing, and the caller hands in the workspace)."""
+    lengths, Hq, Hkv, d = [300, 1, 0, 517, 64], 8, 2, 128
+    print(f"\n[packed graph] lengths={lengths} Hq={Hq} Hkv={Hkv} d={d}", flush=True)
+    t = {n: x.to(DEV) for n, x in workloads.make_varlen_tensors(lengths, Hq, Hkv, d, 43, with_do=True).items()}
+    cu, ms, scale = t["cu_seqlens"], max(lengths), d ** -0.5
+    o, lse = ea.attn_fwd_varlen(t["q"], t["k"], t["v"], cu, ms, scale, True)
+    dq, dk, dv = ea.attn_bwd_varlen(t["q"], t["k"], t["v"], o, lse, t["do"], cu, ms, scale, True)
+    torch.cuda.synchronize()
+    ref = [x.clone() for x in (o, lse, dq, dk, dv)]
+
+    go, glse = torch.empty_like(o), torch.empty_like(lse)
+    gdq, gdk, gdv = torch.empty_like(dq), torch.empty_like(dk), torch.empty_like(dv)
+    ws = torch.empty(ea.attn_bwd_workspace_bytes(len(lengths), Hq, Hkv, ms, d), dtype=torch.uint8, device=DEV)
+
+    def passes():
+        ea.attn_fwd_varlen(t["q"], t["k"], t["v"], cu, ms, scale, True, o=go, lse=glse)
+        ea.attn_bwd_varlen(t["q"], t["k"], t["v"], go, glse, t["do"], cu, ms, scale, True, gdq, gdk, gdv, ws)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):  # warm-up on the capture stream
+        passes()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        passes()
+    for rep in range(3):
+        for x in (go, glse, gdq, gdk, gdv):
+            x.fill_(float("nan") if x.dtype == torch.float32 else 7.0)  # eager work between replays
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for name, x, r in zip(("o", "lse", "dq", "dk", "dv"), (go, glse, gdq, gdk, gdv), ref):
+            assert torch.equal(x, r), f"replay {rep}: {name} differs from the eager result"
+
+
 def test_many_small_heads():
     """A large grid of short sequences: B=96, Hq=16, Hkv=4, S=100 (one query tile and two
     key tiles per head, the last one ragged); sampled heads against the oracle."""
