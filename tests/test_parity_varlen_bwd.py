@@ -201,3 +201,30 @@ def test_varlen_bwd_prefill_workload():
         assert torch.isfinite(x.float()).all()
     check(host, host["cu_seqlens"], (dq.cpu(), dk.cpu(), dv.cpu()), w.Hq, w.Hkv, w.scale, w.causal, kv_heads=[0],
           pool=True)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_offsets_outside_the_tensor_are_clamped(causal):
+    """cu_seqlens entries below 0 or past total are clamped (include/attn.h): offsets
+    [-7, 40, 40, 130] over 100 tokens are the sequences [0, 40), [40, 40) (empty) and
+    [40, 100).  Both packed passes compute exactly those sequences."""
+    Hq, Hkv, d, total = 4, 2, 64, 100
+    print(f"\n[varlen clamped offsets] causal={causal}", flush=True)
+    t = workloads.make_varlen_tensors([total], Hq, Hkv, d, 71, with_do=True)
+    dev = {n: x.to(DEV) for n, x in t.items()}
+    cu = torch.tensor([-7, 40, 40, 130], dtype=torch.int32, device=DEV)
+    scale = d ** -0.5
+    o, lse = ea.attn_fwd_varlen(dev["q"], dev["k"], dev["v"], cu, 60, scale, causal)
+    dq, dk, dv = ea.attn_bwd_varlen(dev["q"], dev["k"], dev["v"], o, lse, dev["do"], cu, 60, scale, causal)
+    torch.cuda.synchronize()
+    G = Hq // Hkv
+    real = torch.tensor([0, 40, 40, 100], dtype=torch.int32)
+    for s in range(3):
+        a, b = int(real[s]), int(real[s + 1])
+        for h in range(Hq):
+            x, y = oracle.head_forward(f64(t["q"][a:b, h]), f64(t["k"][a:b, h // G]), f64(t["v"][a:b, h // G]),
+                                       scale, causal)
+            if b > a:
+                assert_bf16_close("o", o[a:b, h].cpu(), x)
+                assert np.abs(f64(lse[h, a:b]) - y).max() <= 1e-3
+    check(t, real, (dq.cpu(), dk.cpu(), dv.cpu()), Hq, Hkv, scale, causal)
