@@ -241,7 +241,7 @@ class VarlenRun:
             self.dq = torch.empty_like(self.t["q"])
             self.dk = torch.empty_like(self.t["k"])
             self.dv = torch.empty_like(self.t["v"])
-            nb = ea.attn_bwd_workspace_bytes(w.n, w.Hq, w.Hkv, self.ms, w.d)
+            nb = ea.attn_bwd_varlen_workspace_bytes(w.n, self.total, w.Hq, w.Hkv, w.d)
             self.ws = torch.empty(max(nb, 1), dtype=torch.uint8, device=dev)
 
     def fwd(self):

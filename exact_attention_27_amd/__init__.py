@@ -23,7 +23,7 @@ import torch
 __all__ = [
     "AttnError", "attn_options", "library_path", "lib",
     "attn_fwd", "attn_fwd_ex", "attn_fwd_varlen", "attn_bwd", "attn_bwd_ex", "attn_bwd_phase", "attn_bwd_workspace_bytes",
-    "attn_bwd_varlen",
+    "attn_bwd_varlen", "attn_bwd_varlen_workspace_bytes",
     "attn_bwd_noalloc", "ATTN_ERR_SCRATCH", "attn_launch_plan", "attn_plan", "attention", "attention_varlen",
     "attn_default_options", "attn_status_string", "attn_exp2_eval", "attn_exp2_poly_host",
     "ATTN_EXP_HW", "ATTN_EXP_POLY3", "ATTN_VARIANT_AUTO", "ATTN_VARIANT_PINGPONG", "ATTN_VARIANT_FOURWAVE",
@@ -96,6 +96,8 @@ def lib() -> ctypes.CDLL:
         L.attn_bwd_phase.restype = _I
         L.attn_bwd_phase.argtypes = [_I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I,
                                      _P, ctypes.c_size_t, ctypes.POINTER(attn_options), _P]
+        L.attn_bwd_varlen_workspace_bytes.restype = ctypes.c_size_t
+        L.attn_bwd_varlen_workspace_bytes.argtypes = [_I, _I, _I, _I, _I]
         L.attn_bwd_varlen.restype = _I
         L.attn_bwd_varlen.argtypes = [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _I,
                                       _P, ctypes.c_size_t, ctypes.POINTER(attn_options), _P]
@@ -277,7 +279,7 @@ def attn_bwd_varlen(q, k, v, o, lse, do, cu_seqlens, max_seqlen: int, scale: Opt
     attn_fwd_varlen returns it); cu_seqlens: [nseq + 1] int32 device tensor of token
     offsets; max_seqlen must be >= every length.  Returns (dq, dk, dv) in the layouts of
     q, k and v; rows outside every sequence are left as allocated (torch.empty).
-    workspace (uint8, >= attn_bwd_workspace_bytes(nseq, Hq, Hkv, max_seqlen, d)) is
+    workspace (uint8, >= attn_bwd_varlen_workspace_bytes(nseq, total, Hq, Hkv, d)) is
     allocated with torch when not given.  scale defaults to 1/sqrt(d)."""
     if q.dim() != 3 or k.dim() != 3:
         raise ValueError("q and k must be [total, H, d]")
@@ -302,7 +304,7 @@ def attn_bwd_varlen(q, k, v, o, lse, do, cu_seqlens, max_seqlen: int, scale: Opt
         raise ValueError("workspace must be a contiguous tensor")
     _same_gpu(q=q, k=k, v=v, o=o, lse=lse, do=do, cu_seqlens=cu_seqlens, dq=dq, dk=dk, dv=dv,
               **({} if workspace is None else {"workspace": workspace}))
-    nbytes = attn_bwd_workspace_bytes(nseq, Hq, Hkv, int(max_seqlen), d)
+    nbytes = attn_bwd_varlen_workspace_bytes(nseq, total, Hq, Hkv, d)
     if workspace is None:
         workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
@@ -336,6 +338,10 @@ def attn_launch_plan(B: int, Hq: int, Hkv: int, S: int, d: int, causal: bool = F
 
 def attn_bwd_workspace_bytes(B: int, Hq: int, Hkv: int, S: int, d: int) -> int:
     return int(lib().attn_bwd_workspace_bytes(B, Hq, Hkv, S, d))
+
+
+def attn_bwd_varlen_workspace_bytes(nseq: int, total: int, Hq: int, Hkv: int, d: int) -> int:
+    return int(lib().attn_bwd_varlen_workspace_bytes(nseq, total, Hq, Hkv, d))
 
 
 ATTN_BWD_ALL, ATTN_BWD_PREPROCESS, ATTN_BWD_MAIN, ATTN_BWD_DQ = 0, 1, 2, 3

@@ -102,6 +102,33 @@ BwdWorkspace bwd_workspace(int B, int Hq, int Hkv, int S, int d) {
   w.total = w.q16 + round_up((size_t)B * Hq * S * d * sizeof(uint16_t));
   return w;
 }
+// The packed backward's workspace: the same parts, the row arrays and the fp16 copies laid
+// out by token (attn::varlen_ws_rows rows per query head, a sequence's rows from
+// attn::varlen_ws_start), so that it grows with the tokens, not with nseq x the longest.
+BwdWorkspace bwd_workspace_varlen(int nseq, int total, int Hq, int Hkv, int d) {
+  const size_t prows = (size_t)Hq * attn::varlen_ws_rows(nseq, total);
+  BwdWorkspace w;
+  w.delta = 0;
+  w.lse2 = w.delta + round_up(prows * sizeof(float));
+  w.ndx = w.lse2 + round_up(prows * sizeof(float));
+  w.pmax = w.ndx + round_up(prows * sizeof(float));
+  w.do16 = w.pmax + round_up((size_t)nseq * Hkv * attn::kPreBlocks * 4 * sizeof(float));
+  w.q16 = w.do16 + round_up(prows * d * sizeof(uint16_t));
+  w.total = w.q16 + round_up(prows * d * sizeof(uint16_t));
+  return w;
+}
+// Sizes of a packed backward, as attn_bwd_varlen checks them (ATTN_OK or the error).
+int check_varlen_sizes(int nseq, int total, int max_seqlen, int Hq, int Hkv, int d, bool* empty) {
+  if (nseq < 0 || total < 0 || max_seqlen < 0 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0) return ATTN_ERR_SHAPE;
+  if (d != 64 && d != 128) return ATTN_ERR_UNSUPPORTED;
+  // The grids are those of a dense batch of nseq sequences of max_seqlen rows; per-lane
+  // offsets within a tile of token-major rows are 32-bit.
+  int st = check_sizes(nseq, Hq, Hkv, max_seqlen, d, empty);
+  if (st != ATTN_OK) return st;
+  if ((int64_t)Hq * d * 64 * 2 >= (int64_t)1 << 31) return ATTN_ERR_SHAPE;
+  *empty = *empty || total == 0;
+  return ATTN_OK;
+}
 
 // ---------------------------------------------------------------------------------
 // Scratch for attn_bwd_noalloc: a file-scope device array (each GPU the library runs on
@@ -314,29 +341,30 @@ int attn_bwd_phase(int phase, const void* q, const void* k, const void* v, const
                                      static_cast<hipStream_t>(stream)));
 }
 
+size_t attn_bwd_varlen_workspace_bytes(int nseq, int total, int Hq, int Hkv, int d) {
+  bool empty = false;
+  if (check_varlen_sizes(nseq, total, 0, Hq, Hkv, d, &empty) != ATTN_OK || nseq == 0 || total == 0) return 0;
+  return bwd_workspace_varlen(nseq, total, Hq, Hkv, d).total;
+}
+
 int attn_bwd_varlen(const void* q, const void* k, const void* v, const void* o, const float* lse,
                     const void* dO, void* dq, void* dk, void* dv,
                     const int* cu_seqlens, int nseq, int total, int max_seqlen,
                     int Hq, int Hkv, int d, float scale, int causal,
                     void* workspace, size_t workspace_bytes, const attn_options* opt, void* stream) {
-  if (nseq < 0 || total < 0 || max_seqlen < 0 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0) return ATTN_ERR_SHAPE;
-  if (d != 64 && d != 128) return ATTN_ERR_UNSUPPORTED;
-  // The grids and the workspace are those of a dense batch of nseq sequences of
-  // max_seqlen rows; per-lane offsets within a tile of token-major rows are 32-bit.
   bool empty = false;
-  int st = check_sizes(nseq, Hq, Hkv, max_seqlen, d, &empty);
+  int st = check_varlen_sizes(nseq, total, max_seqlen, Hq, Hkv, d, &empty);
   if (st != ATTN_OK) return st;
-  if ((int64_t)Hq * d * 64 * 2 >= (int64_t)1 << 31) return ATTN_ERR_SHAPE;
   const attn_options o_ = opt ? *opt : attn_default_options();
   if ((st = check_options(o_)) != ATTN_OK) return st;
   if (!std::isfinite(scale)) return ATTN_ERR_VALUE;
-  if (empty || total == 0) return ATTN_OK;
+  if (empty) return ATTN_OK;
   if (!q || !k || !v || !o || !lse || !dO || !dq || !dk || !dv || !cu_seqlens) return ATTN_ERR_NULL;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse) ||
       !aligned16(dO) || !aligned16(dq) || !aligned16(dk) || !aligned16(dv) ||
       (reinterpret_cast<uintptr_t>(cu_seqlens) & 3u) != 0)
     return ATTN_ERR_ALIGN;
-  const size_t need = attn_bwd_workspace_bytes(nseq, Hq, Hkv, max_seqlen, d);
+  const size_t need = attn_bwd_varlen_workspace_bytes(nseq, total, Hq, Hkv, d);
   if (!workspace || workspace_bytes < need || (reinterpret_cast<uintptr_t>(workspace) % kAlign) != 0)
     return ATTN_ERR_WORKSPACE;
 
@@ -350,7 +378,7 @@ int attn_bwd_varlen(const void* q, const void* k, const void* v, const void* o, 
   a.dq = static_cast<uint16_t*>(dq);
   a.dk = static_cast<uint16_t*>(dk);
   a.dv = static_cast<uint16_t*>(dv);
-  const BwdWorkspace wl = bwd_workspace(nseq, Hq, Hkv, max_seqlen, d);
+  const BwdWorkspace wl = bwd_workspace_varlen(nseq, total, Hq, Hkv, d);
   char* ws = static_cast<char*>(workspace);
   a.delta = reinterpret_cast<float*>(ws + wl.delta);
   a.lse2 = reinterpret_cast<float*>(ws + wl.lse2);

@@ -85,6 +85,7 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdArgs a, int S_pad) {
   int S;
   size_t qbase, kvb, lbase, ls_h;
   int rs_q = D, rs_kv = D;
+  size_t wrow0 = 0, wstride = S_pad;  // workspace row of (this group's first head, row 0); rows per head
   if constexpr (VARLEN) {
     const int start = min(max(a.cu_seqlens[b], 0), a.total);
     const int end = min(max(a.cu_seqlens[b + 1], start), a.total);
@@ -95,6 +96,8 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdArgs a, int S_pad) {
     kvb = (size_t)start * rs_kv + (size_t)hkv * D;
     lbase = start;
     ls_h = a.total;
+    wstride = varlen_ws_rows(a.B, a.total);
+    wrow0 = (size_t)hkv * G * wstride + varlen_ws_start(b, start);
   } else {
     S = a.S;
     qbase = (size_t)b * a.Hq * S * D;
@@ -128,7 +131,7 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdArgs a, int S_pad) {
         hl = (int)(r / S_pad);
         srow = (int)(r - (long)hl * S_pad);
       }
-      wi[u] = VARLEN ? row0 + (long)hl * S_pad + srow : row0 + r;  // workspace row
+      wi[u] = VARLEN ? (long)(wrow0 + (size_t)hl * wstride) + srow : row0 + r;  // workspace row
       real[u] = r < r_end && srow < S;
       const int h = hkv * G + hl;  // query head
       row[u] = real[u] ? (long)(lbase + (size_t)h * ls_h) + srow : 0;  // LSE index of the row
@@ -351,6 +354,7 @@ void bwd_main_kernel(BwdArgs a) {
   int S;
   size_t kvbase;
   int rs_kv = D;
+  size_t wq0 = 0, wstride = 0;  // packed: workspace row of (query head 0, row 0), rows per head
   if constexpr (VARLEN) {
     const int start = min(max(a.cu_seqlens[b], 0), a.total);
     const int end = min(max(a.cu_seqlens[b + 1], start), a.total);
@@ -358,6 +362,8 @@ void bwd_main_kernel(BwdArgs a) {
     if (k0 >= S) return;  // the whole workgroup: this key tile lies past its sequence
     rs_kv = a.Hkv * D;
     kvbase = (size_t)start * rs_kv + (size_t)hkv * D;
+    wstride = varlen_ws_rows(a.B, a.total);
+    wq0 = varlen_ws_start(b, start);
   } else {
     S = a.S;
     kvbase = ((size_t)b * a.Hkv + hkv) * (size_t)S * D;
@@ -408,7 +414,7 @@ void bwd_main_kernel(BwdArgs a) {
       --stage_qt;
     }
     const int hq = hkv * G + g;
-    const size_t rbase = ((size_t)b * a.Hq + hq) * (size_t)a.S;
+    const size_t rbase = VARLEN ? hq * wstride + wq0 : ((size_t)b * a.Hq + hq) * (size_t)a.S;
     const int q0 = qt * BM;
     const char* qb = (const char*)(a.q16 + (rbase + q0) * D);
     const char* ob = (const char*)(a.do16 + (rbase + q0) * D);
@@ -432,7 +438,7 @@ void bwd_main_kernel(BwdArgs a) {
     }
     // LSE log2e (wave 0) and D (wave 1) of the BM queries: BM / 4 lanes x 16 bytes each.
     if (wave_u < 2) {
-      const size_t pbase = ((size_t)b * a.Hq + hq) * (size_t)S_pad + q0;
+      const size_t pbase = (VARLEN ? hq * wstride + wq0 : ((size_t)b * a.Hq + hq) * (size_t)S_pad) + q0;
       const void* src = uniform_ptr((wave_u == 0 ? a.lse2 : a.ndx) + pbase);
       if (lane < BM / 4) dma16_s(src, (uint32_t)lane * 16u, &sd_lds[st][wave_u * BM]);
     }
@@ -801,6 +807,10 @@ void bwd_dq_kernel(BwdArgs a) {
   int S;
   size_t qbase, kvbase;
   int rs_q = D, rs_kv = D;
+  // Workspace row of this (batch or sequence, head)'s row 0: in the row arrays (prow0) and
+  // in the fp16 Q and dO copies (wrow0); and the rows a tile may write past S (ws_rows).
+  size_t prow0, wrow0;
+  int ws_rows;
   if constexpr (VARLEN) {
     const int start = min(max(a.cu_seqlens[b], 0), a.total);
     const int end = min(max(a.cu_seqlens[b + 1], start), a.total);
@@ -810,14 +820,18 @@ void bwd_dq_kernel(BwdArgs a) {
     rs_kv = a.Hkv * D;
     qbase = (size_t)start * rs_q + (size_t)hq * D;
     kvbase = (size_t)start * rs_kv + (size_t)hkv * D;
+    prow0 = wrow0 = hq * varlen_ws_rows(a.B, a.total) + varlen_ws_start(b, start);
+    ws_rows = (S + kBwdBM - 1) / kBwdBM * kBwdBM;  // the sequence's own rows, up to 64
   } else {
     S = a.S;
     qbase = ((size_t)b * a.Hq + hq) * (size_t)S * D;
     kvbase = ((size_t)b * a.Hkv + hkv) * (size_t)S * D;
+    prow0 = ((size_t)b * a.Hq + hq) * (size_t)S_pad;
+    wrow0 = ((size_t)b * a.Hq + hq) * (size_t)a.S;
+    ws_rows = S_pad;
   }
   const int ROWB = rs_kv * 2;  // bytes between K/V rows in memory
-  // This (batch or sequence, head)'s rows of the workspace's fp16 Q and dO copies.
-  const size_t wbase = ((size_t)b * a.Hq + hq) * (size_t)a.S * D;
+  const size_t wbase = wrow0 * D;
   const int qw = q0 + wave * 32;
   const int qi = qw + col;  // this lane's query
   const int qc = min(qi, S - 1);  // rows past the end read the last row; never stored
@@ -887,7 +901,7 @@ void bwd_dq_kernel(BwdArgs a) {
       dst_q[ks * 2] = bf16x8_to_f16x8(__builtin_bit_cast(u32x4, qf[ks]), sq);
     }
   }
-  const size_t prow = ((size_t)b * a.Hq + hq) * (size_t)S_pad + qc;
+  const size_t prow = prow0 + qc;
   const float lse2 = a.lse2[prow];
   float dsum = 0.0f;  // this lane's part of sum_j dS_ij
   // -D from the bf16 O (every register of a lane belongs to its query), subtracted as dS
@@ -1035,10 +1049,11 @@ void bwd_dq_kernel(BwdArgs a) {
   }
 
   // -D_i = -(D_i(bf16 O) + sum_j dS_ij) for the dK/dV kernel, in its dP units; 0 on the
-  // padding rows up to S_pad (that kernel moves whole 64-row blocks of it into LDS).
+  // padding rows up to the next multiple of 64 (that kernel moves whole 64-row blocks of it
+  // into LDS).
   const float dtot = sum_halves(dsum);
-  if (half == 0 && qi < S_pad) {
-    const size_t pr = ((size_t)b * a.Hq + hq) * (size_t)S_pad + qi;
+  if (half == 0 && qi < ws_rows) {
+    const size_t pr = prow0 + qi;
     a.ndx[pr] = qi < S ? (nd0 - dtot) * ldexpf(1.0f, gs.e_do + gs.e_v) : 0.0f;
   }
   if (qi < S) {

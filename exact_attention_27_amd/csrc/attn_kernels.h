@@ -60,12 +60,26 @@ struct BwdArgs {
   int dq_chunk, kv_chunk;
   // Variable-length (packed) batches; nullptr for the dense [B, H, S, d] layout.  With
   // cu_seqlens set, B is the number of sequences and S the longest sequence (it sizes the
-  // grids and the workspace's dense layout above); q, o, dO, dq are [total, Hq, d], k, v,
-  // dk, dv [total, Hkv, d] and lse [Hq, total]; sequence b is the rows cu_seqlens[b] ..
-  // cu_seqlens[b + 1] - 1 (clamped to [0, total]), of which the first S are used.
+  // grids); q, o, dO, dq are [total, Hq, d], k, v, dk, dv [total, Hkv, d] and lse
+  // [Hq, total]; sequence b is the rows cu_seqlens[b] .. cu_seqlens[b + 1] - 1 (clamped to
+  // [0, total]), of which the first S are used; the workspace's row arrays and fp16 copies
+  // are laid out by token (varlen_ws_rows below) instead of [B*Hq][S_pad] and [B*Hq][S][d].
   const int* cu_seqlens;
   int total;
 };
+
+// The packed backward's workspace rows (every row array, and the fp16 copies' rows): per
+// query head h, varlen_ws_rows(B, total) rows at h * varlen_ws_rows; sequence b's rows from
+// varlen_ws_start(b, start), start being its first token.  Starts are multiples of 64 and
+// a sequence of L tokens owns at least L rounded up to 64 rows before the next one's start
+// (start_{b+1} >= start_b + L_b), so 64-row blocks stay aligned and inside the sequence's
+// rows; the whole takes rows in proportion to the tokens, not to B times the longest.
+__host__ __device__ inline size_t varlen_ws_rows(int B, int total) {
+  return (size_t)64 * ((size_t)B + ((size_t)total + 63) / 64);
+}
+__host__ __device__ inline size_t varlen_ws_start(int b, int start) {
+  return (size_t)64 * ((size_t)b + ((size_t)start + 63) / 64);
+}
 
 // Dispatch chunks.  A launch whose workgroups of one (batch, KV head) group all re-read
 // that group's group_bytes of operands (K and V; Q and dO) runs its grid in chunks of

@@ -230,12 +230,21 @@ int attn_bwd_ex(const void* q, const void* k, const void* v, const void* o, cons
  * written.  Rows not covered by any sequence are not written; overlapping sequences (offsets
  * that are not non-decreasing) leave the rows they share unspecified.  Offsets outside
  * [0, total] are clamped, so no access leaves the tensors.  workspace: at least
- * attn_bwd_workspace_bytes(nseq, Hq, Hkv, max_seqlen, d) bytes, 256-byte aligned, owned
- * by the caller (the dense layout of nseq sequences of max_seqlen rows; contents on
- * entry do not matter).  nseq == 0, total == 0 or max_seqlen == 0 is an empty problem
- * (ATTN_OK, nothing launched).  Rounding, determinism, checks and the other conventions
- * are those of attn_bwd_ex; opt == NULL means the defaults.
+ * attn_bwd_varlen_workspace_bytes(nseq, total, Hq, Hkv, d) bytes, 256-byte aligned, owned
+ * by the caller (contents on entry do not matter).  nseq == 0, total == 0 or
+ * max_seqlen == 0 is an empty problem (ATTN_OK, nothing launched).  Rounding, determinism,
+ * checks and the other conventions are those of attn_bwd_ex; opt == NULL means the
+ * defaults.
  */
+/*
+ * Bytes of device workspace attn_bwd_varlen needs: the parts of attn_bwd's workspace, with
+ * the row arrays and the fp16 copies of dO and Q laid out by token: per query head,
+ * 64 (nseq + ceil(total / 64)) rows (each sequence's rows start on a multiple of 64 and
+ * are followed by their padding to 64).  About Hq (total + 64 nseq)(4d + 12) bytes, however
+ * the lengths are spread.  Returns 0 for invalid or empty sizes.
+ */
+size_t attn_bwd_varlen_workspace_bytes(int nseq, int total, int Hq, int Hkv, int d);
+
 int attn_bwd_varlen(const void* q, const void* k, const void* v, const void* o, const float* lse,
                     const void* dO, void* dq, void* dk, void* dv,
                     const int* cu_seqlens, int nseq, int total, int max_seqlen,

@@ -257,7 +257,7 @@ def bwd_varlen(q=A, k=A, v=A, o=A, lse=A, do=A, dq=A, dk=A, dv=A, cu=ctypes.c_vo
                max_seqlen=8, Hq=2, Hkv=1, d=64, scale=0.125, causal=0, ws=A2, wsb=None, opt=None):
     lib = ea.lib()
     if wsb is None:
-        wsb = max(ea.attn_bwd_workspace_bytes(max(nseq, 0), Hq, Hkv, max(max_seqlen, 0), d), 1) if Hq >= 1 and Hkv >= 1 else 1
+        wsb = max(ea.attn_bwd_varlen_workspace_bytes(nseq, total, Hq, Hkv, d), 1)
     return lib.attn_bwd_varlen(q, k, v, o, lse, do, dq, dk, dv, cu, nseq, total, max_seqlen, Hq, Hkv, d, scale,
                                causal, ws, wsb, None if opt is None else ctypes.byref(opt), None)
 
@@ -297,3 +297,20 @@ def test_bwd_varlen_binding_checks_arguments():
         ea.attn_bwd_varlen(q, k, k, q, lse, q.float(), cu, 10)
     with pytest.raises(ValueError, match="must be on a GPU device"):
         ea.attn_bwd_varlen(q, k, k, q, lse, q, cu, 10)
+
+
+def test_varlen_workspace_bytes():
+    """The packed backward's workspace grows with the tokens: per query head 64 (nseq +
+    ceil(total / 64)) rows of the three fp32 row arrays and the two fp16 copies, plus the
+    preprocess's partial maxima per (sequence, KV head)."""
+    nseq, total, Hq, Hkv, d = 3, 1000, 4, 2, 128
+    rup = lambda x: (x + 255) // 256 * 256
+    prows = Hq * 64 * (nseq + (total + 63) // 64)
+    want = 3 * rup(prows * 4) + rup(nseq * Hkv * 64 * 4 * 4) + 2 * rup(prows * d * 2)
+    assert ea.attn_bwd_varlen_workspace_bytes(nseq, total, Hq, Hkv, d) == want
+    # 1000 sequences of mean 500 with one of 32k: tokens, not nseq x the longest
+    assert ea.attn_bwd_varlen_workspace_bytes(1000, 500_000, 32, 8, 128) < 10e9
+    assert ea.attn_bwd_varlen_workspace_bytes(0, total, Hq, Hkv, d) == 0
+    assert ea.attn_bwd_varlen_workspace_bytes(nseq, 0, Hq, Hkv, d) == 0
+    assert ea.attn_bwd_varlen_workspace_bytes(nseq, total, 3, 2, d) == 0
+    assert ea.attn_bwd_varlen_workspace_bytes(nseq, total, Hq, Hkv, 80) == 0

@@ -68,7 +68,8 @@ def test_packed_graph_capture_and_replay():
 
     go, glse = torch.empty_like(o), torch.empty_like(lse)
     gdq, gdk, gdv = torch.empty_like(dq), torch.empty_like(dk), torch.empty_like(dv)
-    ws = torch.empty(ea.attn_bwd_workspace_bytes(len(lengths), Hq, Hkv, ms, d), dtype=torch.uint8, device=DEV)
+    ws = torch.empty(ea.attn_bwd_varlen_workspace_bytes(len(lengths), int(t["q"].shape[0]), Hq, Hkv, d),
+                     dtype=torch.uint8, device=DEV)
 
     def passes():
         ea.attn_fwd_varlen(t["q"], t["k"], t["v"], cu, ms, scale, True, o=go, lse=glse)
