@@ -1029,7 +1029,9 @@ void bwd_dq_kernel(BwdArgs a) {
       dma_tile(Vg, j + 1, Vring + (1 - P) * TILE);
     }
     const int k0 = j * BN;
-    if (k0 <= qhi + 31) {
+    // No products for a tile wholly above the wave's rows, nor for a wave whose 32 rows
+    // all lie past the end of the sequence (nothing of theirs is stored).
+    if (k0 <= qhi + 31 && qw < S) {
       const bool need_mask = (k0 + BN > S) || (k0 + BN - 1 > qhi);
       if (need_mask) {
         compute(j, parity, std::true_type{});

@@ -450,10 +450,14 @@ void fwd_kernel(FwdArgs a) {
   };
 
   // This wave's live tiles: all nkv, or under the causal mask those holding a key at or
-  // below its last query (wave-uniform, at least 1).  The steps past them are dead.  (The
-  // last live step still forms S_{nlive} and discards it: peeling that step off costs
-  // more registers than the 16 products it would save.)
-  const int nlive = CAUSAL ? min(nkv, (min(S, q0 + wave_u * 32 + 32) + BN - 1) / BN) : nkv;
+  // below its last query (wave-uniform).  The steps past them are dead.  (The last live
+  // step still forms S_{nlive} and discards it: peeling that step off costs more registers
+  // than the 16 products it would save.)  In the four-wave schedule a wave whose 32 rows
+  // all lie past the end of the sequence has none: its products would be discarded.  (The
+  // ping-pong groups keep every wave live: their barriers are staggered by group.)
+  const int nlive = (W == 4 && q0 + wave_u * 32 >= Sq)
+                        ? 0
+                        : (CAUSAL ? min(nkv, (min(S, q0 + wave_u * 32 + 32) + BN - 1) / BN) : nkv);
   using Even = std::integral_constant<int, 0>;
   using Odd = std::integral_constant<int, 1>;
   f32x16 sn[KB];
